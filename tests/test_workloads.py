@@ -1,0 +1,56 @@
+"""The seeded input generators: both backends agree bit for bit, and the
+workloads have the stated shapes, lengths and integrity faults (CPU only)."""
+import numpy as np
+import torch
+
+import workloads
+
+
+def test_backends_bit_identical():
+    for outl in (0, 66):
+        for key in (1, 0xDEADBEEF, 2 ** 32 - 1):
+            a = workloads.draw_bits(key, 12345, 50_000, "numpy", outlier_per_65536=outl)
+            b = workloads.draw_bits(key, 12345, 50_000, "torch", "cpu", outlier_per_65536=outl)
+            assert (a.view(np.int16) == b.numpy()).all()
+
+
+def test_workload_streams_bit_identical():
+    w = workloads.make(4, batch=1)
+    L = int(w.ctx_before[0])
+    a = w.kv_tokens("k", 0, L - 20, L + 1)
+    b = w.kv_tokens("k", 0, L - 20, L + 1, backend="torch", device="cpu")
+    assert (a.view(np.int16) == b.numpy()).all()
+    assert (w.q_bits().view(np.int16) == w.q_bits("torch", "cpu").numpy()).all()
+    # saturating values sit on the appended token only
+    f = workloads.bf16_bits_to_f32(a)
+    assert np.abs(f[-1]).max() == 25.0 and np.abs(f[:-1]).max() <= 20.0
+
+
+def test_distribution_is_roughly_standard_normal():
+    x = workloads.bf16_bits_to_f32(workloads.draw_bits(77, 0, 1_000_000))
+    assert abs(x.mean()) < 0.01 and abs(x.std() - 1.0) < 0.01
+
+
+def test_configs():
+    w1 = workloads.make(1)
+    assert (w1.ctx_before == [17, 64, 100, 256]).all() and w1.num_pages == 64
+    assert (w1.n_pages == [2, 5, 7, 17]).all() and w1.G == 4
+    w3 = workloads.make(3)
+    assert w3.B == 64 and w3.ctx_before.min() >= 1024 and w3.ctx_before.max() <= 32768
+    assert w3.num_pages == int(w3.n_pages.sum())
+    used = w3.page_table[w3.page_table >= 0]
+    assert np.unique(used).size == used.size == w3.num_pages
+    assert (w3.expected_abort == 0).all()
+    w5 = workloads.make(5)
+    assert w5.num_pages == 81250 and w5.Hq == 32 and w5.Hkv == 4
+    frac = w5.stale.sum() / (w5.page_table >= 0).sum()
+    assert abs(frac - 0.01) < 1e-4
+    ab = w5.expected_abort
+    assert 0.5 < ab.mean() < 0.95
+    w5r = workloads.make(5, stale_mode="requests")
+    assert w5r.expected_abort.sum() == round(0.01 * 256)
+
+
+def test_scales_recipe():
+    s = workloads.scales_from_amax(np.array([448.0, 0.0, 20.0], np.float32))
+    assert s[0] == 1.0 and s[1] == 1.0 and s[2] == np.float32(20.0) / np.float32(448.0)
