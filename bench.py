@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode step of FP8 paged attention with page-tag integrity.
+
+A step = tag check (separate batched kernel) + quantize-on-append of each
+request's new token + paged attention over the e4m3 cache (+ split merge),
+for one layer, all requests, one stream.  Inputs are synthetic and already
+resident in HBM when timing starts.
+
+Default workload: 64 requests with context lengths uniform in [1024, 32768],
+64 query / 8 kv heads, head_dim 128, 16-token pages, pages a seeded random
+permutation of the pool, tag check on.
+
+Prints ONE JSON line (rank 0, one GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FP8 paged decode attn: tokens/s and achieved HBM GB/s (% of 8 TB/s) @1 GPU"
+PEAK_GBPS = 8000.0
+
+
+def log(msg: str):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def alg_bytes(w, cache_dtype: int, tag_check: bool, active=None):
+    """Algorithmic HBM bytes of one step and of the attention kernel alone.
+
+    KV reads 2*Hkv*D*(L_b+1)*E per active request (E = 1 e4m3, 2 bf16);
+    Q read and O write 2*Hq*D bytes each; append reads 2*Hkv*D*2 bytes and
+    writes 2*Hkv*D*E; page ids 4*n_b; the tag check 12*n_b (id, expected
+    tag, current tag) when enabled.  Split-K partials are overhead, not
+    counted."""
+    import numpy as np
+    E = 1 if cache_dtype == 0 else 2
+    D = 128
+    act = np.ones(w.B, bool) if active is None else active
+    L1 = w.ctx_lens.astype(np.int64)
+    n = w.n_pages.astype(np.int64)
+    kv = int((2 * w.Hkv * D * L1 * E)[act].sum())
+    qo = int(act.sum()) * w.Hq * D * 2 * 2
+    ids = int((4 * n)[act].sum())
+    attn = kv + qo + ids
+    append = int(act.sum()) * (2 * w.Hkv * D * 2 + 2 * w.Hkv * D * E)
+    verify = int((12 * n).sum()) if tag_check else 0
+    return attn + append + verify, attn
+
+
+def time_steps(fn, steps: int):
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def event_times(fns, steps: int):
+    """Per-stage HIP-event durations (ms) on the current stream."""
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        ev[k][0].record()
+        for i, f in enumerate(fns):
+            f()
+            ev[k][i + 1].record()
+    torch.cuda.synchronize()
+    return [[ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)] for i in range(len(fns))]
+
+
+def cpu_baseline(w, target_s: float = 15.0):
+    """The oracle as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    import workloads
+    from workloads import device  # noqa: F401
+
+    rng_key = 0x5EED
+    K, V = oracle.new_cache(w.num_pages, w.Hkv)
+
+    def fill(b):
+        pages = w.page_table[b, : w.n_pages[b]]
+        nbytes = pages.size * w.Hkv * 16 * 128
+        for X, k in ((K, rng_key + 2 * b), (V, rng_key + 2 * b + 1)):
+            bits = workloads.draw_bits(k, 0, nbytes).astype(np.uint8)
+            bits[(bits & 0x7F) == 0x7F] = 0x7E
+            X[pages] = bits.reshape(pages.size, w.Hkv, 16, 128)
+
+    ks = np.full(w.Hkv, 0.01, np.float32)
+    vs = np.full(w.Hkv, 0.01, np.float32)
+    q = w.q_bits()
+    sm = np.float32(1.0 / np.sqrt(128.0))
+
+    def run(reqs):
+        reqs = np.asarray(reqs)
+        t0 = time.perf_counter()
+        ab = oracle.verify(w.page_table[reqs], w.expected_tags[reqs], w.ctx_lens[reqs], w.pool_tags)
+        kn = np.stack([w.kv_tokens("k", b, int(w.ctx_before[b]), int(w.ctx_before[b]) + 1)[0]
+                       for b in reqs])
+        vn = np.stack([w.kv_tokens("v", b, int(w.ctx_before[b]), int(w.ctx_before[b]) + 1)[0]
+                       for b in reqs])
+        oracle.append(K, V, ks, vs, kn, vn, np.arange(len(reqs), dtype=np.int32),
+                      w.ctx_before[reqs].astype(np.int32), w.page_table[reqs], abort=ab)
+        oracle.attention(K, V, ks, vs, q[reqs], w.page_table[reqs], w.ctx_lens[reqs], sm, abort=ab)
+        return time.perf_counter() - t0
+
+    fill(0)
+    t1 = run([0])
+    per_tok = t1 / max(1, int(w.ctx_lens[0]))
+    reqs, est = [0], t1
+    for b in range(1, w.B):
+        if est >= target_s:
+            break
+        fill(b)
+        reqs.append(b)
+        est += per_tok * int(w.ctx_lens[b])
+    t = run(reqs)
+    return {"value": len(reqs) / t, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"requests 0..{len(reqs) - 1} of the workload ({int(w.ctx_lens[reqs].sum())} "
+                      f"attended tokens, all {w.Hq} q-heads): tag check + append + fp64 attention, "
+                      f"one step in {t:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip bf16 variant and tag overhead")
+    ap.add_argument("--overhead-rounds", type=int, default=20)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus "
+              f"{args.gpus}", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    import workloads
+    from workloads import device
+
+    torch.cuda.set_device(0)
+    log("bench: building ragged workload (64 requests, U[1024, 32768])")
+    w = workloads.make(3)
+    st = device.build(w, split_tokens=args.split_tokens)
+    step_bytes, attn_bytes = alg_bytes(w, 0, True)
+    step = lambda: st.step(check_tags=True)  # noqa: E731
+
+    for _ in range(args.warmup):
+        step()
+    log(f"bench: timing {args.steps} steps")
+    t_step = time_steps(step, args.steps)
+    # per-kernel HIP-event times on the launch stream
+    nev = max(20, args.steps // 2)
+    tv, ta, td = event_times([st.verify, lambda: st.append(True), lambda: st.decode(True)], nev)
+    t_dec = statistics.median(td) * 1e-3
+    t_ver = statistics.median(tv) * 1e-3
+    tokens_s = w.B / t_step
+    gbps = step_bytes / t_step / 1e9
+    attn_gbps = attn_bytes / t_dec / 1e9
+    res = {
+        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e4m3 cache; bf16/f16 MFMA, f32 accumulate", "data": "synthetic",
+        "config": {"workload": w.name, "requests": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": 128, "page_tokens": 16, "kv_cache": "e4m3", "tag_check": True,
+                   "attended_tokens": int(w.ctx_lens.sum()),
+                   "split_tokens": st.split_tokens, "parallelism": "none (1 GPU)"},
+        "hbm_gbps": round(gbps, 1), "pct_of_8tbps": round(100 * gbps / PEAK_GBPS, 2),
+        "step_alg_bytes": step_bytes,
+        "roofline": {"bound": "hbm", "kernel": "decode attention (split + merge)",
+                     "achieved": round(attn_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(attn_gbps / PEAK_GBPS, 4), "traffic": None,
+                     "alg_bytes_per_launch": attn_bytes,
+                     "avg_launch_us": round(t_dec * 1e6, 2)},
+        "verify_kernel_us": round(t_ver * 1e6, 2),
+    }
+    if not args.no_extras:
+        log("bench: tag-check overhead (interleaved on/off)")
+        off = lambda: st.step(check_tags=False)  # noqa: E731
+        deltas = []
+        M = 10
+        for r in range(args.overhead_rounds):
+            a = time_steps(step, M)
+            b = time_steps(off, M)
+            deltas.append((a - b) / b)
+        rng = np.random.default_rng(0)
+        d = np.array(deltas)
+        boots = [rng.choice(d, d.size).mean() for _ in range(2000)]
+        res["tag_check_overhead"] = {"mean_pct": round(100 * d.mean(), 3),
+                                     "ci95_pct": [round(100 * float(np.percentile(boots, 2.5)), 3),
+                                                  round(100 * float(np.percentile(boots, 97.5)), 3)],
+                                     "rounds": args.overhead_rounds, "steps_per_round": M}
+        del st
+        torch.cuda.empty_cache()
+        log("bench: uniform 32x8192, e4m3 vs bf16 cache")
+        w2 = workloads.make(2)
+        var = {}
+        for cd, name in ((0, "e4m3"), (1, "bf16")):
+            s2 = device.build(w2, cache_dtype=cd)
+            for _ in range(5):
+                s2.step(True)
+            t2 = time_steps(lambda: s2.step(True), 50)
+            b2, a2 = alg_bytes(w2, cd, True)
+            td2 = statistics.median(event_times([lambda: s2.decode(True)], 30)[0]) * 1e-3
+            var[name] = {"ms_per_step": round(t2 * 1e3, 4), "tokens_s": round(w2.B / t2, 1),
+                         "hbm_gbps": round(b2 / t2 / 1e9, 1),
+                         "attn_gbps": round(a2 / td2 / 1e9, 1)}
+            del s2
+            torch.cuda.empty_cache()
+        res["uniform_32x8192"] = var
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline")
+        res["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,280 @@
+"""Python binding for libfp8kv (FP8 paged decode attention with page tags).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+library (``libfp8kv.so``, built in-tree by ``build.py``).  PyTorch supplies
+device memory and the current stream; nothing here computes.  If the library
+is missing the import fails -- there is no fallback.
+
+Names mirror the C ABI in ``include/fp8kv.h``:
+  Pool, verify_tags, append, decode_attention, decode_workspace_size,
+  decode_split_tokens, cache_offset, cache_bytes, debug_convert_e4m3.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfp8kv.so")
+
+E4M3, BF16 = 0, 1
+OUT_BF16, OUT_F32 = 0, 1
+PAGE_SIZE = 16
+HEAD_DIM = 128
+
+_STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype",
+           -3: "out of pages", -4: "workspace too small", -5: "HIP error"}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m decode_attention_paged_fp8kv_amd.build` "
+        "(or __graft_entry__.build()); there is no non-HIP fallback")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("cache_dtype", ctypes.c_int32)]
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_status_string = _sig("fp8kv_status_string", ctypes.c_char_p, [_i32])
+_last_hip_error = _sig("fp8kv_last_hip_error", _i32, [])
+_cache_bytes = _sig("fp8kv_cache_bytes", ctypes.c_size_t, [ctypes.POINTER(CacheDesc)])
+_cache_offset = _sig("fp8kv_cache_offset", ctypes.c_int64,
+                     [ctypes.POINTER(CacheDesc), _i32, _i32, _i32, _i32, _i32])
+_pool_create = _sig("fp8kv_pool_create", _i32, [_i32, ctypes.c_uint64, ctypes.POINTER(_p)])
+_pool_destroy = _sig("fp8kv_pool_destroy", None, [_p])
+_pool_alloc = _sig("fp8kv_pool_alloc", _i32, [_p, _i32, _p, _p])
+_pool_free = _sig("fp8kv_pool_free", _i32, [_p, _i32, _p])
+_pool_tag = _sig("fp8kv_pool_tag", ctypes.c_uint32, [_p, _i32])
+_pool_num_free = _sig("fp8kv_pool_num_free", _i32, [_p])
+_pool_read_tags = _sig("fp8kv_pool_read_tags", _i32, [_p, _p])
+_pool_sync = _sig("fp8kv_pool_sync", _i32, [_p, _p, _p])
+_verify = _sig("fp8kv_verify_tags", _i32, [_p, _p, _i32, _p, _i32, _p, _i32, _i32, _p, _p])
+_append = _sig("fp8kv_append", _i32, [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _p, _i32,
+                                      _p, _p, _i32, _p, _i32, _p, _p])
+_split_tokens = _sig("fp8kv_decode_split_tokens", _i32,
+                     [ctypes.POINTER(CacheDesc), _i32, _i32, _i32, _i32])
+_ws_size = _sig("fp8kv_decode_workspace_size", ctypes.c_size_t,
+                [ctypes.POINTER(CacheDesc), _i32, _i32, _i32, _i32])
+_decode = _sig("fp8kv_decode_attention", _i32,
+               [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32,
+                ctypes.c_float, _p, _p, _i32, _i32, _p, ctypes.c_size_t, _p])
+_debug_convert = _sig("fp8kv_debug_convert_e4m3", _i32, [_p, _p, _i32, _i32, _p])
+
+
+class Fp8kvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = f"{where}: {_status_string(status).decode()} ({status})"
+        if status == -5:
+            msg += f", hipError {_last_hip_error()}"
+        super().__init__(msg)
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise Fp8kvError(status, where)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: Optional[torch.Tensor], dtypes, name: str, allow_none: bool = False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+_BITS16 = (torch.bfloat16, torch.int16, torch.uint16)
+_I32 = (torch.int32,)
+_U32 = (torch.int32, torch.uint32)
+_U8 = (torch.uint8,)
+_F32 = (torch.float32,)
+
+
+def desc(num_pages: int, num_kv_heads: int, cache_dtype: int = E4M3) -> CacheDesc:
+    return CacheDesc(num_pages, PAGE_SIZE, num_kv_heads, HEAD_DIM, cache_dtype)
+
+
+def cache_bytes(d: CacheDesc) -> int:
+    return int(_cache_bytes(ctypes.byref(d)))
+
+
+def cache_offset(d: CacheDesc, is_v: int, page: int, kv_head: int, slot: int, dim: int) -> int:
+    return int(_cache_offset(ctypes.byref(d), is_v, page, kv_head, slot, dim))
+
+
+def new_cache(d: CacheDesc, device="cuda"):
+    """Allocate the K and V pools (uint8 byte tensors) for a descriptor."""
+    n = cache_bytes(d)
+    if n == 0:
+        raise ValueError("invalid cache descriptor")
+    k = torch.zeros(n, dtype=torch.uint8, device=device)
+    v = torch.zeros(n, dtype=torch.uint8, device=device)
+    return k, v
+
+
+# ---------------------------------------------------------------------------
+# page pool
+# ---------------------------------------------------------------------------
+class Pool:
+    """Free list + per-page generation tags (host object in the library)."""
+
+    def __init__(self, num_pages: int, seed: int = 0):
+        h = _p()
+        _check(_pool_create(num_pages, seed, ctypes.byref(h)), "pool_create")
+        self._h = h
+        self.num_pages = num_pages
+
+    def close(self):
+        if self._h:
+            _pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc(self, n: int):
+        import numpy as np
+        ids = np.zeros(n, np.int32)
+        tags = np.zeros(n, np.uint32)
+        _check(_pool_alloc(self._h, n, ids.ctypes.data, tags.ctypes.data), "pool_alloc")
+        return ids, tags
+
+    def free(self, ids):
+        import numpy as np
+        a = np.ascontiguousarray(ids, np.int32)
+        _check(_pool_free(self._h, a.size, a.ctypes.data), "pool_free")
+
+    def tag(self, page_id: int) -> int:
+        return int(_pool_tag(self._h, page_id))
+
+    @property
+    def num_free(self) -> int:
+        return int(_pool_num_free(self._h))
+
+    def tags(self):
+        import numpy as np
+        out = np.zeros(self.num_pages, np.uint32)
+        _check(_pool_read_tags(self._h, out.ctypes.data), "pool_read_tags")
+        return out
+
+    def sync(self, d_tags: torch.Tensor, stream=None):
+        _dev(d_tags, _U32, "d_tags")
+        _check(_pool_sync(self._h, d_tags.data_ptr(), _stream(stream)), "pool_sync")
+
+
+# ---------------------------------------------------------------------------
+# hot path
+# ---------------------------------------------------------------------------
+def verify_tags(page_table, expected_tags, ctx_lens, pool_tags, abort=None, stream=None):
+    """Batched page-tag check; returns the uint8 abort tensor [B]."""
+    B = ctx_lens.shape[0]
+    if abort is None:
+        abort = torch.empty(B, dtype=torch.uint8, device=ctx_lens.device)
+    P = page_table.shape[1] if page_table.dim() == 2 else 0
+    _check(_verify(_dev(page_table, _I32, "page_table"), _dev(expected_tags, _U32, "expected_tags"),
+                   P, _dev(ctx_lens, _I32, "ctx_lens"), B, _dev(pool_tags, _U32, "pool_tags"),
+                   pool_tags.shape[0], PAGE_SIZE, _dev(abort, _U8, "abort"), _stream(stream)),
+           "verify_tags")
+    return abort
+
+
+def append(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, k_new, v_new, token_seq, token_pos,
+           page_table, abort=None, stream=None):
+    """Quantize-on-append of num_tokens new K/V rows ([T][Hkv][128] BF16)."""
+    T = token_seq.shape[0]
+    fp8 = d.cache_dtype == E4M3
+    _check(_append(ctypes.byref(d), _dev(k_cache, _U8 + _BITS16, "k_cache"),
+                   _dev(v_cache, _U8 + _BITS16, "v_cache"),
+                   _dev(k_scale, _F32, "k_scale", allow_none=not fp8),
+                   _dev(v_scale, _F32, "v_scale", allow_none=not fp8),
+                   _dev(k_new, _BITS16, "k_new"), _dev(v_new, _BITS16, "v_new"), T,
+                   _dev(token_seq, _I32, "token_seq"), _dev(token_pos, _I32, "token_pos"),
+                   page_table.shape[0], _dev(page_table, _I32, "page_table"), page_table.shape[1],
+                   _dev(abort, _U8, "abort", allow_none=True), _stream(stream)), "append")
+
+
+def decode_split_tokens(d: CacheDesc, batch: int, num_q_heads: int, max_ctx_len: int,
+                        split_tokens: int = 0) -> int:
+    return int(_split_tokens(ctypes.byref(d), batch, num_q_heads, max_ctx_len, split_tokens))
+
+
+def decode_workspace_size(d: CacheDesc, batch: int, num_q_heads: int, max_ctx_len: int,
+                          split_tokens: int = 0) -> int:
+    return int(_ws_size(ctypes.byref(d), batch, num_q_heads, max_ctx_len, split_tokens))
+
+
+def decode_attention(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, page_table, ctx_lens,
+                     max_ctx_len: int, abort=None, out=None, out_dtype: int = OUT_BF16,
+                     sm_scale: Optional[float] = None, split_tokens: int = 0, workspace=None,
+                     stream=None):
+    """Paged decode attention; returns out [B][Hq][128] (bf16 or f32)."""
+    B, Hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), device=q.device,
+                          dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32)
+    need = decode_workspace_size(d, B, Hq, max_ctx_len, split_tokens)
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wptr = workspace.data_ptr() if (workspace is not None and need > 0) else None
+    wbytes = workspace.numel() * workspace.element_size() if wptr else 0
+    fp8 = d.cache_dtype == E4M3
+    _check(_decode(ctypes.byref(d), _dev(k_cache, _U8 + _BITS16, "k_cache"),
+                   _dev(v_cache, _U8 + _BITS16, "v_cache"),
+                   _dev(k_scale, _F32, "k_scale", allow_none=not fp8),
+                   _dev(v_scale, _F32, "v_scale", allow_none=not fp8),
+                   _dev(q, _BITS16, "q"), Hq, _dev(page_table, _I32, "page_table"),
+                   page_table.shape[1], _dev(ctx_lens, _I32, "ctx_lens"), max_ctx_len, B,
+                   float(sm_scale), _dev(abort, _U8, "abort", allow_none=True),
+                   _dev(out, (torch.bfloat16, torch.int16, torch.float32), "out"), out_dtype,
+                   split_tokens, wptr, wbytes, _stream(stream)), "decode_attention")
+    return out
+
+
+def debug_convert_e4m3(codes: torch.Tensor, which: int, stream=None) -> torch.Tensor:
+    out = torch.empty(codes.numel(), dtype=torch.float32, device=codes.device)
+    _check(_debug_convert(_dev(codes, _U8, "codes"), out.data_ptr(), codes.numel(), which,
+                          _stream(stream)), "debug_convert_e4m3")
+    return out
+
+
+def status_string(status: int) -> str:
+    return _status_string(status).decode()
+
+
+def raw_library():
+    """The ctypes handle (used by tests that call the C ABI directly)."""
+    return _lib

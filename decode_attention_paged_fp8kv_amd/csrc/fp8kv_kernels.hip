@@ -1,0 +1,864 @@
+// fp8kv: HIP kernels for gfx950 (MI355X) and their C-ABI launchers.
+//
+// One decode step over an FP8 e4m3 paged KV cache with page-tag integrity
+// (Cloudflare, "Smaller, faster, safer: running Kimi and GLM at scale":
+// KV-cache section -- e4m3 storage converted on read; integrity section --
+// per-page generation tags checked by a separate batch pass before decode,
+// mismatching requests aborted).
+//
+// Kernels:
+//   verify_tags_kernel      one workgroup per request: any stale/out-of-range
+//                           page among the pages the step reads -> abort[b]=1
+//   append_kernel<C>        quantize-on-append of new tokens into their pages
+//   decode_split_kernel<C>  per (request, kv-head, split): paged K/V tiles are
+//                           loaded straight into matrix-core fragment registers
+//                           (16-byte buffer loads, tile layout = fragment
+//                           order), converted e4m3 -> bf16/f16 in hardware,
+//                           QK^T and PV on MFMA, online softmax in registers,
+//                           4 waves merged through LDS; writes the output, or a
+//                           (max, sum, weighted V) partial when the request is
+//                           split
+//   combine_kernel          log-sum-exp merge of the partials in split order
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8kv.h"
+#include "fp8kv_internal.h"
+
+namespace fp8kv_detail {
+thread_local int32_t g_last_hip_error = 0;
+void record_hip_error(int32_t e) { g_last_hip_error = e; }
+}  // namespace fp8kv_detail
+
+namespace {
+
+constexpr int kHeadDim = 128;
+constexpr int kPage = 16;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxSplitTokens = 16384;
+constexpr int kMaxSplitPages = kMaxSplitTokens / kPage;
+constexpr int kMaxGroup = 16;
+// word 3 of a raw buffer resource on gfx9-family parts (32-bit data, no
+// swizzle, no index stride)
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+template <int CACHE>
+struct Tile;
+template <>
+struct Tile<FP8KV_E4M3> {
+  static constexpr int kBytes = 2048;  // 16 tokens x 128 dims x 1 byte
+  static constexpr int kChunks = 2;    // 16-byte loads per lane per tile
+};
+template <>
+struct Tile<FP8KV_BF16> {
+  static constexpr int kBytes = 4096;
+  static constexpr int kChunks = 4;
+};
+
+// ---------------------------------------------------------------------------
+// conversions
+// ---------------------------------------------------------------------------
+
+// 8 e4m3 codes (two dwords, byte i -> element i) -> 8 bf16, exact.
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(unsigned w0, unsigned w1) {
+  u32x4_t r;
+  r.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+  r.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+  r.z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+  r.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// 4 e4m3 codes (one dword) -> 4 f16, exact.
+__device__ __forceinline__ f16x4_t e4m3x4_to_f16(unsigned w) {
+  u32x2_t r;
+  r.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  r.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+  return __builtin_bit_cast(f16x4_t, r);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<unsigned>(b) << 16);
+}
+
+// binary32 -> OCP e4m3, round to nearest even, saturating at +-448, sign
+// kept, NaN -> 0x7F|sign.  Bit-level: the normal range keeps 3 mantissa bits
+// and rounds the 20 dropped bits half-to-even; below 2^-6 the codes are the
+// multiples of 2^-9, so |x|*512 rounded half-to-even is the code.
+__device__ __forceinline__ unsigned e4m3_encode(float x) {
+  const unsigned u = __float_as_uint(x);
+  const unsigned sign = (u >> 24) & 0x80u;
+  const unsigned a = u & 0x7FFFFFFFu;
+  unsigned code;
+  if (a > 0x7F800000u) {
+    code = 0x7Fu;
+  } else if (a >= 0x43E00000u) {  // |x| >= 448
+    code = 0x7Eu;
+  } else if (a < 0x3C800000u) {   // |x| < 2^-6
+    code = static_cast<unsigned>(__builtin_rintf(__uint_as_float(a) * 512.0f));
+  } else {
+    const unsigned r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+  }
+  return code | sign;
+}
+
+__device__ __forceinline__ float wave_max_rows(float x) {
+  // lanes l, l^16, l^32, l^48 hold the same head: reduce across them
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum_rows(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// 1. page-tag check
+// ---------------------------------------------------------------------------
+struct VerifyArgs {
+  const int32_t* page_table;
+  const uint32_t* expected;
+  const int32_t* ctx_lens;
+  const uint32_t* tags;
+  uint8_t* abort;
+  int32_t max_pages, num_pages, page_size;
+};
+
+__global__ __launch_bounds__(256) void verify_tags_kernel(VerifyArgs a) {
+  const int b = blockIdx.x;
+  const int ctx = a.ctx_lens[b];
+  int bad = 0;
+  if (ctx < 0) {
+    bad = 1;
+  } else {
+    const int n = (ctx + a.page_size - 1) / a.page_size;
+    if (n > a.max_pages) {
+      bad = 1;
+    } else {
+      const int32_t* pt = a.page_table + static_cast<int64_t>(b) * a.max_pages;
+      const uint32_t* et = a.expected + static_cast<int64_t>(b) * a.max_pages;
+      // four independent entries per thread per round keep loads in flight
+      for (int i0 = threadIdx.x; i0 < n; i0 += 4 * 256) {
+        int32_t id[4];
+        uint32_t ex[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * 256;
+          id[u] = i < n ? pt[i] : 0;
+          ex[u] = i < n ? et[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * 256;
+          if (i < n) {
+            if (static_cast<unsigned>(id[u]) >= static_cast<unsigned>(a.num_pages))
+              bad = 1;
+            else if (a.tags[id[u]] != ex[u])
+              bad = 1;
+          }
+        }
+      }
+    }
+  }
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) a.abort[b] = static_cast<uint8_t>(bad ? 1 : 0);
+}
+
+// ---------------------------------------------------------------------------
+// 2. quantize-on-append
+// ---------------------------------------------------------------------------
+struct AppendArgs {
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int32_t* token_seq;
+  const int32_t* token_pos;
+  const int32_t* page_table;
+  const uint8_t* abort;
+  int64_t page_stride;  // bytes per physical page in one pool
+  int64_t total_items;  // num_tokens * Hkv * 8
+  int32_t num_seqs, max_pages, num_pages, Hkv;
+};
+
+// One thread quantizes 16 consecutive dims of one (token, kv-head) for K and V.
+template <int CACHE>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (item >= a.total_items) return;
+  const int c = static_cast<int>(item & 7);  // dims [16c, 16c+16)
+  const int64_t th = item >> 3;
+  const int h = static_cast<int>(th % a.Hkv);
+  const int64_t tok = th / a.Hkv;
+  const int seq = a.token_seq[tok];
+  const int pos = a.token_pos[tok];
+  if (seq < 0 || seq >= a.num_seqs) return;
+  if (a.abort && a.abort[seq]) return;
+  if (pos < 0 || pos / kPage >= a.max_pages) return;
+  const int32_t pid = a.page_table[static_cast<int64_t>(seq) * a.max_pages + pos / kPage];
+  if (static_cast<unsigned>(pid) >= static_cast<unsigned>(a.num_pages)) return;
+  const int slot = pos % kPage;
+
+  const int64_t src = (tok * a.Hkv + h) * kHeadDim + 16 * c;
+  const u32x4_t* kin = reinterpret_cast<const u32x4_t*>(a.k_new + src);
+  const u32x4_t* vin = reinterpret_cast<const u32x4_t*>(a.v_new + src);
+  const u32x4_t k0 = kin[0], k1 = kin[1], v0 = vin[0], v1 = vin[1];
+  uint16_t kb[16], vb[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    kb[2 * i] = k0[i] & 0xFFFF;
+    kb[2 * i + 1] = k0[i] >> 16;
+    kb[8 + 2 * i] = k1[i] & 0xFFFF;
+    kb[8 + 2 * i + 1] = k1[i] >> 16;
+    vb[2 * i] = v0[i] & 0xFFFF;
+    vb[2 * i + 1] = v0[i] >> 16;
+    vb[8 + 2 * i] = v1[i] & 0xFFFF;
+    vb[8 + 2 * i + 1] = v1[i] >> 16;
+  }
+  const int64_t tile = static_cast<int64_t>(pid) * a.page_stride +
+                       static_cast<int64_t>(h) * Tile<CACHE>::kBytes;
+  uint8_t* kt = a.k_cache + tile;
+  uint8_t* vt = a.v_cache + tile;
+  // K: dims d = 16c+i have f = d%32 = 16(c%2)+i and lane 16(c/2)+slot
+  const int klane = 16 * (c >> 1) + slot;
+  if constexpr (CACHE == FP8KV_E4M3) {
+    const float ks = a.k_scale[h], vs = a.v_scale[h];
+    u32x4_t out = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out[i >> 2] |= e4m3_encode(bf16_to_f32(kb[i]) / ks) << (8 * (i & 3));
+    *reinterpret_cast<u32x4_t*>(kt + (c & 1) * 1024 + 16 * klane) = out;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int d = 16 * c + i;
+      const int f = 4 * (d & 7) + (slot & 3);
+      const int vlane = 16 * (slot >> 2) + (d >> 3);
+      vt[(f >> 4) * 1024 + 16 * vlane + (f & 15)] =
+          static_cast<uint8_t>(e4m3_encode(bf16_to_f32(vb[i]) / vs));
+    }
+  } else {
+    // f = 16(c%2)+i; chunk f/8 = 2(c%2) + i/8: two contiguous 16-byte stores
+    *reinterpret_cast<u32x4_t*>(kt + (2 * (c & 1)) * 1024 + 16 * klane) = k0;
+    *reinterpret_cast<u32x4_t*>(kt + (2 * (c & 1) + 1) * 1024 + 16 * klane) = k1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int d = 16 * c + i;
+      const int f = 4 * (d & 7) + (slot & 3);
+      const int vlane = 16 * (slot >> 2) + (d >> 3);
+      *reinterpret_cast<uint16_t*>(vt + (f >> 3) * 1024 + 16 * vlane + 2 * (f & 7)) = vb[i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. decode: per (request, kv-head, split)
+// ---------------------------------------------------------------------------
+struct DecodeArgs {
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const uint16_t* q;
+  const int32_t* page_table;
+  const int32_t* ctx_lens;
+  const uint8_t* abort;
+  void* out;
+  float* ws_o;   // [B*Hq][max_splits][128] unnormalised weighted V
+  float* ws_ml;  // [B*Hq][max_splits][2]   (running max in log2 units, sum)
+  int64_t page_stride;
+  int32_t max_pages, max_ctx_len, num_pages, Hq, Hkv, G, split_tokens, max_splits, out_f32;
+  float sm_scale;
+};
+
+__device__ __forceinline__ bool request_dead(const DecodeArgs& a, int b, int ctx) {
+  if (ctx <= 0 || ctx > a.max_ctx_len || (ctx + kPage - 1) / kPage > a.max_pages) return true;
+  return a.abort != nullptr && a.abort[b] != 0;
+}
+
+__device__ __forceinline__ void store_out8(const DecodeArgs& a, int64_t idx, const float* v) {
+  if (a.out_f32) {
+    f32x4_t* o = reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + idx);
+    o[0] = f32x4_t{v[0], v[1], v[2], v[3]};
+    o[1] = f32x4_t{v[4], v[5], v[6], v[7]};
+  } else {
+    u32x4_t w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const unsigned lo = __builtin_bit_cast(unsigned short, static_cast<__bf16>(v[2 * i]));
+      const unsigned hi = __builtin_bit_cast(unsigned short, static_cast<__bf16>(v[2 * i + 1]));
+      w[i] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.out) + idx) = w;
+  }
+}
+
+template <int CACHE, int DEPTH>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
+  constexpr int TB = Tile<CACHE>::kBytes;
+  constexpr int NC = Tile<CACHE>::kChunks;
+  __shared__ int s_pid[kMaxSplitPages];
+  __shared__ float s_acc[kWaves][32][64];
+  __shared__ float s_m[kWaves][16];
+  __shared__ float s_l[kWaves][16];
+
+  const int lane = threadIdx.x & 63;
+  // wave index is uniform per wave; say so, so that page addresses and buffer
+  // descriptors derived from it stay in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;   // head within the group (MFMA column)
+  const int qd = lane >> 4;  // lane quarter
+
+  int bid = blockIdx.x;
+  const int g = bid % a.Hkv;
+  bid /= a.Hkv;
+  const int split = bid % a.max_splits;
+  const int b = bid / a.max_splits;
+  const int ctx = a.ctx_lens[b];
+
+  if (request_dead(a, b, ctx)) {
+    // fail closed: +0 rows, nothing read from the cache
+    if (split == 0) {
+      const int64_t base = (static_cast<int64_t>(b) * a.Hq + g * a.G) * kHeadDim;
+      const int cnt = a.G * kHeadDim;
+      for (int i = threadIdx.x; i < cnt; i += kThreads) {
+        if (a.out_f32)
+          static_cast<float*>(a.out)[base + i] = 0.0f;
+        else
+          static_cast<uint16_t*>(a.out)[base + i] = 0;
+      }
+    }
+    return;
+  }
+  const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
+  if (split >= nsplit) return;
+  const int tok0 = split * a.split_tokens;
+  const int tok1 = min(ctx, tok0 + a.split_tokens);
+  const int pg0 = tok0 / kPage;
+  const int np = (tok1 + kPage - 1) / kPage - pg0;
+  const int32_t* ptrow = a.page_table + static_cast<int64_t>(b) * a.max_pages + pg0;
+  for (int i = threadIdx.x; i < np; i += kThreads) s_pid[i] = ptrow[i];
+
+  // Q fragment (B operand of the QK^T MFMA): lane (n, qd) holds, for step kk,
+  // q[head n][32 qd + 8 kk + i], i < 8.  Heads beyond the group are zero.
+  bf16x8_t qf[4];
+  {
+    const int hq = g * a.G + n;
+    const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(
+        a.q + (static_cast<int64_t>(b) * a.Hq + hq) * kHeadDim + 32 * qd);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4_t w = {0u, 0u, 0u, 0u};
+      if (n < a.G) w = qrow[kk];
+      qf[kk] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+  // scores in log2 units: s = (q.k_code) * sm_scale * k_scale * log2(e)
+  const float sc = a.sm_scale * (a.k_scale ? a.k_scale[g] : 1.0f) * kLog2e;
+  __syncthreads();
+
+  // this wave's pages: page index pg0 + wave + kWaves*i, i < npw
+  const int npw = (np - wave + kWaves - 1) / kWaves;
+  const int iters = (npw + DEPTH - 1) / DEPTH * DEPTH;
+
+  f32x4_t acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // running max for head n (log2 units)
+  float l_run = 0.f;        // this lane's share of the softmax denominator
+
+  u32x4_t kr[DEPTH][NC], vr[DEPTH][NC];
+  bool okp[DEPTH];
+
+  auto issue = [&](int i, int slot) {
+    const int li = min(wave + kWaves * i, np - 1);
+    int pid = __builtin_amdgcn_readfirstlane(s_pid[li]);
+    const bool ok = (i < npw) && static_cast<unsigned>(pid) < static_cast<unsigned>(a.num_pages);
+    const int64_t off = ok ? static_cast<int64_t>(pid) * a.page_stride +
+                                 static_cast<int64_t>(g) * TB
+                           : 0;
+    const auto krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_cache + off),
+                                                       (short)0, ok ? TB : 0, kRsrcWord3);
+    const auto vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_cache + off),
+                                                       (short)0, ok ? TB : 0, kRsrcWord3);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      kr[slot][c] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, c * 1024 + lane * 16, 0, 0));
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      vr[slot][c] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, c * 1024 + lane * 16, 0, 0));
+    okp[slot] = ok;
+  };
+
+#pragma unroll
+  for (int s = 0; s < DEPTH; ++s) issue(s, s);
+
+  for (int i0 = 0; i0 < iters; i0 += DEPTH) {
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) {
+      const int i = i0 + s;
+      const int pg = pg0 + wave + kWaves * i;
+      int valid = okp[s] ? min(ctx - pg * kPage, kPage) : 0;
+
+      // ---- S^T = K Q^T : rows = 16 tokens, cols = 16 heads --------------
+      f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8_t kfrag;
+        if constexpr (CACHE == FP8KV_E4M3) {
+          const u32x4_t w = kr[s][kk >> 1];
+          kfrag = (kk & 1) ? e4m3x8_to_bf16(w.z, w.w) : e4m3x8_to_bf16(w.x, w.y);
+        } else {
+          kfrag = __builtin_bit_cast(bf16x8_t, kr[s][kk]);
+        }
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[kk], st, 0, 0, 0);
+      }
+      // lane (n, qd) now holds scores of head n for tokens 4qd + r
+      float sv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[r] = st[r] * sc;
+      u32x4_t vmask = {~0u, ~0u, ~0u, ~0u};
+      if (valid < kPage) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * qd + r >= valid) sv[r] = -INFINITY;
+        // tokens past the end may hold any bytes: clear their V so 0*x stays 0
+        const int keep = min(max(valid - 4 * qd, 0), 4);  // tokens 4qd+j, j<keep
+        if constexpr (CACHE == FP8KV_E4M3) {
+          const unsigned m = keep >= 4 ? ~0u : ((1u << (8 * keep)) - 1u);
+          vmask = u32x4_t{m, m, m, m};
+        } else {
+          const unsigned m0 = keep >= 2 ? ~0u : (keep == 1 ? 0xFFFFu : 0u);
+          const unsigned m1 = keep >= 4 ? ~0u : (keep == 3 ? 0xFFFFu : 0u);
+          vmask = u32x4_t{m0, m1, m0, m1};
+        }
+      }
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mx = wave_max_rows(mx);
+      const float m_new = fmaxf(m_run, mx);
+      if (__any(m_new > m_run)) {
+        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sv[r] - mref);
+      l_run += (p[0] + p[1]) + (p[2] + p[3]);
+
+      // ---- O^T += V^T P^T : rows = dims 8m + t (tile t), cols = heads ----
+      if constexpr (CACHE == FP8KV_E4M3) {
+        // P split into two f16 terms (hi + lo) so the weights keep ~22 bits
+        f16x4_t ph, pl;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          ph[r] = static_cast<_Float16>(p[r]);
+          pl[r] = static_cast<_Float16>(p[r] - static_cast<float>(ph[r]));
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const unsigned w = vr[s][t >> 2][t & 3] & vmask[t & 3];
+          const f16x4_t vfrag = e4m3x4_to_f16(w);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(vfrag, ph, acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(vfrag, pl, acc[t], 0, 0, 0);
+        }
+      } else {
+        s16x4_t ph, pl;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const __bf16 h = static_cast<__bf16>(p[r]);
+          ph[r] = __builtin_bit_cast(short, h);
+          pl[r] = __builtin_bit_cast(short, static_cast<__bf16>(p[r] - static_cast<float>(h)));
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const u32x4_t w = vr[s][t >> 1];
+          u32x2_t pair;
+          pair.x = ((t & 1) ? w.z : w.x) & vmask.x;
+          pair.y = ((t & 1) ? w.w : w.y) & vmask.y;
+          const s16x4_t vfrag = __builtin_bit_cast(s16x4_t, pair);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vfrag, ph, acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vfrag, pl, acc[t], 0, 0, 0);
+        }
+      }
+      issue(i + DEPTH, s);
+    }
+  }
+
+  // ---- merge the 4 waves through LDS ----------------------------------
+  l_run = wave_sum_rows(l_run);
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_acc[wave][t * 4 + r][lane] = acc[t][r];
+  if (qd == 0) {
+    s_m[wave][n] = m_run;
+    s_l[wave][n] = l_run;
+  }
+  __syncthreads();
+  // wave w merges accumulator row r = w: dims d = 32 qd + 8 w + t, t < 8
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][n]);
+  float e[kWaves];
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float mw = s_m[w][n];
+    e[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+    L += e[w] * s_l[w][n];
+  }
+  float O[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) o += e[w] * s_acc[w][t * 4 + wave][lane];
+    O[t] = o;
+  }
+  if (n < a.G) {
+    const int64_t row = static_cast<int64_t>(b) * a.Hq + g * a.G + n;
+    const int d0 = 32 * qd + 8 * wave;
+    if (nsplit == 1) {
+      const float inv = L > 0.f ? (a.v_scale ? a.v_scale[g] : 1.0f) / L : 0.f;
+      float v[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[t] = O[t] * inv;
+      store_out8(a, row * kHeadDim + d0, v);
+    } else {
+      const int64_t pidx = row * a.max_splits + split;
+      f32x4_t* po = reinterpret_cast<f32x4_t*>(a.ws_o + pidx * kHeadDim + d0);
+      po[0] = f32x4_t{O[0], O[1], O[2], O[3]};
+      po[1] = f32x4_t{O[4], O[5], O[6], O[7]};
+      if (qd == 0 && wave == 0) {
+        a.ws_ml[pidx * 2] = M;
+        a.ws_ml[pidx * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4. log-sum-exp merge of split partials, one wave per (request, q-head)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int32_t batch) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= static_cast<int64_t>(batch) * a.Hq) return;
+  const int b = static_cast<int>(row / a.Hq);
+  const int h = static_cast<int>(row % a.Hq);
+  const int g = h / a.G;
+  const int ctx = a.ctx_lens[b];
+  if (request_dead(a, b, ctx)) return;
+  const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
+  if (nsplit <= 1) return;
+  const float* ml = a.ws_ml + row * a.max_splits * 2;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * s]);
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float ms = ml[2 * s];
+    const float e = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
+    L += e * ml[2 * s + 1];
+    const float* po = a.ws_o + (row * a.max_splits + s) * kHeadDim + 2 * lane;
+    o0 += e * po[0];
+    o1 += e * po[1];
+  }
+  const float inv = L > 0.f ? (a.v_scale ? a.v_scale[g] : 1.0f) / L : 0.f;
+  const int64_t idx = row * kHeadDim + 2 * lane;
+  if (a.out_f32) {
+    static_cast<float*>(a.out)[idx] = o0 * inv;
+    static_cast<float*>(a.out)[idx + 1] = o1 * inv;
+  } else {
+    const unsigned lo = __builtin_bit_cast(unsigned short, static_cast<__bf16>(o0 * inv));
+    const unsigned hi = __builtin_bit_cast(unsigned short, static_cast<__bf16>(o1 * inv));
+    *reinterpret_cast<unsigned*>(static_cast<uint16_t*>(a.out) + idx) = lo | (hi << 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// self-test of the conversions used above
+// ---------------------------------------------------------------------------
+__global__ void debug_convert_kernel(const uint8_t* codes, float* out, int n, int which) {
+  const int i = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= n) return;
+  const unsigned w = *reinterpret_cast<const unsigned*>(codes + i);
+  if (which == 0) {
+    const bf16x8_t v = e4m3x8_to_bf16(w, 0u);
+    for (int j = 0; j < 4; ++j) out[i + j] = static_cast<float>(v[j]);
+  } else {
+    const f16x4_t v = e4m3x4_to_f16(w);
+    for (int j = 0; j < 4; ++j) out[i + j] = static_cast<float>(v[j]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host helpers
+// ---------------------------------------------------------------------------
+fp8kv_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return FP8KV_OK;
+  fp8kv_detail::record_hip_error(static_cast<int32_t>(e));
+  return FP8KV_HIP_ERROR;
+}
+
+fp8kv_status launched() { return hip_status(hipGetLastError()); }
+
+fp8kv_status check_desc(const fp8kv_cache_desc* d) {
+  if (!d) return FP8KV_INVALID_ARG;
+  if (d->page_size != kPage || d->head_dim != kHeadDim) return FP8KV_UNSUPPORTED;
+  if (d->cache_dtype != FP8KV_E4M3 && d->cache_dtype != FP8KV_BF16) return FP8KV_UNSUPPORTED;
+  if (d->num_pages <= 0 || d->num_kv_heads <= 0) return FP8KV_INVALID_ARG;
+  return FP8KV_OK;
+}
+
+int tile_bytes(const fp8kv_cache_desc* d) {
+  return d->cache_dtype == FP8KV_E4M3 ? Tile<FP8KV_E4M3>::kBytes : Tile<FP8KV_BF16>::kBytes;
+}
+
+// Split size: aim for about kTargetUnits (request, kv-head, split) workgroups
+// so that every CU holds several, with splits a multiple of 64 tokens
+// (4 waves x 16-token pages).
+constexpr int kTargetUnits = 2048;
+
+int plan_split_tokens(const fp8kv_cache_desc* d, int batch, int max_ctx, int requested) {
+  if (requested > 0) return requested;
+  const int64_t pairs = static_cast<int64_t>(batch) * d->num_kv_heads;
+  int64_t splits = pairs > 0 ? (kTargetUnits + pairs - 1) / pairs : 1;
+  if (splits < 1) splits = 1;
+  int64_t t = (static_cast<int64_t>(max_ctx) + splits - 1) / splits;
+  t = (t + 63) / 64 * 64;
+  if (t < 256) t = 256;
+  if (t > kMaxSplitTokens) t = kMaxSplitTokens;
+  return static_cast<int>(t);
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char* fp8kv_status_string(fp8kv_status s) {
+  switch (s) {
+    case FP8KV_OK: return "ok";
+    case FP8KV_INVALID_ARG: return "invalid argument";
+    case FP8KV_UNSUPPORTED: return "unsupported shape or dtype";
+    case FP8KV_OUT_OF_PAGES: return "out of pages";
+    case FP8KV_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case FP8KV_HIP_ERROR: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int32_t fp8kv_last_hip_error(void) { return fp8kv_detail::g_last_hip_error; }
+
+size_t fp8kv_cache_bytes(const fp8kv_cache_desc* d) {
+  if (check_desc(d) != FP8KV_OK) return 0;
+  return static_cast<size_t>(d->num_pages) * d->num_kv_heads * tile_bytes(d);
+}
+
+int64_t fp8kv_cache_offset(const fp8kv_cache_desc* d, int32_t is_v, int32_t page,
+                           int32_t kv_head, int32_t slot, int32_t dim) {
+  if (check_desc(d) != FP8KV_OK) return -1;
+  if (page < 0 || page >= d->num_pages || kv_head < 0 || kv_head >= d->num_kv_heads ||
+      slot < 0 || slot >= kPage || dim < 0 || dim >= kHeadDim)
+    return -1;
+  const int E = d->cache_dtype == FP8KV_E4M3 ? 1 : 2;
+  const int C = 16 / E;
+  int f, lane;
+  if (is_v) {
+    f = 4 * (dim % 8) + slot % 4;
+    lane = 16 * (slot / 4) + dim / 8;
+  } else {
+    f = dim % 32;
+    lane = 16 * (dim / 32) + slot;
+  }
+  const int64_t tile = (static_cast<int64_t>(page) * d->num_kv_heads + kv_head) * tile_bytes(d);
+  return tile + (f / C) * 1024 + 16 * lane + E * (f % C);
+}
+
+fp8kv_status fp8kv_verify_tags(const int32_t* d_page_table, const uint32_t* d_expected_tags,
+                               int32_t max_pages_per_seq, const int32_t* d_ctx_lens,
+                               int32_t batch, const uint32_t* d_pool_tags, int32_t num_pages,
+                               int32_t page_size, uint8_t* d_abort, hipStream_t stream) {
+  if (batch < 0 || max_pages_per_seq < 0 || num_pages < 0 || page_size <= 0)
+    return FP8KV_INVALID_ARG;
+  if (batch == 0) return FP8KV_OK;
+  if (!d_ctx_lens || !d_abort || (max_pages_per_seq > 0 && (!d_page_table || !d_expected_tags)) ||
+      (num_pages > 0 && !d_pool_tags))
+    return FP8KV_INVALID_ARG;
+  VerifyArgs a{d_page_table, d_expected_tags, d_ctx_lens, d_pool_tags, d_abort,
+               max_pages_per_seq, num_pages, page_size};
+  hipLaunchKernelGGL(verify_tags_kernel, dim3(batch), dim3(256), 0, stream, a);
+  return launched();
+}
+
+fp8kv_status fp8kv_append(const fp8kv_cache_desc* desc, void* d_k_cache, void* d_v_cache,
+                          const float* d_k_scale, const float* d_v_scale,
+                          const uint16_t* d_k_new, const uint16_t* d_v_new, int32_t num_tokens,
+                          const int32_t* d_token_seq, const int32_t* d_token_pos,
+                          int32_t num_seqs, const int32_t* d_page_table,
+                          int32_t max_pages_per_seq, const uint8_t* d_abort,
+                          hipStream_t stream) {
+  fp8kv_status st = check_desc(desc);
+  if (st != FP8KV_OK) return st;
+  if (num_tokens < 0 || num_seqs < 0 || max_pages_per_seq < 0) return FP8KV_INVALID_ARG;
+  if (num_tokens == 0) return FP8KV_OK;
+  if (!d_k_cache || !d_v_cache || !d_k_new || !d_v_new || !d_token_seq || !d_token_pos ||
+      !d_page_table)
+    return FP8KV_INVALID_ARG;
+  if (desc->cache_dtype == FP8KV_E4M3 && (!d_k_scale || !d_v_scale)) return FP8KV_INVALID_ARG;
+  AppendArgs a;
+  a.k_cache = static_cast<uint8_t*>(d_k_cache);
+  a.v_cache = static_cast<uint8_t*>(d_v_cache);
+  a.k_scale = d_k_scale;
+  a.v_scale = d_v_scale;
+  a.k_new = d_k_new;
+  a.v_new = d_v_new;
+  a.token_seq = d_token_seq;
+  a.token_pos = d_token_pos;
+  a.page_table = d_page_table;
+  a.abort = d_abort;
+  a.page_stride = static_cast<int64_t>(desc->num_kv_heads) * tile_bytes(desc);
+  a.total_items = static_cast<int64_t>(num_tokens) * desc->num_kv_heads * 8;
+  a.num_seqs = num_seqs;
+  a.max_pages = max_pages_per_seq;
+  a.num_pages = desc->num_pages;
+  a.Hkv = desc->num_kv_heads;
+  const int64_t blocks = (a.total_items + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return FP8KV_INVALID_ARG;
+  if (desc->cache_dtype == FP8KV_E4M3)
+    hipLaunchKernelGGL(append_kernel<FP8KV_E4M3>, dim3(blocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(append_kernel<FP8KV_BF16>, dim3(blocks), dim3(256), 0, stream, a);
+  return launched();
+}
+
+int32_t fp8kv_decode_split_tokens(const fp8kv_cache_desc* desc, int32_t batch,
+                                  int32_t num_q_heads, int32_t max_ctx_len,
+                                  int32_t split_tokens) {
+  (void)num_q_heads;
+  if (check_desc(desc) != FP8KV_OK || batch < 0 || max_ctx_len < 0) return -1;
+  if (split_tokens != 0 &&
+      (split_tokens < kPage || split_tokens > kMaxSplitTokens || split_tokens % kPage != 0))
+    return -1;
+  return plan_split_tokens(desc, batch, max_ctx_len, split_tokens);
+}
+
+size_t fp8kv_decode_workspace_size(const fp8kv_cache_desc* desc, int32_t batch,
+                                   int32_t num_q_heads, int32_t max_ctx_len,
+                                   int32_t split_tokens) {
+  const int32_t t = fp8kv_decode_split_tokens(desc, batch, num_q_heads, max_ctx_len, split_tokens);
+  if (t <= 0 || num_q_heads <= 0) return 0;
+  const int64_t max_splits = (static_cast<int64_t>(max_ctx_len) + t - 1) / t;
+  if (max_splits <= 1) return 0;
+  const int64_t rows = static_cast<int64_t>(batch) * num_q_heads * max_splits;
+  return static_cast<size_t>(rows) * (kHeadDim + 2) * sizeof(float);
+}
+
+fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc* desc, const void* d_k_cache,
+                                    const void* d_v_cache, const float* d_k_scale,
+                                    const float* d_v_scale, const uint16_t* d_q,
+                                    int32_t num_q_heads, const int32_t* d_page_table,
+                                    int32_t max_pages_per_seq, const int32_t* d_ctx_lens,
+                                    int32_t max_ctx_len, int32_t batch, float sm_scale,
+                                    const uint8_t* d_abort, void* d_out, int32_t out_dtype,
+                                    int32_t split_tokens, void* d_workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  fp8kv_status st = check_desc(desc);
+  if (st != FP8KV_OK) return st;
+  if (batch < 0 || max_ctx_len < 0 || max_pages_per_seq < 0 || num_q_heads <= 0)
+    return FP8KV_INVALID_ARG;
+  if (num_q_heads % desc->num_kv_heads != 0) return FP8KV_UNSUPPORTED;
+  const int G = num_q_heads / desc->num_kv_heads;
+  if (G > kMaxGroup) return FP8KV_UNSUPPORTED;
+  if (out_dtype != FP8KV_OUT_BF16 && out_dtype != FP8KV_OUT_F32) return FP8KV_INVALID_ARG;
+  if (batch == 0) return FP8KV_OK;
+  if (!d_k_cache || !d_v_cache || !d_q || !d_ctx_lens || !d_out ||
+      (max_pages_per_seq > 0 && !d_page_table))
+    return FP8KV_INVALID_ARG;
+  if (desc->cache_dtype == FP8KV_E4M3 && (!d_k_scale || !d_v_scale)) return FP8KV_INVALID_ARG;
+  const int32_t T = fp8kv_decode_split_tokens(desc, batch, num_q_heads, max_ctx_len, split_tokens);
+  if (T <= 0) return FP8KV_INVALID_ARG;
+  const size_t need =
+      fp8kv_decode_workspace_size(desc, batch, num_q_heads, max_ctx_len, split_tokens);
+  if (need > 0 && (d_workspace == nullptr || workspace_bytes < need))
+    return FP8KV_WORKSPACE_TOO_SMALL;
+  int64_t max_splits = (static_cast<int64_t>(max_ctx_len) + T - 1) / T;
+  if (max_splits < 1) max_splits = 1;
+  const int64_t blocks = static_cast<int64_t>(batch) * desc->num_kv_heads * max_splits;
+  if (blocks > 0x7FFFFFFF) return FP8KV_INVALID_ARG;
+
+  DecodeArgs a;
+  a.k_cache = static_cast<const uint8_t*>(d_k_cache);
+  a.v_cache = static_cast<const uint8_t*>(d_v_cache);
+  // a BF16 cache holds the values themselves: no scales
+  a.k_scale = desc->cache_dtype == FP8KV_E4M3 ? d_k_scale : nullptr;
+  a.v_scale = desc->cache_dtype == FP8KV_E4M3 ? d_v_scale : nullptr;
+  a.q = d_q;
+  a.page_table = d_page_table;
+  a.ctx_lens = d_ctx_lens;
+  a.abort = d_abort;
+  a.out = d_out;
+  a.ws_o = static_cast<float*>(d_workspace);
+  a.ws_ml = need > 0 ? static_cast<float*>(d_workspace) +
+                           static_cast<int64_t>(batch) * num_q_heads * max_splits * kHeadDim
+                     : nullptr;
+  a.page_stride = static_cast<int64_t>(desc->num_kv_heads) * tile_bytes(desc);
+  a.max_pages = max_pages_per_seq;
+  a.max_ctx_len = max_ctx_len;
+  a.num_pages = desc->num_pages;
+  a.Hq = num_q_heads;
+  a.Hkv = desc->num_kv_heads;
+  a.G = G;
+  a.split_tokens = T;
+  a.max_splits = static_cast<int32_t>(max_splits);
+  a.out_f32 = out_dtype == FP8KV_OUT_F32 ? 1 : 0;
+  a.sm_scale = sm_scale;
+  if (desc->cache_dtype == FP8KV_E4M3) {
+    hipLaunchKernelGGL((decode_split_kernel<FP8KV_E4M3, 3>), dim3(blocks), dim3(kThreads), 0,
+                       stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<FP8KV_BF16, 2>), dim3(blocks), dim3(kThreads), 0,
+                       stream, a);
+  }
+  st = launched();
+  if (st != FP8KV_OK || max_splits <= 1) return st;
+  const int64_t rows = static_cast<int64_t>(batch) * num_q_heads;
+  hipLaunchKernelGGL(combine_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, a, batch);
+  return launched();
+}
+
+fp8kv_status fp8kv_debug_convert_e4m3(const uint8_t* d_codes, float* d_out, int32_t n,
+                                      int32_t which, hipStream_t stream) {
+  if (!d_codes || !d_out || n < 0 || n % 4 != 0 || (which != 0 && which != 1))
+    return FP8KV_INVALID_ARG;
+  if (n == 0) return FP8KV_OK;
+  const int blocks = (n / 4 + 255) / 256;
+  hipLaunchKernelGGL(debug_convert_kernel, dim3(blocks), dim3(256), 0, stream, d_codes, d_out, n,
+                     which);
+  return launched();
+}
+
+}  // extern "C"

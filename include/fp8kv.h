@@ -1,0 +1,231 @@
+/*
+ * fp8kv -- one decode step of paged attention over an FP8 (e4m3) KV cache
+ * with page-tag integrity, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (Cloudflare, "Smaller, faster, safer: running Kimi and GLM at
+ * scale", KV-cache and integrity sections; restated on the commentary page in
+ * "Giving Every Physical Cache Page a 'Generation Number'"):
+ *   - keys and values are stored in 8-bit floating point, e4m3, instead of
+ *     BF16, halving the cache; the attention kernel converts on read;
+ *   - every physical cache page carries a tag that changes whenever the page
+ *     is reallocated; each request records the (page, tag) pairs it expects;
+ *   - before decode reads the cache, a separate batched check compares the
+ *     two; a mismatch aborts that request only (fail closed), and a
+ *     deployment that does not enable the check runs a no-op path.
+ *
+ * Conventions for every entry point below:
+ *   - "d_" pointers are device pointers owned by the caller; "h_" pointers are
+ *     host pointers owned by the caller.  The library keeps no pointer past a
+ *     call's return, allocates no device memory in the hot-path calls and
+ *     never synchronizes the stream.  Work is enqueued on `stream` in call
+ *     order; errors detected on the host are returned before anything is
+ *     enqueued.
+ *   - Device pointers to 16-byte vectors (Q, new K/V rows, cache pools,
+ *     outputs) must be 16-byte aligned.
+ *   - No call throws; each returns an fp8kv_status.  A tag mismatch is data,
+ *     not an error: it sets the request's abort flag.
+ *   - Nothing here is thread-safe for concurrent calls on one pool object.
+ *
+ * Fixed shapes: page_size 16 tokens, head_dim 128.  Hq % Hkv == 0 and the
+ * group size G = Hq / Hkv is at most 16.  Q-head h reads kv-head h / G.
+ *
+ * Cache layout.  One K pool and one V pool per layer, each
+ *     [num_pages][num_kv_heads][tile]
+ * where a tile holds the 16 tokens x 128 dims of one (page, kv-head):
+ * 2048 bytes for e4m3, 4096 bytes for bf16.  Inside a tile the elements are
+ * stored in the order the attention kernel's matrix-core fragments consume
+ * them, so that each of 64 lanes reads its fragment with 16-byte loads and no
+ * reshuffle.  With E = bytes per element (1 or 2), C = 16 / E elements per
+ * 16-byte chunk, and the tile viewed as [2*E chunks-rows][64 lanes][16 bytes]:
+ *   K element (slot s, dim d):  f = d % 32,  lane = 16*(d/32) + s
+ *   V element (slot s, dim d):  f = 4*(d%8) + s%4,  lane = 16*(s/4) + d/8
+ *   byte offset in tile = (f / C) * 1024 + 16 * lane + E * (f % C)
+ * fp8kv_cache_offset() evaluates this formula.
+ */
+#ifndef FP8KV_H
+#define FP8KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t fp8kv_status;
+enum {
+  FP8KV_OK = 0,
+  FP8KV_INVALID_ARG = -1,          /* null pointer, negative size, bad id    */
+  FP8KV_UNSUPPORTED = -2,          /* page_size != 16, head_dim != 128, G>16 */
+  FP8KV_OUT_OF_PAGES = -3,         /* pool has fewer free pages than asked   */
+  FP8KV_WORKSPACE_TOO_SMALL = -4,  /* decode workspace below the query size  */
+  FP8KV_HIP_ERROR = -5             /* a HIP call failed: fp8kv_last_hip_error */
+};
+
+enum { FP8KV_E4M3 = 0, FP8KV_BF16 = 1 };          /* cache element type       */
+enum { FP8KV_OUT_BF16 = 0, FP8KV_OUT_F32 = 1 };   /* attention output type    */
+
+typedef struct {
+  int32_t num_pages;     /* physical pages in each pool                        */
+  int32_t page_size;     /* tokens per page; must be 16                        */
+  int32_t num_kv_heads;  /* Hkv                                                */
+  int32_t head_dim;      /* must be 128                                        */
+  int32_t cache_dtype;   /* FP8KV_E4M3 or FP8KV_BF16                           */
+} fp8kv_cache_desc;
+
+/* Human-readable name of a status code (static string). */
+const char *fp8kv_status_string(fp8kv_status status);
+
+/* The hipError_t of the last failing HIP call made by this library on the
+ * calling thread (0 if none). */
+int32_t fp8kv_last_hip_error(void);
+
+/* Bytes of ONE pool (K or V) for this descriptor; 0 if the descriptor is
+ * invalid. */
+size_t fp8kv_cache_bytes(const fp8kv_cache_desc *desc);
+
+/* Byte offset of element (page, kv_head, slot, dim) inside a pool, following
+ * the layout above; `is_v` selects the V order.  -1 if out of range. */
+int64_t fp8kv_cache_offset(const fp8kv_cache_desc *desc, int32_t is_v, int32_t page,
+                           int32_t kv_head, int32_t slot, int32_t dim);
+
+/* ------------------------------------------------------------------------ */
+/* Page pool: free list and one generation tag per physical page.            */
+/* The pages' integrity scheme: a page's tag changes every time the page is  */
+/* handed out again (integrity section; "Generation Number" section).  Here  */
+/* the tag is a uint32 counter, seeded-random at creation and incremented    */
+/* (mod 2^32) on every allocation of the page.  Pages are reused first-in    */
+/* first-out.  The library owns the host object; the caller owns the device  */
+/* tag array (uint32[num_pages]) that fp8kv_pool_sync keeps current.         */
+/* ------------------------------------------------------------------------ */
+typedef struct fp8kv_pool fp8kv_pool;
+
+/* Create a pool of num_pages free pages (ids 0..num_pages-1).  Host only: no
+ * HIP call is made.  *out receives the pool. */
+fp8kv_status fp8kv_pool_create(int32_t num_pages, uint64_t seed, fp8kv_pool **out);
+
+/* Release the pool (waits for its last pending tag upload, if any). */
+void fp8kv_pool_destroy(fp8kv_pool *pool);
+
+/* Take n pages.  On success h_page_ids[0..n) receive the ids and h_tags[0..n)
+ * their new tags (the values a request must record as expected).  If fewer
+ * than n pages are free nothing is taken and FP8KV_OUT_OF_PAGES is returned. */
+fp8kv_status fp8kv_pool_alloc(fp8kv_pool *pool, int32_t n, int32_t *h_page_ids,
+                              uint32_t *h_tags);
+
+/* Return n pages.  Every id must be in range, currently allocated and listed
+ * once; otherwise nothing is freed and FP8KV_INVALID_ARG is returned.  Tags are
+ * not changed on free; they change at the next allocation. */
+fp8kv_status fp8kv_pool_free(fp8kv_pool *pool, int32_t n, const int32_t *h_page_ids);
+
+/* Current tag of a page (0 for an id out of range). */
+uint32_t fp8kv_pool_tag(const fp8kv_pool *pool, int32_t page_id);
+
+/* Number of free pages. */
+int32_t fp8kv_pool_num_free(const fp8kv_pool *pool);
+
+/* Copy the host tags of all num_pages pages into h_tags. */
+fp8kv_status fp8kv_pool_read_tags(const fp8kv_pool *pool, uint32_t *h_tags);
+
+/* Upload the tags changed since the last sync (all tags on the first call)
+ * into d_tags with an asynchronous host-to-device copy on `stream`, so that
+ * it is ordered before a later fp8kv_verify_tags on the same stream.  Uses a
+ * pinned staging buffer owned by the pool; a new sync waits for the previous
+ * upload to leave that buffer. */
+fp8kv_status fp8kv_pool_sync(fp8kv_pool *pool, uint32_t *d_tags, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Batched page-tag check (integrity section of the Cloudflare post; the    */
+/* "Generation Number" pseudocode).  A separate kernel, run before append   */
+/* and attention on the same stream; never fused into attention.            */
+/*   n_b = ceil(d_ctx_lens[b] / page_size)  (the pages attention will read)  */
+/*   d_abort[b] = 1 iff d_ctx_lens[b] < 0, or n_b > max_pages_per_seq, or     */
+/*                some i < n_b has d_page_table[b][i] outside [0, num_pages)  */
+/*                or d_pool_tags[id] != d_expected_tags[b][i]; else 0.        */
+/* d_page_table int32 [batch][max_pages_per_seq]; d_expected_tags uint32,    */
+/* same shape; d_ctx_lens int32 [batch] (tokens the step attends over,       */
+/* i.e. cached tokens + the appended one); d_pool_tags uint32 [num_pages];   */
+/* d_abort uint8 [batch], written for every b.  Entries past n_b are ignored.*/
+/* ------------------------------------------------------------------------ */
+fp8kv_status fp8kv_verify_tags(const int32_t *d_page_table, const uint32_t *d_expected_tags,
+                               int32_t max_pages_per_seq, const int32_t *d_ctx_lens,
+                               int32_t batch, const uint32_t *d_pool_tags, int32_t num_pages,
+                               int32_t page_size, uint8_t *d_abort, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Quantize-on-append: write new tokens' K and V into their cache pages.     */
+/* Token t of num_tokens belongs to request d_token_seq[t] (a row of the     */
+/* page table, < num_seqs) at position p = d_token_pos[t]; it goes to page   */
+/* d_page_table[seq][p / 16], slot p % 16.  For e4m3 every element is        */
+/*     code = E( fl32( bf16(x) / scale[h] ) )                               */
+/* with fl32 the correctly rounded binary32 quotient and E round-to-nearest- */
+/* even onto OCP e4m3 with saturation at +-448 (sign kept, NaN -> 0x7F|sign). */
+/* A BF16 cache stores the input bits unchanged (scales unused).             */
+/* d_k_new / d_v_new: BF16 bits [num_tokens][Hkv][128].  d_k_scale /         */
+/* d_v_scale: fp32 [Hkv] for this layer.  d_abort (nullable, uint8 [num_seqs])*/
+/* skips tokens of aborted requests -- a stale mapping must not write into a */
+/* page now owned by someone else.  Tokens whose request, position or page   */
+/* id is out of range are skipped; nothing outside the pools is written.     */
+/* ------------------------------------------------------------------------ */
+fp8kv_status fp8kv_append(const fp8kv_cache_desc *desc, void *d_k_cache, void *d_v_cache,
+                          const float *d_k_scale, const float *d_v_scale,
+                          const uint16_t *d_k_new, const uint16_t *d_v_new, int32_t num_tokens,
+                          const int32_t *d_token_seq, const int32_t *d_token_pos,
+                          int32_t num_seqs, const int32_t *d_page_table,
+                          int32_t max_pages_per_seq, const uint8_t *d_abort,
+                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Paged decode attention (one query token per request) over the cache,      */
+/* converting e4m3 on read.  For request b and q-head h (kv-head g = h/G):  */
+/*   s_j = sm_scale * k_scale[g] * sum_d q[b][h][d] * DEC(K[j][g][d]),        */
+/*   o   = v_scale[g] * sum_j e^{s_j - max s} DEC(V[j][g]) / sum_j e^{s_j-max s}*/
+/* over the d_ctx_lens[b] tokens j of the request (token j at page           */
+/* d_page_table[b][j/16], slot j%16).  Long contexts are split into chunks of */
+/* split_tokens tokens whose partial (max, sum, weighted V) are merged with a */
+/* log-sum-exp reduction in a fixed order.                                   */
+/*   d_q: BF16 bits [batch][Hq][128];  d_out: [batch][Hq][128] of BF16 bits   */
+/*   (out_dtype FP8KV_OUT_BF16, round-to-nearest-even) or fp32 (FP8KV_OUT_F32).*/
+/*   max_ctx_len: host upper bound of d_ctx_lens (sizes the launch); a        */
+/*   request whose length exceeds it or the table width produces zeros.       */
+/*   d_abort (nullable): requests flagged 1 produce +0 rows and read nothing  */
+/*   from the cache; NULL is the no-op tracker (no check at all).  Without    */
+/*   the check, page ids outside [0, num_pages) are still never dereferenced; */
+/*   their tokens are left out (results for such a request are unspecified).  */
+/*   split_tokens: 0 picks a value from the shapes; otherwise a multiple of   */
+/*   16 in [16, 16384].  d_workspace: at least fp8kv_decode_workspace_size()  */
+/*   bytes for the same arguments (may be NULL when that size is 0).          */
+/* ------------------------------------------------------------------------ */
+int32_t fp8kv_decode_split_tokens(const fp8kv_cache_desc *desc, int32_t batch,
+                                  int32_t num_q_heads, int32_t max_ctx_len,
+                                  int32_t split_tokens);
+
+size_t fp8kv_decode_workspace_size(const fp8kv_cache_desc *desc, int32_t batch,
+                                   int32_t num_q_heads, int32_t max_ctx_len,
+                                   int32_t split_tokens);
+
+fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc *desc, const void *d_k_cache,
+                                    const void *d_v_cache, const float *d_k_scale,
+                                    const float *d_v_scale, const uint16_t *d_q,
+                                    int32_t num_q_heads, const int32_t *d_page_table,
+                                    int32_t max_pages_per_seq, const int32_t *d_ctx_lens,
+                                    int32_t max_ctx_len, int32_t batch, float sm_scale,
+                                    const uint8_t *d_abort, void *d_out, int32_t out_dtype,
+                                    int32_t split_tokens, void *d_workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Self-test of the on-read conversion: d_out[i] = the value the attention   */
+/* kernel's e4m3 -> bf16 (which = 0) or e4m3 -> f16 (which = 1) conversion   */
+/* gives for code d_codes[i], widened to fp32.  n a multiple of 4.           */
+/* ------------------------------------------------------------------------ */
+fp8kv_status fp8kv_debug_convert_e4m3(const uint8_t *d_codes, float *d_out, int32_t n,
+                                      int32_t which, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8KV_H */

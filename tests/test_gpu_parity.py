@@ -1,0 +1,240 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Quantized cache bytes and abort flags must match bit for bit; attention
+outputs within 2e-3 (f32 output mode), and the BF16 output must be the
+round-to-nearest-even of the f32 one (see _helpers.check_outputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from _helpers import SM_SCALE, check_outputs, oracle_state, unswizzle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import decode_attention_paged_fp8kv_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def dev():
+    from workloads import device
+    return device
+
+
+def _host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# conversions and quantization
+# ---------------------------------------------------------------------------
+def test_on_read_conversion_all_codes(lib):
+    codes = torch.arange(256, dtype=torch.uint8, device="cuda")
+    tab = oracle.e4m3_table()
+    for which in (0, 1):
+        got = _host(lib.debug_convert_e4m3(codes, which)).astype(np.float64)
+        nan = np.isnan(tab)
+        assert (np.isnan(got) == nan).all(), which
+        assert (got[~nan] == tab[~nan]).all(), which
+        assert (np.signbit(got[~nan]) == np.signbit(tab[~nan])).all(), which
+
+
+@pytest.mark.parametrize("cache_dtype", [0, 1])
+def test_append_every_bf16_pattern(lib, cache_dtype):
+    T, Hkv = 512, 1
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    kn = pats.reshape(T, Hkv, 128)
+    vn = pats[::-1].copy().reshape(T, Hkv, 128)
+    pt = np.arange(32, dtype=np.int32).reshape(1, 32)
+    seq = np.zeros(T, np.int32)
+    pos = np.arange(T, dtype=np.int32)
+    scales = [1.0, 0.0123, float(np.float32(20) / np.float32(448)), 1e-3, 3.3e4, 2.0 ** -10, 7.0]
+    d = lib.desc(32, Hkv, cache_dtype)
+    for s in scales:
+        sc = np.array([s], np.float32)
+        K, V = lib.new_cache(d)
+        lib.append(d, K, V, torch.from_numpy(sc).cuda(), torch.from_numpy(sc).cuda(),
+                   torch.from_numpy(kn.view(np.int16)).cuda(),
+                   torch.from_numpy(vn.view(np.int16)).cuda(),
+                   torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(),
+                   torch.from_numpy(pt).cuda())
+        Ko, Vo = oracle.new_cache(32, Hkv, cache_dtype)
+        oracle.append(Ko, Vo, sc, sc, kn, vn, seq, pos, pt, cache_dtype=cache_dtype)
+        gk = unswizzle(_host(K), Hkv, cache_dtype, range(32), False)
+        gv = unswizzle(_host(V), Hkv, cache_dtype, range(32), True)
+        bad_k = np.flatnonzero(gk.ravel() != Ko.ravel())
+        bad_v = np.flatnonzero(gv.ravel() != Vo.ravel())
+        assert bad_k.size == 0 and bad_v.size == 0, (s, bad_k[:8], bad_v[:8])
+
+
+# ---------------------------------------------------------------------------
+# tag check
+# ---------------------------------------------------------------------------
+def test_verify_hand_cases_and_random(lib):
+    from test_oracle_verify import _load_cases
+    pool, cases = _load_cases()
+    tags = np.array([pool[i] for i in range(len(pool))], np.uint32)
+    P = max(len(c[2]) for c in cases)
+    pt = np.full((len(cases), P), -1, np.int32)
+    et = np.zeros((len(cases), P), np.uint32)
+    cl = np.zeros(len(cases), np.int32)
+    for b, (_, ctx, ids, tg, _) in enumerate(cases):
+        pt[b, :len(ids)] = ids
+        et[b, :len(tg)] = tg
+        cl[b] = ctx
+    exp = np.array([c[4] for c in cases], np.uint8)
+    ab = lib.verify_tags(torch.from_numpy(pt).cuda(), torch.from_numpy(et.view(np.int32)).cuda(),
+                         torch.from_numpy(cl).cuda(), torch.from_numpy(tags.view(np.int32)).cuda())
+    assert (_host(ab) == exp).all()
+    rng = np.random.default_rng(21)
+    for trial in range(10):
+        N = int(rng.integers(1, 5000))
+        tags = rng.integers(0, 2 ** 32, N, dtype=np.uint64).astype(np.uint32)
+        B = int(rng.integers(1, 300))
+        P = int(rng.integers(1, 3000))
+        ptr = rng.integers(0, N, size=(B, P)).astype(np.int32)
+        bad = rng.random((B, P)) < 0.0005
+        ptr[bad] = rng.choice(np.array([-1, -7, N, N + 5], np.int32), size=int(bad.sum()))
+        ok = (ptr >= 0) & (ptr < N)
+        etr = np.where(ok, tags[np.clip(ptr, 0, N - 1)], 0).astype(np.uint32)
+        etr[rng.random((B, P)) < 0.001] += np.uint32(1)
+        clr = rng.integers(-1, P * 16 + 40, B).astype(np.int32)
+        exp = oracle.verify(ptr, etr, clr, tags)
+        got = lib.verify_tags(torch.from_numpy(ptr).cuda(), torch.from_numpy(etr.view(np.int32)).cuda(),
+                              torch.from_numpy(clr).cuda(), torch.from_numpy(tags.view(np.int32)).cuda())
+        assert (_host(got) == exp).all(), trial
+
+
+# ---------------------------------------------------------------------------
+# full step on the tiny workload
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cache_dtype", [0, 1])
+def test_tiny_step_parity(lib, dev, cache_dtype):
+    w = workloads.make(1)
+    st = dev.build(w, cache_dtype=cache_dtype)
+    out16 = st.step(check_tags=True)
+    out32 = st.decode(out_dtype=lib.OUT_F32)
+    ab = _host(st.abort)
+    exp_ab = oracle.verify(w.page_table, w.expected_tags, w.ctx_lens, w.pool_tags)
+    assert (ab == exp_ab).all() and (ab == 0).all()
+    Ko, Vo = oracle_state(w, st.k_scale_host, st.v_scale_host, cache_dtype, abort=exp_ab)
+    pages = np.arange(w.num_pages)
+    gk = unswizzle(_host(st.K), w.Hkv, cache_dtype, pages, False)
+    gv = unswizzle(_host(st.V), w.Hkv, cache_dtype, pages, True)
+    assert (gk == Ko).all() and (gv == Vo).all()
+    ref, _ = oracle.attention(Ko, Vo, st.k_scale_host, st.v_scale_host, w.q_bits(), w.page_table,
+                              w.ctx_lens, SM_SCALE, abort=exp_ab, cache_dtype=cache_dtype)
+    err = check_outputs(_host(out32), _host(out16.view(torch.int16)), ref)
+    print(f"tiny cache_dtype={cache_dtype} max abs err {err:.3e}")
+
+
+# ---------------------------------------------------------------------------
+# shapes, lengths, splits
+# ---------------------------------------------------------------------------
+EDGE_LENS = [0, 1, 14, 15, 16, 17, 30, 31, 32, 47, 63, 64, 65, 127, 255, 256, 300, 1023, 2100]
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 4), (2, 2), (4, 2), (8, 1), (16, 1), (8, 3)])
+@pytest.mark.parametrize("split", [0, 16, 64, 272])
+def test_lengths_groups_splits(lib, dev, G, Hkv, split):
+    w = workloads.custom("edge", EDGE_LENS, Hq=G * Hkv, Hkv=Hkv, seed=G * 10 + Hkv, pool_slack=5)
+    st = dev.build(w, split_tokens=split)
+    out16 = st.step(check_tags=True)
+    out32 = st.decode(out_dtype=lib.OUT_F32)
+    Ko, Vo = oracle_state(w, st.k_scale_host, st.v_scale_host)
+    ref, _ = oracle.attention(Ko, Vo, st.k_scale_host, st.v_scale_host, w.q_bits(), w.page_table,
+                              w.ctx_lens, SM_SCALE)
+    err = check_outputs(_host(out32), _host(out16.view(torch.int16)), ref)
+    assert err < 1e-4
+
+
+def test_empty_context_and_abort_rows_are_zero(lib, dev):
+    w = workloads.custom("edge", [40, 100, 7, 300], Hq=8, Hkv=2, seed=3)
+    st = dev.build(w, split_tokens=64)
+    st.step(check_tags=True)
+    ref = _host(st.decode(out_dtype=lib.OUT_F32)).copy()
+    cl = st.ctx_lens.clone()
+    st.ctx_lens[1] = 0                       # empty context
+    st.abort.copy_(torch.tensor([0, 0, 1, 0], dtype=torch.uint8))
+    out = _host(st.decode(out_dtype=lib.OUT_F32))
+    assert (out[1] == 0).all() and (out[2] == 0).all() and not np.signbit(out[1:3]).any()
+    assert (out[0] == ref[0]).all() and (out[3] == ref[3]).all()
+    st.ctx_lens.copy_(cl)
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+def test_bitwise_invariants(lib, dev):
+    w = workloads.custom("inv", [100, 33, 700, 1500, 16, 2047], Hq=16, Hkv=2, seed=5, pool_slack=7)
+    st = dev.build(w, split_tokens=256)
+    out = _host(st.step(check_tags=True).view(torch.int16)).copy()
+    # run-to-run determinism
+    for _ in range(3):
+        assert (_host(st.decode().view(torch.int16)) == out).all()
+    # permute physical pages (move the tiles, rewrite the page table): identical
+    N = w.num_pages
+    perm = torch.from_numpy(np.random.default_rng(1).permutation(N)).cuda()
+    tile = st.K.numel() // N
+    K2 = torch.empty_like(st.K).view(N, tile)
+    V2 = torch.empty_like(st.V).view(N, tile)
+    K2[perm] = st.K.view(N, tile)
+    V2[perm] = st.V.view(N, tile)
+    pt2 = torch.where(st.page_table >= 0, perm[st.page_table.clamp(min=0).long()].int(),
+                      st.page_table)
+    out2 = lib.decode_attention(st.desc, K2.view(-1), V2.view(-1), st.k_scale, st.v_scale, st.q,
+                                pt2.contiguous(), st.ctx_lens, st.max_ctx_len,
+                                split_tokens=st.split_tokens)
+    assert (_host(out2.view(torch.int16)) == out).all()
+    # reorder the batch: the output rows move with it, bit for bit
+    order = torch.tensor([3, 0, 5, 1, 4, 2], device="cuda")
+    out3 = lib.decode_attention(st.desc, st.K, st.V, st.k_scale, st.v_scale,
+                                st.q[order].contiguous(), st.page_table[order].contiguous(),
+                                st.ctx_lens[order].contiguous(), st.max_ctx_len,
+                                split_tokens=st.split_tokens)
+    assert (_host(out3.view(torch.int16)) == out[order.cpu().numpy()]).all()
+    # a different split size agrees within tolerance (different merge order)
+    f1 = _host(st.decode(out_dtype=lib.OUT_F32, split_tokens=256)).copy()
+    f2 = _host(st.decode(out_dtype=lib.OUT_F32, split_tokens=16384))
+    assert np.abs(f1 - f2).max() < 1e-5
+
+
+def test_abort_isolation(lib, dev):
+    """Stale tags: aborted requests get +0 rows and write nothing; the others
+    are bit-identical to a run in which the stale requests never existed."""
+    w = workloads.make(5, batch=24)
+    st = dev.build(w)
+    K0, V0 = st.K.clone(), st.V.clone()
+    out = _host(st.step(check_tags=True).view(torch.int16)).copy()
+    ab = _host(st.abort)
+    exp_ab = w.expected_abort
+    assert (ab == exp_ab).all() and 0 < ab.sum() < w.B
+    assert (out[ab == 1] == 0).all()
+    # the aborted requests' new-token slots are untouched
+    Kh, K0h = _host(st.K), _host(K0)
+    changed = np.flatnonzero(Kh != K0h)
+    d = st.desc
+    for b in np.flatnonzero(ab):
+        L = int(w.ctx_before[b])
+        page = int(w.page_table[b, L // 16])
+        for h in range(w.Hkv):
+            for dim in (0, 77, 127):
+                off = lib.cache_offset(d, 0, page, h, L % 16, dim)
+                assert Kh[off] == K0h[off]
+    assert changed.size > 0
+    # survivors equal a batch made of survivors only
+    keep = np.flatnonzero(ab == 0)
+    kt = torch.from_numpy(keep).cuda()
+    out_k = lib.decode_attention(st.desc, st.K, st.V, st.k_scale, st.v_scale,
+                                 st.q[kt].contiguous(), st.page_table[kt].contiguous(),
+                                 st.ctx_lens[kt].contiguous(), st.max_ctx_len,
+                                 split_tokens=st.split_tokens)
+    assert (_host(out_k.view(torch.int16)) == out[keep]).all()

@@ -54,3 +54,11 @@ def test_configs():
 def test_scales_recipe():
     s = workloads.scales_from_amax(np.array([448.0, 0.0, 20.0], np.float32))
     assert s[0] == 1.0 and s[1] == 1.0 and s[2] == np.float32(20.0) / np.float32(448.0)
+
+
+def test_keys_independent_of_integer_type():
+    assert workloads.stream_key(np.int64(3), 2, np.int64(63)) == workloads.stream_key(3, 2, 63)
+    w = workloads.make(1)
+    a = w.kv_tokens("k", np.int64(2), 0, 5)
+    b = w.kv_tokens("k", 2, 0, 5)
+    assert (a == b).all()

@@ -75,7 +75,7 @@ def _hash_np(x: np.ndarray) -> np.ndarray:
 
 
 def _hash_scalar(x: int) -> int:
-    x &= _M32
+    x = int(x) & _M32
     x ^= x >> 16
     x = (x * _C1) & _M32
     x ^= x >> 15
@@ -94,6 +94,7 @@ def _hash_torch(x):
 
 
 def stream_key(seed: int, tensor_id: int, row: int) -> int:
+    seed, tensor_id, row = int(seed), int(tensor_id), int(row)   # never numpy ints
     k = _hash_scalar(seed * 0x9E3779B1 + 0x85EBCA77)
     k = _hash_scalar(k ^ (tensor_id * 0xC2B2AE3D))
     return _hash_scalar(k + row * 0x27D4EB2F)
@@ -110,6 +111,7 @@ def draw_bits(key: int, start: int, count: int, backend: str = "numpy",
             return np.zeros(0, np.uint16)
         import torch
         return torch.zeros(0, dtype=torch.int16, device=device)
+    key, start, count = int(key), int(start), int(count)
     if backend == "numpy":
         ctr = np.arange(start, start + count, dtype=np.uint64)
         x = ((ctr + np.uint64(key)) & np.uint64(_M32)).astype(np.uint32)

@@ -1,0 +1,146 @@
+"""Device-resident state for one decode step of a workload.
+
+Inputs are drawn on the device by the torch backend of the seeded generator
+(bit-identical to the numpy backend the oracle side uses).  The cache is then
+filled by the library's own append entry point -- the way a prefill would
+write it -- so every byte in HBM is produced by the product path.  Scales
+follow the workloads' calibration recipe (amax over every generated value of
+a kv-head, / 448), amax being taken with torch on the generated data.
+
+Nothing here computes any part of the method.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+import decode_attention_paged_fp8kv_amd as fp8kv
+
+from . import Workload, scales_from_amax
+
+
+@dataclasses.dataclass
+class DeviceStep:
+    w: Workload
+    desc: "fp8kv.CacheDesc"
+    K: torch.Tensor
+    V: torch.Tensor
+    k_scale: torch.Tensor
+    v_scale: torch.Tensor
+    k_scale_host: np.ndarray
+    v_scale_host: np.ndarray
+    q: torch.Tensor
+    k_new: torch.Tensor
+    v_new: torch.Tensor
+    page_table: torch.Tensor
+    expected_tags: torch.Tensor
+    pool_tags: torch.Tensor
+    ctx_lens: torch.Tensor      # L_b + 1
+    token_seq: torch.Tensor
+    token_pos: torch.Tensor     # L_b
+    abort: torch.Tensor
+    max_ctx_len: int
+    split_tokens: int
+    workspace: Optional[torch.Tensor]
+    out: torch.Tensor
+
+    @property
+    def cache_dtype(self) -> int:
+        return self.desc.cache_dtype
+
+    def verify(self, stream=None):
+        fp8kv.verify_tags(self.page_table, self.expected_tags, self.ctx_lens, self.pool_tags,
+                          abort=self.abort, stream=stream)
+
+    def append(self, use_abort=True, stream=None):
+        fp8kv.append(self.desc, self.K, self.V, self.k_scale, self.v_scale, self.k_new,
+                     self.v_new, self.token_seq, self.token_pos, self.page_table,
+                     abort=self.abort if use_abort else None, stream=stream)
+
+    def decode(self, use_abort=True, out_dtype=fp8kv.OUT_BF16, out=None, stream=None,
+               split_tokens=None):
+        if out is None:
+            out = self.out if out_dtype == fp8kv.OUT_BF16 else torch.empty(
+                self.out.shape, dtype=torch.float32, device=self.out.device)
+        return fp8kv.decode_attention(
+            self.desc, self.K, self.V, self.k_scale, self.v_scale, self.q, self.page_table,
+            self.ctx_lens, self.max_ctx_len, abort=self.abort if use_abort else None, out=out,
+            out_dtype=out_dtype, split_tokens=self.split_tokens if split_tokens is None else split_tokens,
+            workspace=self.workspace, stream=stream)
+
+    def step(self, check_tags=True, out_dtype=fp8kv.OUT_BF16, stream=None):
+        """One decode step: tag check (optional), append, attention."""
+        if check_tags:
+            self.verify(stream)
+        self.append(use_abort=check_tags, stream=stream)
+        return self.decode(use_abort=check_tags, out_dtype=out_dtype, stream=stream)
+
+
+def _bf16(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.bfloat16)
+
+
+def kv_amax(w: Workload, which: str, device) -> np.ndarray:
+    am = torch.zeros(w.Hkv, dtype=torch.float32, device=device)
+    for b in range(w.B):
+        n = int(w.ctx_before[b]) + 1
+        x = _bf16(w.kv_tokens(which, b, 0, n, "torch", device, with_saturation=False))
+        am = torch.maximum(am, x.float().abs().amax(dim=(0, 2)))
+    return am.cpu().numpy()
+
+
+def build(w: Workload, cache_dtype: int = fp8kv.E4M3, device="cuda", split_tokens: int = 0,
+          fill: bool = True, fill_chunk_tokens: int = 1 << 20) -> DeviceStep:
+    d = fp8kv.desc(w.num_pages, w.Hkv, cache_dtype)
+    K, V = fp8kv.new_cache(d, device)
+    ksh = scales_from_amax(kv_amax(w, "k", device))
+    vsh = scales_from_amax(kv_amax(w, "v", device))
+    ks = torch.from_numpy(ksh).to(device)
+    vs = torch.from_numpy(vsh).to(device)
+    pt = torch.from_numpy(np.ascontiguousarray(w.page_table)).to(device)
+    if fill:
+        # history tokens 0..L_b-1 of every request, in chunks
+        seqs, poss, ks_rows, vs_rows, tot = [], [], [], [], 0
+
+        def flush():
+            nonlocal seqs, poss, ks_rows, vs_rows, tot
+            if not seqs:
+                return
+            fp8kv.append(d, K, V, ks, vs, torch.cat(ks_rows), torch.cat(vs_rows),
+                         torch.cat(seqs), torch.cat(poss), pt)
+            seqs, poss, ks_rows, vs_rows, tot = [], [], [], [], 0
+
+        for b in range(w.B):
+            L = int(w.ctx_before[b])
+            for t0 in range(0, L, fill_chunk_tokens):
+                t1 = min(L, t0 + fill_chunk_tokens)
+                ks_rows.append(w.kv_tokens("k", b, t0, t1, "torch", device).contiguous())
+                vs_rows.append(w.kv_tokens("v", b, t0, t1, "torch", device).contiguous())
+                seqs.append(torch.full((t1 - t0,), b, dtype=torch.int32, device=device))
+                poss.append(torch.arange(t0, t1, dtype=torch.int32, device=device))
+                tot += t1 - t0
+                if tot >= fill_chunk_tokens:
+                    flush()
+        flush()
+    q = w.q_bits("torch", device).contiguous()
+    k_new = w.new_kv_bits("k", "torch", device).contiguous()
+    v_new = w.new_kv_bits("v", "torch", device).contiguous()
+    max_ctx = int(w.ctx_lens.max()) if w.B > 0 else 0
+    T = fp8kv.decode_split_tokens(d, w.B, w.Hq, max_ctx, split_tokens)
+    need = fp8kv.decode_workspace_size(d, w.B, w.Hq, max_ctx, split_tokens)
+    ws = torch.empty(need, dtype=torch.uint8, device=device) if need > 0 else None
+    torch.cuda.synchronize()
+    return DeviceStep(
+        w=w, desc=d, K=K, V=V, k_scale=ks, v_scale=vs, k_scale_host=ksh, v_scale_host=vsh,
+        q=q, k_new=k_new, v_new=v_new, page_table=pt,
+        expected_tags=torch.from_numpy(w.expected_tags.view(np.int32).copy()).to(device),
+        pool_tags=torch.from_numpy(w.pool_tags.view(np.int32).copy()).to(device),
+        ctx_lens=torch.from_numpy(w.ctx_lens).to(device),
+        token_seq=torch.arange(w.B, dtype=torch.int32, device=device),
+        token_pos=torch.from_numpy(w.ctx_before.astype(np.int32)).to(device),
+        abort=torch.zeros(w.B, dtype=torch.uint8, device=device),
+        max_ctx_len=max_ctx, split_tokens=T, workspace=ws,
+        out=torch.empty((w.B, w.Hq, 128), dtype=torch.bfloat16, device=device))
