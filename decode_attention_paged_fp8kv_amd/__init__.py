@@ -6,8 +6,9 @@ device memory and the current stream; nothing here computes.  If the library
 is missing the import fails -- there is no fallback.
 
 Names mirror the C ABI in ``include/fp8kv.h``:
-  Pool, verify_tags, append, decode_attention, decode_workspace_size,
-  decode_split_tokens, cache_offset, cache_bytes, debug_convert_e4m3.
+  Pool, verify_tags, append, verify_append, decode_attention,
+  decode_workspace_size, decode_num_workers, cache_offset, cache_bytes,
+  debug_convert_e4m3.
 """
 from __future__ import annotations
 
@@ -68,13 +69,15 @@ _pool_sync = _sig("fp8kv_pool_sync", _i32, [_p, _p, _p])
 _verify = _sig("fp8kv_verify_tags", _i32, [_p, _p, _i32, _p, _i32, _p, _i32, _i32, _p, _p])
 _append = _sig("fp8kv_append", _i32, [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _p, _i32,
                                       _p, _p, _i32, _p, _i32, _p, _p])
-_split_tokens = _sig("fp8kv_decode_split_tokens", _i32,
-                     [ctypes.POINTER(CacheDesc), _i32, _i32, _i32, _i32])
+_num_workers = _sig("fp8kv_decode_num_workers", _i32, [_i32])
 _ws_size = _sig("fp8kv_decode_workspace_size", ctypes.c_size_t,
-                [ctypes.POINTER(CacheDesc), _i32, _i32, _i32, _i32])
+                [ctypes.POINTER(CacheDesc), _i32, _i32, _i32])
 _decode = _sig("fp8kv_decode_attention", _i32,
-               [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32,
+               [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _i32,
                 ctypes.c_float, _p, _p, _i32, _i32, _p, ctypes.c_size_t, _p])
+_verify_append = _sig("fp8kv_verify_append", _i32,
+                      [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _p,
+                       _i32, _p, _p, _p])
 _debug_convert = _sig("fp8kv_debug_convert_e4m3", _i32, [_p, _p, _i32, _i32, _p])
 
 
@@ -225,19 +228,37 @@ def append(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, k_new, v_new, token
                    _dev(abort, _U8, "abort", allow_none=True), _stream(stream)), "append")
 
 
-def decode_split_tokens(d: CacheDesc, batch: int, num_q_heads: int, max_ctx_len: int,
-                        split_tokens: int = 0) -> int:
-    return int(_split_tokens(ctypes.byref(d), batch, num_q_heads, max_ctx_len, split_tokens))
+def verify_append(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, k_new, v_new, new_pos,
+                  page_table, expected_tags, ctx_lens, pool_tags, abort=None, stream=None):
+    """Tag check + the step's append in one launch (one new token per request);
+    returns the uint8 abort tensor [B]."""
+    B = ctx_lens.shape[0]
+    if abort is None:
+        abort = torch.empty(B, dtype=torch.uint8, device=ctx_lens.device)
+    fp8 = d.cache_dtype == E4M3
+    _check(_verify_append(ctypes.byref(d), _dev(k_cache, _U8 + _BITS16, "k_cache"),
+                          _dev(v_cache, _U8 + _BITS16, "v_cache"),
+                          _dev(k_scale, _F32, "k_scale", allow_none=not fp8),
+                          _dev(v_scale, _F32, "v_scale", allow_none=not fp8),
+                          _dev(k_new, _BITS16, "k_new"), _dev(v_new, _BITS16, "v_new"),
+                          _dev(new_pos, _I32, "new_pos"), _dev(page_table, _I32, "page_table"),
+                          _dev(expected_tags, _U32, "expected_tags"), page_table.shape[1],
+                          _dev(ctx_lens, _I32, "ctx_lens"), B, _dev(pool_tags, _U32, "pool_tags"),
+                          _dev(abort, _U8, "abort"), _stream(stream)), "verify_append")
+    return abort
 
 
-def decode_workspace_size(d: CacheDesc, batch: int, num_q_heads: int, max_ctx_len: int,
-                          split_tokens: int = 0) -> int:
-    return int(_ws_size(ctypes.byref(d), batch, num_q_heads, max_ctx_len, split_tokens))
+def decode_num_workers(requested: int = 0) -> int:
+    return int(_num_workers(requested))
+
+
+def decode_workspace_size(d: CacheDesc, batch: int, num_q_heads: int, num_workers: int = 0) -> int:
+    return int(_ws_size(ctypes.byref(d), batch, num_q_heads, num_workers))
 
 
 def decode_attention(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, page_table, ctx_lens,
-                     max_ctx_len: int, abort=None, out=None, out_dtype: int = OUT_BF16,
-                     sm_scale: Optional[float] = None, split_tokens: int = 0, workspace=None,
+                     abort=None, out=None, out_dtype: int = OUT_BF16,
+                     sm_scale: Optional[float] = None, num_workers: int = 0, workspace=None,
                      stream=None):
     """Paged decode attention; returns out [B][Hq][128] (bf16 or f32)."""
     B, Hq, D = q.shape
@@ -246,21 +267,20 @@ def decode_attention(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, page_t
     if out is None:
         out = torch.empty((B, Hq, D), device=q.device,
                           dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32)
-    need = decode_workspace_size(d, B, Hq, max_ctx_len, split_tokens)
-    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    wptr = workspace.data_ptr() if (workspace is not None and need > 0) else None
-    wbytes = workspace.numel() * workspace.element_size() if wptr else 0
+    need = decode_workspace_size(d, B, Hq, num_workers)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     fp8 = d.cache_dtype == E4M3
     _check(_decode(ctypes.byref(d), _dev(k_cache, _U8 + _BITS16, "k_cache"),
                    _dev(v_cache, _U8 + _BITS16, "v_cache"),
                    _dev(k_scale, _F32, "k_scale", allow_none=not fp8),
                    _dev(v_scale, _F32, "v_scale", allow_none=not fp8),
                    _dev(q, _BITS16, "q"), Hq, _dev(page_table, _I32, "page_table"),
-                   page_table.shape[1], _dev(ctx_lens, _I32, "ctx_lens"), max_ctx_len, B,
+                   page_table.shape[1], _dev(ctx_lens, _I32, "ctx_lens"), B,
                    float(sm_scale), _dev(abort, _U8, "abort", allow_none=True),
                    _dev(out, (torch.bfloat16, torch.int16, torch.float32), "out"), out_dtype,
-                   split_tokens, wptr, wbytes, _stream(stream)), "decode_attention")
+                   num_workers, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                   _stream(stream)), "decode_attention")
     return out
 
 

@@ -36,13 +36,23 @@ constexpr int kHeadDim = 128;
 constexpr int kPage = 16;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxSplitTokens = 16384;
-constexpr int kMaxSplitPages = kMaxSplitTokens / kPage;
 constexpr int kMaxGroup = 16;
 // word 3 of a raw buffer resource on gfx9-family parts (32-bit data, no
 // swizzle, no index stride)
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr float kLog2e = 1.4426950408889634f;
+
+// pages in flight per wave (register ring depth), per cache type
+#ifndef FP8KV_DEPTH_E4M3
+#define FP8KV_DEPTH_E4M3 2
+#endif
+#ifndef FP8KV_DEPTH_BF16
+#define FP8KV_DEPTH_BF16 2
+#endif
+// waves per compute unit the automatic worker count aims for
+#ifndef FP8KV_WAVES_PER_CU
+#define FP8KV_WAVES_PER_CU 12
+#endif
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
@@ -198,24 +208,11 @@ struct AppendArgs {
   int32_t num_seqs, max_pages, num_pages, Hkv;
 };
 
-// One thread quantizes 16 consecutive dims of one (token, kv-head) for K and V.
+// Quantize 16 consecutive dims [16c, 16c+16) of token `tok`, kv-head h, into
+// slot `slot` of physical page `pid` (K and V).
 template <int CACHE>
-__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (item >= a.total_items) return;
-  const int c = static_cast<int>(item & 7);  // dims [16c, 16c+16)
-  const int64_t th = item >> 3;
-  const int h = static_cast<int>(th % a.Hkv);
-  const int64_t tok = th / a.Hkv;
-  const int seq = a.token_seq[tok];
-  const int pos = a.token_pos[tok];
-  if (seq < 0 || seq >= a.num_seqs) return;
-  if (a.abort && a.abort[seq]) return;
-  if (pos < 0 || pos / kPage >= a.max_pages) return;
-  const int32_t pid = a.page_table[static_cast<int64_t>(seq) * a.max_pages + pos / kPage];
-  if (static_cast<unsigned>(pid) >= static_cast<unsigned>(a.num_pages)) return;
-  const int slot = pos % kPage;
-
+__device__ __forceinline__ void append_one(const AppendArgs& a, int64_t tok, int h, int c,
+                                           int32_t pid, int slot) {
   const int64_t src = (tok * a.Hkv + h) * kHeadDim + 16 * c;
   const u32x4_t* kin = reinterpret_cast<const u32x4_t*>(a.k_new + src);
   const u32x4_t* vin = reinterpret_cast<const u32x4_t*>(a.v_new + src);
@@ -266,9 +263,105 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
+// One thread per (token, kv-head, 16-dim chunk).
+template <int CACHE>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (item >= a.total_items) return;
+  const int c = static_cast<int>(item & 7);
+  const int64_t th = item >> 3;
+  const int h = static_cast<int>(th % a.Hkv);
+  const int64_t tok = th / a.Hkv;
+  const int seq = a.token_seq[tok];
+  const int pos = a.token_pos[tok];
+  if (seq < 0 || seq >= a.num_seqs) return;
+  if (a.abort && a.abort[seq]) return;
+  if (pos < 0 || pos / kPage >= a.max_pages) return;
+  const int32_t pid = a.page_table[static_cast<int64_t>(seq) * a.max_pages + pos / kPage];
+  if (static_cast<unsigned>(pid) >= static_cast<unsigned>(a.num_pages)) return;
+  append_one<CACHE>(a, tok, h, c, pid, pos % kPage);
+}
+
 // ---------------------------------------------------------------------------
-// 3. decode: per (request, kv-head, split)
+// 3. tag check fused with the step's append (one workgroup per request)
 // ---------------------------------------------------------------------------
+struct VerifyAppendArgs {
+  VerifyArgs v;
+  AppendArgs w;
+  const int32_t* new_pos;  // position of each request's new token
+};
+
+// The check still runs as its own batched pass ahead of attention; fusing it
+// with the append only removes a launch: a request's token is written after
+// (and only if) all of that request's pages passed.
+template <int CACHE>
+__global__ __launch_bounds__(256) void verify_append_kernel(VerifyAppendArgs a) {
+  const int b = blockIdx.x;
+  const int ctx = a.v.ctx_lens[b];
+  const int pos = a.new_pos[b];
+  // the new token's page id and inputs do not depend on the check: load early
+  const bool pos_ok = pos >= 0 && pos / kPage < a.w.max_pages;
+  const int32_t pid =
+      pos_ok ? a.w.page_table[static_cast<int64_t>(b) * a.w.max_pages + pos / kPage] : -1;
+  int bad = 0;
+  if (ctx < 0) {
+    bad = 1;
+  } else {
+    const int n = (ctx + a.v.page_size - 1) / a.v.page_size;
+    if (n > a.v.max_pages) {
+      bad = 1;
+    } else {
+      const int32_t* pt = a.v.page_table + static_cast<int64_t>(b) * a.v.max_pages;
+      const uint32_t* et = a.v.expected + static_cast<int64_t>(b) * a.v.max_pages;
+      for (int i0 = threadIdx.x; i0 < n; i0 += 4 * 256) {
+        int32_t id[4];
+        uint32_t ex[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * 256;
+          id[u] = i < n ? pt[i] : 0;
+          ex[u] = i < n ? et[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * 256;
+          if (i < n) {
+            if (static_cast<unsigned>(id[u]) >= static_cast<unsigned>(a.v.num_pages))
+              bad = 1;
+            else if (a.v.tags[id[u]] != ex[u])
+              bad = 1;
+          }
+        }
+      }
+    }
+  }
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) a.v.abort[b] = static_cast<uint8_t>(bad ? 1 : 0);
+  if (bad || !pos_ok) return;
+  if (static_cast<unsigned>(pid) >= static_cast<unsigned>(a.w.num_pages)) return;
+  const int slot = pos % kPage;
+  for (int item = threadIdx.x; item < a.w.Hkv * 8; item += 256)
+    append_one<CACHE>(a.w, static_cast<int64_t>(b), item >> 3, item & 7, pid, slot);
+}
+
+// ---------------------------------------------------------------------------
+// 4. decode: persistent workgroups, equal work per workgroup
+// ---------------------------------------------------------------------------
+// Work list: for every live request b (in order) and kv-head g, the n_b pages
+// the step reads: W = Hkv * sum_b n_b page-tiles (one tile = 16 tokens of one
+// kv-head: 2 KiB of K + 2 KiB of V for e4m3).  Workgroup w of NWG takes items
+// [w*W/NWG, (w+1)*W/NWG), so every workgroup moves the same number of bytes
+// however ragged the lengths.  Its slice is cut at (request, kv-head)
+// boundaries into pieces; inside a piece the 4 waves take pages round robin,
+// each with its own online softmax, and are merged through LDS at the end of
+// the piece.  A piece that is a whole segment writes the output; any other
+// piece leaves (max, sum, weighted V) in slot  w + segment  (unique per
+// (workgroup, segment) pair) for merge_kernel.
+//
+// Each wave walks its own padded sequence of pages (per piece, its pages
+// rounded up to a multiple of DEPTH with masked dummies), so the register
+// ring slot of every page is known at compile time; loads run DEPTH pages
+// ahead and page ids 2*DEPTH pages ahead, across piece boundaries.
 struct DecodeArgs {
   const uint8_t* k_cache;
   const uint8_t* v_cache;
@@ -279,16 +372,23 @@ struct DecodeArgs {
   const int32_t* ctx_lens;
   const uint8_t* abort;
   void* out;
-  float* ws_o;   // [B*Hq][max_splits][128] unnormalised weighted V
-  float* ws_ml;  // [B*Hq][max_splits][2]   (running max in log2 units, sum)
+  float* ws_o;     // [slots][G][128] unnormalised weighted V
+  float* ws_ml;    // [slots][G][2]   (max in log2 units, sum)
+  int32_t* ws_pre; // [B+1] page prefix sums of live requests (for the merge)
   int64_t page_stride;
-  int32_t max_pages, max_ctx_len, num_pages, Hq, Hkv, G, split_tokens, max_splits, out_f32;
+  int32_t batch, max_pages, num_pages, Hq, Hkv, G, out_f32;
   float sm_scale;
 };
 
-__device__ __forceinline__ bool request_dead(const DecodeArgs& a, int b, int ctx) {
-  if (ctx <= 0 || ctx > a.max_ctx_len || (ctx + kPage - 1) / kPage > a.max_pages) return true;
-  return a.abort != nullptr && a.abort[b] != 0;
+constexpr int kMaxBatch = 4096;
+
+__device__ __forceinline__ int live_pages(const DecodeArgs& a, int b) {
+  const int ctx = a.ctx_lens[b];
+  if (ctx <= 0) return 0;
+  const int n = (ctx + kPage - 1) / kPage;
+  if (n > a.max_pages) return 0;                        // does not fit the table: fail closed
+  if (a.abort != nullptr && a.abort[b] != 0) return 0;  // aborted: +0 rows, nothing read
+  return n;
 }
 
 __device__ __forceinline__ void store_out8(const DecodeArgs& a, int64_t idx, const float* v) {
@@ -308,90 +408,198 @@ __device__ __forceinline__ void store_out8(const DecodeArgs& a, int64_t idx, con
   }
 }
 
+// A piece: the part of segment (b, g) inside this workgroup's slice.
+struct Piece {
+  int b, g, n;   // request, kv-head, pages of the segment
+  int64_t sx;    // work-list index of the segment's first page
+  int64_t ps;    // first item of the piece
+  int64_t pe;    // one past its last item
+};
+
+__device__ __forceinline__ Piece first_piece(const int* s_pre, int B, int Hkv, int64_t X0,
+                                             int64_t X1) {
+  int lo = 0, hi = B;  // largest b with Hkv*pre[b] <= X0 (a live request since X0 < W)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (static_cast<int64_t>(Hkv) * s_pre[mid] <= X0)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  Piece p;
+  p.b = lo;
+  p.n = s_pre[lo + 1] - s_pre[lo];
+  const int64_t sb = static_cast<int64_t>(Hkv) * s_pre[lo];
+  p.g = static_cast<int>((X0 - sb) / p.n);
+  p.sx = sb + static_cast<int64_t>(p.g) * p.n;
+  p.ps = X0;
+  p.pe = min(X1, p.sx + p.n);
+  return p;
+}
+
+// the piece after p inside [.., X1); returns false at the end of the slice
+__device__ __forceinline__ bool next_piece(Piece& p, const int* s_pre, int B, int Hkv,
+                                           int64_t X1) {
+  if (p.pe >= X1) return false;
+  if (p.g + 1 < Hkv) {
+    ++p.g;
+    p.sx += p.n;
+  } else {
+    int b = p.b;
+    do {
+      ++b;
+    } while (b < B && s_pre[b + 1] == s_pre[b]);
+    if (b >= B) return false;
+    p.b = b;
+    p.g = 0;
+    p.n = s_pre[b + 1] - s_pre[b];
+    p.sx = static_cast<int64_t>(Hkv) * s_pre[b];
+  }
+  p.ps = p.sx;
+  p.pe = min(X1, p.sx + p.n);
+  return true;
+}
+
+// pages of piece p that wave `wave` takes (round robin), and that count
+// rounded up to a multiple of `depth`
+__device__ __forceinline__ int wave_count(const Piece& p, int wave) {
+  const int len = static_cast<int>(p.pe - p.ps);
+  return len > wave ? (len - wave + kWaves - 1) / kWaves : 0;
+}
+
+// position in a wave's padded page sequence
+template <int DEPTH>
+struct SeqCursor {
+  Piece p;
+  int i;       // index within the piece's padded run
+  int cnt;     // real pages of this wave in the piece
+  bool done;
+
+  __device__ __forceinline__ void settle(const int* s_pre, int B, int Hkv, int64_t X1,
+                                         int wave) {
+    // skip pieces in which this wave has nothing to do
+    while (!done && (cnt + DEPTH - 1) / DEPTH * DEPTH <= i) {
+      if (!next_piece(p, s_pre, B, Hkv, X1)) {
+        done = true;
+        break;
+      }
+      i = 0;
+      cnt = wave_count(p, wave);
+    }
+  }
+  __device__ __forceinline__ void advance(const int* s_pre, int B, int Hkv, int64_t X1,
+                                          int wave) {
+    ++i;
+    settle(s_pre, B, Hkv, X1, wave);
+  }
+  __device__ __forceinline__ bool real() const { return !done && i < cnt; }
+  // page index within the request
+  __device__ __forceinline__ int page(int wave) const {
+    return static_cast<int>(p.ps - p.sx) + wave + kWaves * i;
+  }
+};
+
 template <int CACHE, int DEPTH>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void decode_kernel(DecodeArgs a) {
   constexpr int TB = Tile<CACHE>::kBytes;
   constexpr int NC = Tile<CACHE>::kChunks;
-  __shared__ int s_pid[kMaxSplitPages];
+  __shared__ int s_pre[kMaxBatch + 1];
+  __shared__ int s_part[kThreads];
   __shared__ float s_acc[kWaves][32][64];
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
 
   const int lane = threadIdx.x & 63;
-  // wave index is uniform per wave; say so, so that page addresses and buffer
-  // descriptors derived from it stay in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;   // head within the group (MFMA column)
   const int qd = lane >> 4;  // lane quarter
+  const int B = a.batch;
 
-  int bid = blockIdx.x;
-  const int g = bid % a.Hkv;
-  bid /= a.Hkv;
-  const int split = bid % a.max_splits;
-  const int b = bid / a.max_splits;
-  const int ctx = a.ctx_lens[b];
-
-  if (request_dead(a, b, ctx)) {
-    // fail closed: +0 rows, nothing read from the cache
-    if (split == 0) {
-      const int64_t base = (static_cast<int64_t>(b) * a.Hq + g * a.G) * kHeadDim;
-      const int cnt = a.G * kHeadDim;
-      for (int i = threadIdx.x; i < cnt; i += kThreads) {
+  // ---- prologue: page prefix sums of the live requests ------------------
+  {
+    const int per = (B + kThreads - 1) / kThreads;
+    const int b0 = min(B, static_cast<int>(threadIdx.x) * per);
+    const int b1 = min(B, b0 + per);
+    int sum = 0;
+    for (int b = b0; b < b1; ++b) {
+      const int np = live_pages(a, b);
+      s_pre[b] = np;
+      sum += np;
+    }
+    s_part[threadIdx.x] = sum;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      int v[4], t = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = s_part[4 * threadIdx.x + i];
+        t += v[i];
+      }
+      int inc = t;  // inclusive scan of the 64 lane totals
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+      }
+      int run = inc - t;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s_part[4 * threadIdx.x + i] = run;
+        run += v[i];
+      }
+      if (threadIdx.x == 63) s_pre[B] = inc;
+    }
+    __syncthreads();
+    int run = s_part[threadIdx.x];
+    for (int b = b0; b < b1; ++b) {
+      const int np = s_pre[b];
+      s_pre[b] = run;
+      run += np;
+    }
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int b = threadIdx.x; b <= B; b += kThreads) a.ws_pre[b] = s_pre[b];
+    // requests with nothing to read get +0 rows (aborted, empty, invalid)
+    for (int b = blockIdx.x; b < B; b += gridDim.x) {
+      if (s_pre[b + 1] != s_pre[b]) continue;
+      const int64_t base = static_cast<int64_t>(b) * a.Hq * kHeadDim;
+      for (int i = threadIdx.x; i < a.Hq * kHeadDim; i += kThreads) {
         if (a.out_f32)
           static_cast<float*>(a.out)[base + i] = 0.0f;
         else
           static_cast<uint16_t*>(a.out)[base + i] = 0;
       }
     }
-    return;
   }
-  const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
-  if (split >= nsplit) return;
-  const int tok0 = split * a.split_tokens;
-  const int tok1 = min(ctx, tok0 + a.split_tokens);
-  const int pg0 = tok0 / kPage;
-  const int np = (tok1 + kPage - 1) / kPage - pg0;
-  const int32_t* ptrow = a.page_table + static_cast<int64_t>(b) * a.max_pages + pg0;
-  for (int i = threadIdx.x; i < np; i += kThreads) s_pid[i] = ptrow[i];
 
-  // Q fragment (B operand of the QK^T MFMA): lane (n, qd) holds, for step kk,
-  // q[head n][32 qd + 8 kk + i], i < 8.  Heads beyond the group are zero.
-  bf16x8_t qf[4];
-  {
-    const int hq = g * a.G + n;
-    const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(
-        a.q + (static_cast<int64_t>(b) * a.Hq + hq) * kHeadDim + 32 * qd);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      u32x4_t w = {0u, 0u, 0u, 0u};
-      if (n < a.G) w = qrow[kk];
-      qf[kk] = __builtin_bit_cast(bf16x8_t, w);
-    }
-  }
-  // scores in log2 units: s = (q.k_code) * sm_scale * k_scale * log2(e)
-  const float sc = a.sm_scale * (a.k_scale ? a.k_scale[g] : 1.0f) * kLog2e;
-  __syncthreads();
+  // ---- this workgroup's slice --------------------------------------------
+  const int64_t W = static_cast<int64_t>(a.Hkv) * s_pre[B];
+  const int64_t NWG = gridDim.x;
+  const int64_t bw = blockIdx.x;
+  const int64_t X0 = bw * W / NWG;
+  const int64_t X1 = (bw + 1) * W / NWG;
+  if (X0 >= X1) return;  // uniform over the workgroup: no barrier follows
 
-  // this wave's pages: page index pg0 + wave + kWaves*i, i < npw
-  const int npw = (np - wave + kWaves - 1) / kWaves;
-  const int iters = (npw + DEPTH - 1) / DEPTH * DEPTH;
-
-  f32x4_t acc[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max for head n (log2 units)
-  float l_run = 0.f;        // this lane's share of the softmax denominator
+  const Piece first = first_piece(s_pre, B, a.Hkv, X0, X1);
+  SeqCursor<DEPTH> I{first, 0, wave_count(first, wave), false};  // next page to load
+  I.settle(s_pre, B, a.Hkv, X1, wave);
+  SeqCursor<DEPTH> J = I;  // next page id to fetch
 
   u32x4_t kr[DEPTH][NC], vr[DEPTH][NC];
   bool okp[DEPTH];
+  int pid_ring[DEPTH];
 
-  auto issue = [&](int i, int slot) {
-    const int li = min(wave + kWaves * i, np - 1);
-    int pid = __builtin_amdgcn_readfirstlane(s_pid[li]);
-    const bool ok = (i < npw) && static_cast<unsigned>(pid) < static_cast<unsigned>(a.num_pages);
-    const int64_t off = ok ? static_cast<int64_t>(pid) * a.page_stride +
-                                 static_cast<int64_t>(g) * TB
-                           : 0;
+  auto fetch_pid = [&]() -> int {
+    int pid = -1;
+    if (J.real()) pid = a.page_table[static_cast<int64_t>(J.p.b) * a.max_pages + J.page(wave)];
+    J.advance(s_pre, B, a.Hkv, X1, wave);
+    return pid;
+  };
+  auto issue = [&](int slot, int pid) {
+    const bool ok = I.real() && static_cast<unsigned>(pid) < static_cast<unsigned>(a.num_pages);
+    const int64_t off =
+        ok ? static_cast<int64_t>(pid) * a.page_stride + static_cast<int64_t>(I.p.g) * TB : 0;
     const auto krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_cache + off),
                                                        (short)0, ok ? TB : 0, kRsrcWord3);
     const auto vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_cache + off),
@@ -405,195 +613,250 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       vr[slot][c] = __builtin_bit_cast(
           u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, c * 1024 + lane * 16, 0, 0));
     okp[slot] = ok;
+    I.advance(s_pre, B, a.Hkv, X1, wave);
   };
 
+  // prime: loads for the first DEPTH pages, page ids for the next DEPTH
 #pragma unroll
-  for (int s = 0; s < DEPTH; ++s) issue(s, s);
-
-  for (int i0 = 0; i0 < iters; i0 += DEPTH) {
+  for (int s = 0; s < DEPTH; ++s) {
+    const int pid = __builtin_amdgcn_readfirstlane(fetch_pid());
+    issue(s, pid);
+  }
 #pragma unroll
-    for (int s = 0; s < DEPTH; ++s) {
-      const int i = i0 + s;
-      const int pg = pg0 + wave + kWaves * i;
-      int valid = okp[s] ? min(ctx - pg * kPage, kPage) : 0;
+  for (int s = 0; s < DEPTH; ++s) pid_ring[s] = fetch_pid();
 
-      // ---- S^T = K Q^T : rows = 16 tokens, cols = 16 heads --------------
-      f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+  Piece P = first;  // piece being processed (all waves visit every piece)
+  for (;;) {
+    const int cnt = wave_count(P, wave);
+    const int iters = (cnt + DEPTH - 1) / DEPTH * DEPTH;
+    const int pg0 = static_cast<int>(P.ps - P.sx) + wave;  // my first page in the piece
+    const int ctx = a.ctx_lens[P.b];
+
+    f32x4_t acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;  // running max for head n (log2 units)
+    float l_run = 0.f;        // this lane's share of the softmax denominator
+
+    if (cnt > 0) {
+      bf16x8_t qf[4];
+      const int hq = P.g * a.G + n;
+      const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(
+          a.q + (static_cast<int64_t>(P.b) * a.Hq + hq) * kHeadDim + 32 * qd);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        bf16x8_t kfrag;
-        if constexpr (CACHE == FP8KV_E4M3) {
-          const u32x4_t w = kr[s][kk >> 1];
-          kfrag = (kk & 1) ? e4m3x8_to_bf16(w.z, w.w) : e4m3x8_to_bf16(w.x, w.y);
-        } else {
-          kfrag = __builtin_bit_cast(bf16x8_t, kr[s][kk]);
-        }
-        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[kk], st, 0, 0, 0);
+        u32x4_t w = {0u, 0u, 0u, 0u};
+        if (n < a.G) w = qrow[kk];
+        qf[kk] = __builtin_bit_cast(bf16x8_t, w);
       }
-      // lane (n, qd) now holds scores of head n for tokens 4qd + r
-      float sv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = st[r] * sc;
-      u32x4_t vmask = {~0u, ~0u, ~0u, ~0u};
-      if (valid < kPage) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (4 * qd + r >= valid) sv[r] = -INFINITY;
-        // tokens past the end may hold any bytes: clear their V so 0*x stays 0
-        const int keep = min(max(valid - 4 * qd, 0), 4);  // tokens 4qd+j, j<keep
-        if constexpr (CACHE == FP8KV_E4M3) {
-          const unsigned m = keep >= 4 ? ~0u : ((1u << (8 * keep)) - 1u);
-          vmask = u32x4_t{m, m, m, m};
-        } else {
-          const unsigned m0 = keep >= 2 ? ~0u : (keep == 1 ? 0xFFFFu : 0u);
-          const unsigned m1 = keep >= 4 ? ~0u : (keep == 3 ? 0xFFFFu : 0u);
-          vmask = u32x4_t{m0, m1, m0, m1};
-        }
-      }
-      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      mx = wave_max_rows(mx);
-      const float m_new = fmaxf(m_run, mx);
-      if (__any(m_new > m_run)) {
-        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc[t] *= alpha;
-        l_run *= alpha;
-        m_run = m_new;
-      }
-      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sv[r] - mref);
-      l_run += (p[0] + p[1]) + (p[2] + p[3]);
+      // scores in log2 units: s = (q.k_code) * sm_scale * k_scale * log2(e)
+      const float sc = a.sm_scale * (a.k_scale ? a.k_scale[P.g] : 1.0f) * kLog2e;
 
-      // ---- O^T += V^T P^T : rows = dims 8m + t (tile t), cols = heads ----
-      if constexpr (CACHE == FP8KV_E4M3) {
-        // P split into two f16 terms (hi + lo) so the weights keep ~22 bits
-        f16x4_t ph, pl;
+      for (int i0 = 0; i0 < iters; i0 += DEPTH) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          ph[r] = static_cast<_Float16>(p[r]);
-          pl[r] = static_cast<_Float16>(p[r] - static_cast<float>(ph[r]));
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const unsigned w = vr[s][t >> 2][t & 3] & vmask[t & 3];
-          const f16x4_t vfrag = e4m3x4_to_f16(w);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(vfrag, ph, acc[t], 0, 0, 0);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(vfrag, pl, acc[t], 0, 0, 0);
-        }
-      } else {
-        s16x4_t ph, pl;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const __bf16 h = static_cast<__bf16>(p[r]);
-          ph[r] = __builtin_bit_cast(short, h);
-          pl[r] = __builtin_bit_cast(short, static_cast<__bf16>(p[r] - static_cast<float>(h)));
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const u32x4_t w = vr[s][t >> 1];
-          u32x2_t pair;
-          pair.x = ((t & 1) ? w.z : w.x) & vmask.x;
-          pair.y = ((t & 1) ? w.w : w.y) & vmask.y;
-          const s16x4_t vfrag = __builtin_bit_cast(s16x4_t, pair);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vfrag, ph, acc[t], 0, 0, 0);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vfrag, pl, acc[t], 0, 0, 0);
-        }
-      }
-      issue(i + DEPTH, s);
-    }
-  }
+        for (int s = 0; s < DEPTH; ++s) {
+          const int i = i0 + s;
+          const int page = pg0 + kWaves * i;
+          const int valid = (i < cnt && okp[s]) ? min(ctx - page * kPage, kPage) : 0;
 
-  // ---- merge the 4 waves through LDS ----------------------------------
-  l_run = wave_sum_rows(l_run);
+          // ---- S^T = K Q^T : rows = 16 tokens, cols = 16 heads ------------
+          f32x4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+          for (int kk = 0; kk < 4; ++kk) {
+            bf16x8_t kfrag;
+            if constexpr (CACHE == FP8KV_E4M3) {
+              const u32x4_t w = kr[s][kk >> 1];
+              kfrag = (kk & 1) ? e4m3x8_to_bf16(w.z, w.w) : e4m3x8_to_bf16(w.x, w.y);
+            } else {
+              kfrag = __builtin_bit_cast(bf16x8_t, kr[s][kk]);
+            }
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[kk], st, 0, 0, 0);
+          }
+          // lane (n, qd) now holds scores of head n for tokens 4qd + r
+          float sv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s_acc[wave][t * 4 + r][lane] = acc[t][r];
-  if (qd == 0) {
-    s_m[wave][n] = m_run;
-    s_l[wave][n] = l_run;
-  }
-  __syncthreads();
-  // wave w merges accumulator row r = w: dims d = 32 qd + 8 w + t, t < 8
-  float M = -INFINITY;
+          for (int r = 0; r < 4; ++r) sv[r] = st[r] * sc;
+          u32x4_t vmask = {~0u, ~0u, ~0u, ~0u};
+          if (valid < kPage) {
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][n]);
-  float e[kWaves];
-  float L = 0.f;
+            for (int r = 0; r < 4; ++r)
+              if (4 * qd + r >= valid) sv[r] = -INFINITY;
+            // tokens past the end may hold any bytes: clear their V so 0*x stays 0
+            const int keep = min(max(valid - 4 * qd, 0), 4);  // tokens 4qd+j, j<keep
+            if constexpr (CACHE == FP8KV_E4M3) {
+              const unsigned m = keep >= 4 ? ~0u : ((1u << (8 * keep)) - 1u);
+              vmask = u32x4_t{m, m, m, m};
+            } else {
+              const unsigned m0 = keep >= 2 ? ~0u : (keep == 1 ? 0xFFFFu : 0u);
+              const unsigned m1 = keep >= 4 ? ~0u : (keep == 3 ? 0xFFFFu : 0u);
+              vmask = u32x4_t{m0, m1, m0, m1};
+            }
+          }
+          float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+          mx = wave_max_rows(mx);
+          const float m_new = fmaxf(m_run, mx);
+          if (__any(m_new > m_run)) {
+            const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const float mw = s_m[w][n];
-    e[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-    L += e[w] * s_l[w][n];
-  }
-  float O[8];
+            for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+            l_run *= alpha;
+            m_run = m_new;
+          }
+          const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+          float p[4];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    float o = 0.f;
+          for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sv[r] - mref);
+          l_run += (p[0] + p[1]) + (p[2] + p[3]);
+
+          // ---- O^T += V^T P^T : rows = dims 8m + t (tile t), cols = heads --
+          if constexpr (CACHE == FP8KV_E4M3) {
+            // P split into two f16 terms (hi + lo) so the weights keep ~22 bits
+            f16x4_t ph, pl;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) o += e[w] * s_acc[w][t * 4 + wave][lane];
-    O[t] = o;
-  }
-  if (n < a.G) {
-    const int64_t row = static_cast<int64_t>(b) * a.Hq + g * a.G + n;
-    const int d0 = 32 * qd + 8 * wave;
-    if (nsplit == 1) {
-      const float inv = L > 0.f ? (a.v_scale ? a.v_scale[g] : 1.0f) / L : 0.f;
-      float v[8];
+            for (int r = 0; r < 4; ++r) {
+              ph[r] = static_cast<_Float16>(p[r]);
+              pl[r] = static_cast<_Float16>(p[r] - static_cast<float>(ph[r]));
+            }
 #pragma unroll
-      for (int t = 0; t < 8; ++t) v[t] = O[t] * inv;
-      store_out8(a, row * kHeadDim + d0, v);
-    } else {
-      const int64_t pidx = row * a.max_splits + split;
-      f32x4_t* po = reinterpret_cast<f32x4_t*>(a.ws_o + pidx * kHeadDim + d0);
-      po[0] = f32x4_t{O[0], O[1], O[2], O[3]};
-      po[1] = f32x4_t{O[4], O[5], O[6], O[7]};
-      if (qd == 0 && wave == 0) {
-        a.ws_ml[pidx * 2] = M;
-        a.ws_ml[pidx * 2 + 1] = L;
+            for (int t = 0; t < 8; ++t) {
+              const unsigned w = vr[s][t >> 2][t & 3] & vmask[t & 3];
+              const f16x4_t vfrag = e4m3x4_to_f16(w);
+              acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(vfrag, ph, acc[t], 0, 0, 0);
+              acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(vfrag, pl, acc[t], 0, 0, 0);
+            }
+          } else {
+            s16x4_t ph, pl;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const __bf16 h = static_cast<__bf16>(p[r]);
+              ph[r] = __builtin_bit_cast(short, h);
+              pl[r] = __builtin_bit_cast(short, static_cast<__bf16>(p[r] - static_cast<float>(h)));
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              const u32x4_t w = vr[s][t >> 1];
+              u32x2_t pair;
+              pair.x = ((t & 1) ? w.z : w.x) & vmask.x;
+              pair.y = ((t & 1) ? w.w : w.y) & vmask.y;
+              const s16x4_t vfrag = __builtin_bit_cast(s16x4_t, pair);
+              acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vfrag, ph, acc[t], 0, 0, 0);
+              acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vfrag, pl, acc[t], 0, 0, 0);
+            }
+          }
+          // refill this slot DEPTH pages ahead; its page id was fetched DEPTH
+          // pages ago; fetch the id 2*DEPTH pages ahead
+          issue(s, __builtin_amdgcn_readfirstlane(pid_ring[s]));
+          pid_ring[s] = fetch_pid();
+        }
       }
     }
+
+    // ---- merge the 4 waves' states for this piece through LDS -----------
+    const float l_tot = wave_sum_rows(l_run);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_acc[wave][t * 4 + r][lane] = acc[t][r];
+    if (qd == 0) {
+      s_m[wave][n] = m_run;
+      s_l[wave][n] = l_tot;
+    }
+    __syncthreads();
+    {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][n]);
+      float e[kWaves];
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = s_m[w][n];
+        e[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+        L += e[w] * s_l[w][n];
+      }
+      // wave `wave` merges accumulator row r = wave: dims 32 qd + 8 wave + t
+      float O[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        float o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) o += e[w] * s_acc[w][t * 4 + wave][lane];
+        O[t] = o;
+      }
+      if (n < a.G) {
+        const int d0 = 32 * qd + 8 * wave;
+        if (P.ps == P.sx && P.pe == P.sx + P.n) {
+          // the whole segment sits in this slice: write the output
+          const float vsc = a.v_scale ? a.v_scale[P.g] : 1.0f;
+          const float inv = L > 0.f ? vsc / L : 0.f;
+          float v[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) v[t] = O[t] * inv;
+          const int64_t row = static_cast<int64_t>(P.b) * a.Hq + P.g * a.G + n;
+          store_out8(a, row * kHeadDim + d0, v);
+        } else {
+          const int64_t pidx = (bw + static_cast<int64_t>(P.b) * a.Hkv + P.g) * a.G + n;
+          f32x4_t* po = reinterpret_cast<f32x4_t*>(a.ws_o + pidx * kHeadDim + d0);
+          po[0] = f32x4_t{O[0], O[1], O[2], O[3]};
+          po[1] = f32x4_t{O[4], O[5], O[6], O[7]};
+          if (qd == 0 && wave == 0) {
+            a.ws_ml[pidx * 2] = M;
+            a.ws_ml[pidx * 2 + 1] = L;
+          }
+        }
+      }
+    }
+    __syncthreads();  // LDS is reused by the next piece
+    if (!next_piece(P, s_pre, B, a.Hkv, X1)) break;
   }
 }
 
 // ---------------------------------------------------------------------------
-// 4. log-sum-exp merge of split partials, one wave per (request, q-head)
+// 5. merge of the pieces of split segments (fixed order: deterministic)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int32_t batch) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= static_cast<int64_t>(batch) * a.Hq) return;
-  const int b = static_cast<int>(row / a.Hq);
-  const int h = static_cast<int>(row % a.Hq);
-  const int g = h / a.G;
-  const int ctx = a.ctx_lens[b];
-  if (request_dead(a, b, ctx)) return;
-  const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
-  if (nsplit <= 1) return;
-  const float* ml = a.ws_ml + row * a.max_splits * 2;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ms = ml[2 * s];
-    const float e = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
-    L += e * ml[2 * s + 1];
-    const float* po = a.ws_o + (row * a.max_splits + s) * kHeadDim + 2 * lane;
-    o0 += e * po[0];
-    o1 += e * po[1];
+// one 128-thread workgroup per (request, kv-head, head in group); thread = dim
+__global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a, int64_t NWG) {
+  const int n = blockIdx.x % a.G;
+  const int seg = blockIdx.x / a.G;
+  const int b = seg / a.Hkv;
+  const int g = seg % a.Hkv;
+  const int pre_b = a.ws_pre[b];
+  const int np = a.ws_pre[b + 1] - pre_b;
+  if (np == 0) return;
+  const int64_t W = static_cast<int64_t>(a.Hkv) * a.ws_pre[a.batch];
+  const int64_t first = static_cast<int64_t>(a.Hkv) * pre_b + static_cast<int64_t>(g) * np;
+  const int64_t last = first + np - 1;
+  // workgroup holding item x: largest w with w*W/NWG <= x
+  const int64_t wf = ((first + 1) * NWG - 1) / W;
+  const int64_t wl = ((last + 1) * NWG - 1) / W;
+  if (wf == wl) return;  // one piece: written by the decode kernel
+  const int d = threadIdx.x;
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  for (int64_t w = wf; w <= wl; ++w) {
+    // with more workgroups than pages some own nothing and wrote no slot
+    if (w * W / NWG == (w + 1) * W / NWG) continue;
+    const int64_t pidx = (w + seg) * a.G + n;
+    const float m = a.ws_ml[pidx * 2];
+    if (m == -INFINITY) continue;
+    const float l = a.ws_ml[pidx * 2 + 1];
+    const float o = a.ws_o[pidx * kHeadDim + d];
+    if (m > M) {
+      const float r = (M == -INFINITY) ? 0.f : fast_exp2(M - m);
+      L *= r;
+      O *= r;
+      M = m;
+    }
+    const float e = fast_exp2(m - M);
+    L += e * l;
+    O += e * o;
   }
-  const float inv = L > 0.f ? (a.v_scale ? a.v_scale[g] : 1.0f) / L : 0.f;
-  const int64_t idx = row * kHeadDim + 2 * lane;
-  if (a.out_f32) {
-    static_cast<float*>(a.out)[idx] = o0 * inv;
-    static_cast<float*>(a.out)[idx + 1] = o1 * inv;
-  } else {
-    const unsigned lo = __builtin_bit_cast(unsigned short, static_cast<__bf16>(o0 * inv));
-    const unsigned hi = __builtin_bit_cast(unsigned short, static_cast<__bf16>(o1 * inv));
-    *reinterpret_cast<unsigned*>(static_cast<uint16_t*>(a.out) + idx) = lo | (hi << 16);
-  }
+  const float vsc = a.v_scale ? a.v_scale[g] : 1.0f;
+  const float v = L > 0.f ? O * (vsc / L) : 0.f;
+  const int64_t idx_out = (static_cast<int64_t>(b) * a.Hq + g * a.G + n) * kHeadDim + d;
+  if (a.out_f32)
+    static_cast<float*>(a.out)[idx_out] = v;
+  else
+    static_cast<uint16_t*>(a.out)[idx_out] = __builtin_bit_cast(unsigned short, static_cast<__bf16>(v));
 }
 
 // ---------------------------------------------------------------------------
@@ -635,21 +898,30 @@ int tile_bytes(const fp8kv_cache_desc* d) {
   return d->cache_dtype == FP8KV_E4M3 ? Tile<FP8KV_E4M3>::kBytes : Tile<FP8KV_BF16>::kBytes;
 }
 
-// Split size: aim for about kTargetUnits (request, kv-head, split) workgroups
-// so that every CU holds several, with splits a multiple of 64 tokens
-// (4 waves x 16-token pages).
-constexpr int kTargetUnits = 2048;
+// Workers (waves) of the decode kernel: all of them resident at once.
+int32_t device_workers() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus * FP8KV_WAVES_PER_CU;
+}
 
-int plan_split_tokens(const fp8kv_cache_desc* d, int batch, int max_ctx, int requested) {
-  if (requested > 0) return requested;
-  const int64_t pairs = static_cast<int64_t>(batch) * d->num_kv_heads;
-  int64_t splits = pairs > 0 ? (kTargetUnits + pairs - 1) / pairs : 1;
-  if (splits < 1) splits = 1;
-  int64_t t = (static_cast<int64_t>(max_ctx) + splits - 1) / splits;
-  t = (t + 63) / 64 * 64;
-  if (t < 256) t = 256;
-  if (t > kMaxSplitTokens) t = kMaxSplitTokens;
-  return static_cast<int>(t);
+struct WorkspaceLayout {
+  size_t o, ml, pre, total;
+};
+
+WorkspaceLayout workspace_layout(int64_t batch, int64_t Hq, int64_t Hkv, int64_t workers) {
+  const int64_t G = Hq / Hkv;
+  const int64_t slots = workers / kWaves + batch * Hkv;  // (workgroup + segment) slots
+  WorkspaceLayout L;
+  L.o = 0;
+  L.ml = L.o + static_cast<size_t>(slots * G * kHeadDim) * sizeof(float);
+  L.pre = L.ml + static_cast<size_t>(slots * G * 2) * sizeof(float);
+  L.pre = (L.pre + 255) / 256 * 256;
+  L.total = L.pre + static_cast<size_t>(batch + 1) * sizeof(int32_t);
+  return L;
 }
 
 }  // namespace
@@ -755,26 +1027,21 @@ fp8kv_status fp8kv_append(const fp8kv_cache_desc* desc, void* d_k_cache, void* d
   return launched();
 }
 
-int32_t fp8kv_decode_split_tokens(const fp8kv_cache_desc* desc, int32_t batch,
-                                  int32_t num_q_heads, int32_t max_ctx_len,
-                                  int32_t split_tokens) {
-  (void)num_q_heads;
-  if (check_desc(desc) != FP8KV_OK || batch < 0 || max_ctx_len < 0) return -1;
-  if (split_tokens != 0 &&
-      (split_tokens < kPage || split_tokens > kMaxSplitTokens || split_tokens % kPage != 0))
-    return -1;
-  return plan_split_tokens(desc, batch, max_ctx_len, split_tokens);
+int32_t fp8kv_decode_num_workers(int32_t requested) {
+  if (requested < 0) return -1;
+  int32_t w = requested > 0 ? requested : device_workers();
+  if (w <= 0) return -1;
+  return (w + kWaves - 1) / kWaves * kWaves;
 }
 
 size_t fp8kv_decode_workspace_size(const fp8kv_cache_desc* desc, int32_t batch,
-                                   int32_t num_q_heads, int32_t max_ctx_len,
-                                   int32_t split_tokens) {
-  const int32_t t = fp8kv_decode_split_tokens(desc, batch, num_q_heads, max_ctx_len, split_tokens);
-  if (t <= 0 || num_q_heads <= 0) return 0;
-  const int64_t max_splits = (static_cast<int64_t>(max_ctx_len) + t - 1) / t;
-  if (max_splits <= 1) return 0;
-  const int64_t rows = static_cast<int64_t>(batch) * num_q_heads * max_splits;
-  return static_cast<size_t>(rows) * (kHeadDim + 2) * sizeof(float);
+                                   int32_t num_q_heads, int32_t num_workers) {
+  if (check_desc(desc) != FP8KV_OK || batch < 0 || num_q_heads <= 0 ||
+      num_q_heads % desc->num_kv_heads != 0)
+    return 0;
+  const int32_t w = fp8kv_decode_num_workers(num_workers);
+  if (w <= 0) return 0;
+  return workspace_layout(batch, num_q_heads, desc->num_kv_heads, w).total;
 }
 
 fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc* desc, const void* d_k_cache,
@@ -782,33 +1049,27 @@ fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc* desc, const void* d_
                                     const float* d_v_scale, const uint16_t* d_q,
                                     int32_t num_q_heads, const int32_t* d_page_table,
                                     int32_t max_pages_per_seq, const int32_t* d_ctx_lens,
-                                    int32_t max_ctx_len, int32_t batch, float sm_scale,
-                                    const uint8_t* d_abort, void* d_out, int32_t out_dtype,
-                                    int32_t split_tokens, void* d_workspace,
-                                    size_t workspace_bytes, hipStream_t stream) {
+                                    int32_t batch, float sm_scale, const uint8_t* d_abort,
+                                    void* d_out, int32_t out_dtype, int32_t num_workers,
+                                    void* d_workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
   fp8kv_status st = check_desc(desc);
   if (st != FP8KV_OK) return st;
-  if (batch < 0 || max_ctx_len < 0 || max_pages_per_seq < 0 || num_q_heads <= 0)
+  if (batch < 0 || max_pages_per_seq < 0 || num_q_heads <= 0 || num_workers < 0)
     return FP8KV_INVALID_ARG;
   if (num_q_heads % desc->num_kv_heads != 0) return FP8KV_UNSUPPORTED;
   const int G = num_q_heads / desc->num_kv_heads;
-  if (G > kMaxGroup) return FP8KV_UNSUPPORTED;
+  if (G > kMaxGroup || batch > kMaxBatch) return FP8KV_UNSUPPORTED;
   if (out_dtype != FP8KV_OUT_BF16 && out_dtype != FP8KV_OUT_F32) return FP8KV_INVALID_ARG;
   if (batch == 0) return FP8KV_OK;
   if (!d_k_cache || !d_v_cache || !d_q || !d_ctx_lens || !d_out ||
       (max_pages_per_seq > 0 && !d_page_table))
     return FP8KV_INVALID_ARG;
   if (desc->cache_dtype == FP8KV_E4M3 && (!d_k_scale || !d_v_scale)) return FP8KV_INVALID_ARG;
-  const int32_t T = fp8kv_decode_split_tokens(desc, batch, num_q_heads, max_ctx_len, split_tokens);
-  if (T <= 0) return FP8KV_INVALID_ARG;
-  const size_t need =
-      fp8kv_decode_workspace_size(desc, batch, num_q_heads, max_ctx_len, split_tokens);
-  if (need > 0 && (d_workspace == nullptr || workspace_bytes < need))
-    return FP8KV_WORKSPACE_TOO_SMALL;
-  int64_t max_splits = (static_cast<int64_t>(max_ctx_len) + T - 1) / T;
-  if (max_splits < 1) max_splits = 1;
-  const int64_t blocks = static_cast<int64_t>(batch) * desc->num_kv_heads * max_splits;
-  if (blocks > 0x7FFFFFFF) return FP8KV_INVALID_ARG;
+  const int32_t workers = fp8kv_decode_num_workers(num_workers);
+  if (workers <= 0) return FP8KV_HIP_ERROR;
+  const WorkspaceLayout L = workspace_layout(batch, num_q_heads, desc->num_kv_heads, workers);
+  if (!d_workspace || workspace_bytes < L.total) return FP8KV_WORKSPACE_TOO_SMALL;
 
   DecodeArgs a;
   a.k_cache = static_cast<const uint8_t*>(d_k_cache);
@@ -821,32 +1082,74 @@ fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc* desc, const void* d_
   a.ctx_lens = d_ctx_lens;
   a.abort = d_abort;
   a.out = d_out;
-  a.ws_o = static_cast<float*>(d_workspace);
-  a.ws_ml = need > 0 ? static_cast<float*>(d_workspace) +
-                           static_cast<int64_t>(batch) * num_q_heads * max_splits * kHeadDim
-                     : nullptr;
+  char* ws = static_cast<char*>(d_workspace);
+  a.ws_o = reinterpret_cast<float*>(ws + L.o);
+  a.ws_ml = reinterpret_cast<float*>(ws + L.ml);
+  a.ws_pre = reinterpret_cast<int32_t*>(ws + L.pre);
   a.page_stride = static_cast<int64_t>(desc->num_kv_heads) * tile_bytes(desc);
+  a.batch = batch;
   a.max_pages = max_pages_per_seq;
-  a.max_ctx_len = max_ctx_len;
   a.num_pages = desc->num_pages;
   a.Hq = num_q_heads;
   a.Hkv = desc->num_kv_heads;
   a.G = G;
-  a.split_tokens = T;
-  a.max_splits = static_cast<int32_t>(max_splits);
   a.out_f32 = out_dtype == FP8KV_OUT_F32 ? 1 : 0;
   a.sm_scale = sm_scale;
+  const int blocks = workers / kWaves;
   if (desc->cache_dtype == FP8KV_E4M3) {
-    hipLaunchKernelGGL((decode_split_kernel<FP8KV_E4M3, 3>), dim3(blocks), dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((decode_kernel<FP8KV_E4M3, FP8KV_DEPTH_E4M3>), dim3(blocks),
+                       dim3(kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((decode_split_kernel<FP8KV_BF16, 2>), dim3(blocks), dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((decode_kernel<FP8KV_BF16, FP8KV_DEPTH_BF16>), dim3(blocks),
+                       dim3(kThreads), 0, stream, a);
   }
   st = launched();
-  if (st != FP8KV_OK || max_splits <= 1) return st;
-  const int64_t rows = static_cast<int64_t>(batch) * num_q_heads;
-  hipLaunchKernelGGL(combine_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, a, batch);
+  if (st != FP8KV_OK) return st;
+  hipLaunchKernelGGL(merge_kernel, dim3(batch * desc->num_kv_heads * G), dim3(128), 0, stream, a,
+                     static_cast<int64_t>(blocks));
+  return launched();
+}
+
+fp8kv_status fp8kv_verify_append(const fp8kv_cache_desc* desc, void* d_k_cache, void* d_v_cache,
+                                 const float* d_k_scale, const float* d_v_scale,
+                                 const uint16_t* d_k_new, const uint16_t* d_v_new,
+                                 const int32_t* d_new_pos, const int32_t* d_page_table,
+                                 const uint32_t* d_expected_tags, int32_t max_pages_per_seq,
+                                 const int32_t* d_ctx_lens, int32_t batch,
+                                 const uint32_t* d_pool_tags, uint8_t* d_abort,
+                                 hipStream_t stream) {
+  fp8kv_status st = check_desc(desc);
+  if (st != FP8KV_OK) return st;
+  if (batch < 0 || max_pages_per_seq < 0) return FP8KV_INVALID_ARG;
+  if (batch == 0) return FP8KV_OK;
+  if (!d_k_cache || !d_v_cache || !d_k_new || !d_v_new || !d_new_pos || !d_ctx_lens ||
+      !d_abort || !d_pool_tags || (max_pages_per_seq > 0 && (!d_page_table || !d_expected_tags)))
+    return FP8KV_INVALID_ARG;
+  if (desc->cache_dtype == FP8KV_E4M3 && (!d_k_scale || !d_v_scale)) return FP8KV_INVALID_ARG;
+  VerifyAppendArgs a;
+  a.v = VerifyArgs{d_page_table, d_expected_tags, d_ctx_lens, d_pool_tags, d_abort,
+                   max_pages_per_seq, desc->num_pages, kPage};
+  a.w.k_cache = static_cast<uint8_t*>(d_k_cache);
+  a.w.v_cache = static_cast<uint8_t*>(d_v_cache);
+  a.w.k_scale = d_k_scale;
+  a.w.v_scale = d_v_scale;
+  a.w.k_new = d_k_new;
+  a.w.v_new = d_v_new;
+  a.w.token_seq = nullptr;
+  a.w.token_pos = nullptr;
+  a.w.page_table = d_page_table;
+  a.w.abort = nullptr;
+  a.w.page_stride = static_cast<int64_t>(desc->num_kv_heads) * tile_bytes(desc);
+  a.w.total_items = static_cast<int64_t>(batch) * desc->num_kv_heads * 8;
+  a.w.num_seqs = batch;
+  a.w.max_pages = max_pages_per_seq;
+  a.w.num_pages = desc->num_pages;
+  a.w.Hkv = desc->num_kv_heads;
+  a.new_pos = d_new_pos;
+  if (desc->cache_dtype == FP8KV_E4M3)
+    hipLaunchKernelGGL(verify_append_kernel<FP8KV_E4M3>, dim3(batch), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(verify_append_kernel<FP8KV_BF16>, dim3(batch), dim3(256), 0, stream, a);
   return launched();
 }
 

@@ -178,43 +178,61 @@ fp8kv_status fp8kv_append(const fp8kv_cache_desc *desc, void *d_k_cache, void *d
                           hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Tag check fused with the step's append (same two operations as            */
+/* fp8kv_verify_tags followed by fp8kv_append gated on d_abort, in one        */
+/* launch).  One workgroup per request b: it checks the request's pages as    */
+/* fp8kv_verify_tags does, writes d_abort[b], and only if the check passed    */
+/* quantizes the request's new token (d_k_new/d_v_new row b, BF16             */
+/* [batch][Hkv][128]) into position d_new_pos[b].  The check is still its    */
+/* own batched pass ahead of attention, as the integrity section describes.  */
+/* ------------------------------------------------------------------------ */
+fp8kv_status fp8kv_verify_append(const fp8kv_cache_desc *desc, void *d_k_cache, void *d_v_cache,
+                                 const float *d_k_scale, const float *d_v_scale,
+                                 const uint16_t *d_k_new, const uint16_t *d_v_new,
+                                 const int32_t *d_new_pos, const int32_t *d_page_table,
+                                 const uint32_t *d_expected_tags, int32_t max_pages_per_seq,
+                                 const int32_t *d_ctx_lens, int32_t batch,
+                                 const uint32_t *d_pool_tags, uint8_t *d_abort,
+                                 hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Paged decode attention (one query token per request) over the cache,      */
 /* converting e4m3 on read.  For request b and q-head h (kv-head g = h/G):  */
 /*   s_j = sm_scale * k_scale[g] * sum_d q[b][h][d] * DEC(K[j][g][d]),        */
 /*   o   = v_scale[g] * sum_j e^{s_j - max s} DEC(V[j][g]) / sum_j e^{s_j-max s}*/
 /* over the d_ctx_lens[b] tokens j of the request (token j at page           */
-/* d_page_table[b][j/16], slot j%16).  Long contexts are split into chunks of */
-/* split_tokens tokens whose partial (max, sum, weighted V) are merged with a */
-/* log-sum-exp reduction in a fixed order.                                   */
+/* d_page_table[b][j/16], slot j%16).  The (request, kv-head, page) work is   */
+/* shared equally by num_workers waves; a (request, kv-head) whose pages      */
+/* fall to several waves is finished by a log-sum-exp merge of their partial  */
+/* (max, sum, weighted V) in a fixed order (flash-decoding split-K), so the   */
+/* result is deterministic for a given num_workers.                           */
 /*   d_q: BF16 bits [batch][Hq][128];  d_out: [batch][Hq][128] of BF16 bits   */
 /*   (out_dtype FP8KV_OUT_BF16, round-to-nearest-even) or fp32 (FP8KV_OUT_F32).*/
-/*   max_ctx_len: host upper bound of d_ctx_lens (sizes the launch); a        */
-/*   request whose length exceeds it or the table width produces zeros.       */
 /*   d_abort (nullable): requests flagged 1 produce +0 rows and read nothing  */
-/*   from the cache; NULL is the no-op tracker (no check at all).  Without    */
-/*   the check, page ids outside [0, num_pages) are still never dereferenced; */
-/*   their tokens are left out (results for such a request are unspecified).  */
-/*   split_tokens: 0 picks a value from the shapes; otherwise a multiple of   */
-/*   16 in [16, 16384].  d_workspace: at least fp8kv_decode_workspace_size()  */
-/*   bytes for the same arguments (may be NULL when that size is 0).          */
+/*   from the cache; NULL is the no-op tracker (no check at all).  Requests   */
+/*   with d_ctx_lens[b] <= 0 or more pages than max_pages_per_seq also give   */
+/*   +0 rows.  Without the check, page ids outside [0, num_pages) are still   */
+/*   never dereferenced; their tokens are left out (results for such a        */
+/*   request are unspecified).                                                */
+/*   batch <= 4096.  num_workers: 0 picks the device's resident wave count    */
+/*   (compute units x 16); otherwise rounded up to a multiple of 4.           */
+/*   d_workspace: at least fp8kv_decode_workspace_size() bytes for the same   */
+/*   batch, num_q_heads and num_workers on the current device.                */
 /* ------------------------------------------------------------------------ */
-int32_t fp8kv_decode_split_tokens(const fp8kv_cache_desc *desc, int32_t batch,
-                                  int32_t num_q_heads, int32_t max_ctx_len,
-                                  int32_t split_tokens);
+int32_t fp8kv_decode_num_workers(int32_t requested);
 
 size_t fp8kv_decode_workspace_size(const fp8kv_cache_desc *desc, int32_t batch,
-                                   int32_t num_q_heads, int32_t max_ctx_len,
-                                   int32_t split_tokens);
+                                   int32_t num_q_heads, int32_t num_workers);
 
 fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc *desc, const void *d_k_cache,
                                     const void *d_v_cache, const float *d_k_scale,
                                     const float *d_v_scale, const uint16_t *d_q,
                                     int32_t num_q_heads, const int32_t *d_page_table,
                                     int32_t max_pages_per_seq, const int32_t *d_ctx_lens,
-                                    int32_t max_ctx_len, int32_t batch, float sm_scale,
-                                    const uint8_t *d_abort, void *d_out, int32_t out_dtype,
-                                    int32_t split_tokens, void *d_workspace,
-                                    size_t workspace_bytes, hipStream_t stream);
+                                    int32_t batch, float sm_scale, const uint8_t *d_abort,
+                                    void *d_out, int32_t out_dtype, int32_t num_workers,
+                                    void *d_workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Self-test of the on-read conversion: d_out[i] = the value the attention   */

@@ -137,16 +137,18 @@ def test_tiny_step_parity(lib, dev, cache_dtype):
 
 
 # ---------------------------------------------------------------------------
-# shapes, lengths, splits
+# shapes, lengths, work partitions
 # ---------------------------------------------------------------------------
 EDGE_LENS = [0, 1, 14, 15, 16, 17, 30, 31, 32, 47, 63, 64, 65, 127, 255, 256, 300, 1023, 2100]
 
 
 @pytest.mark.parametrize("G,Hkv", [(1, 4), (2, 2), (4, 2), (8, 1), (16, 1), (8, 3)])
-@pytest.mark.parametrize("split", [0, 16, 64, 272])
-def test_lengths_groups_splits(lib, dev, G, Hkv, split):
+@pytest.mark.parametrize("workers", [0, 4, 12, 64, 1024])
+def test_lengths_groups_workers(lib, dev, G, Hkv, workers):
+    """Few workers: slices cross many (request, kv-head) boundaries.  Many
+    workers: most segments are split and merged."""
     w = workloads.custom("edge", EDGE_LENS, Hq=G * Hkv, Hkv=Hkv, seed=G * 10 + Hkv, pool_slack=5)
-    st = dev.build(w, split_tokens=split)
+    st = dev.build(w, num_workers=workers)
     out16 = st.step(check_tags=True)
     out32 = st.decode(out_dtype=lib.OUT_F32)
     Ko, Vo = oracle_state(w, st.k_scale_host, st.v_scale_host)
@@ -156,9 +158,22 @@ def test_lengths_groups_splits(lib, dev, G, Hkv, split):
     assert err < 1e-4
 
 
+@pytest.mark.parametrize("cache_dtype", [0, 1])
+def test_fused_equals_separate_check_and_append(lib, dev, cache_dtype):
+    w = workloads.make(5, batch=40)
+    a = dev.build(w, cache_dtype=cache_dtype, num_workers=64)
+    b = dev.build(w, cache_dtype=cache_dtype, num_workers=64)
+    oa = _host(a.step(check_tags=True, fused=True).view(torch.int16)).copy()
+    ob = _host(b.step(check_tags=True, fused=False).view(torch.int16)).copy()
+    assert (_host(a.abort) == w.expected_abort).all()
+    assert (_host(a.abort) == _host(b.abort)).all()
+    assert (_host(a.K) == _host(b.K)).all() and (_host(a.V) == _host(b.V)).all()
+    assert (oa == ob).all()
+
+
 def test_empty_context_and_abort_rows_are_zero(lib, dev):
     w = workloads.custom("edge", [40, 100, 7, 300], Hq=8, Hkv=2, seed=3)
-    st = dev.build(w, split_tokens=64)
+    st = dev.build(w, num_workers=8)
     st.step(check_tags=True)
     ref = _host(st.decode(out_dtype=lib.OUT_F32)).copy()
     cl = st.ctx_lens.clone()
@@ -166,21 +181,21 @@ def test_empty_context_and_abort_rows_are_zero(lib, dev):
     st.abort.copy_(torch.tensor([0, 0, 1, 0], dtype=torch.uint8))
     out = _host(st.decode(out_dtype=lib.OUT_F32))
     assert (out[1] == 0).all() and (out[2] == 0).all() and not np.signbit(out[1:3]).any()
-    assert (out[0] == ref[0]).all() and (out[3] == ref[3]).all()
+    assert np.abs(out[0] - ref[0]).max() < 1e-5 and np.abs(out[3] - ref[3]).max() < 1e-5
     st.ctx_lens.copy_(cl)
 
 
 # ---------------------------------------------------------------------------
 # invariants
 # ---------------------------------------------------------------------------
-def test_bitwise_invariants(lib, dev):
+def test_invariants(lib, dev):
     w = workloads.custom("inv", [100, 33, 700, 1500, 16, 2047], Hq=16, Hkv=2, seed=5, pool_slack=7)
-    st = dev.build(w, split_tokens=256)
+    st = dev.build(w, num_workers=16)
     out = _host(st.step(check_tags=True).view(torch.int16)).copy()
     # run-to-run determinism
     for _ in range(3):
         assert (_host(st.decode().view(torch.int16)) == out).all()
-    # permute physical pages (move the tiles, rewrite the page table): identical
+    # permute physical pages (move the tiles, rewrite the page table): identical bits
     N = w.num_pages
     perm = torch.from_numpy(np.random.default_rng(1).permutation(N)).cuda()
     tile = st.K.numel() // N
@@ -191,36 +206,35 @@ def test_bitwise_invariants(lib, dev):
     pt2 = torch.where(st.page_table >= 0, perm[st.page_table.clamp(min=0).long()].int(),
                       st.page_table)
     out2 = lib.decode_attention(st.desc, K2.view(-1), V2.view(-1), st.k_scale, st.v_scale, st.q,
-                                pt2.contiguous(), st.ctx_lens, st.max_ctx_len,
-                                split_tokens=st.split_tokens)
+                                pt2.contiguous(), st.ctx_lens, num_workers=16)
     assert (_host(out2.view(torch.int16)) == out).all()
-    # reorder the batch: the output rows move with it, bit for bit
+    # reorder the batch: rows move with it (the work partition changes, so
+    # agreement is to rounding, not bits)
+    f_ref = _host(st.decode(out_dtype=lib.OUT_F32)).copy()
     order = torch.tensor([3, 0, 5, 1, 4, 2], device="cuda")
     out3 = lib.decode_attention(st.desc, st.K, st.V, st.k_scale, st.v_scale,
                                 st.q[order].contiguous(), st.page_table[order].contiguous(),
-                                st.ctx_lens[order].contiguous(), st.max_ctx_len,
-                                split_tokens=st.split_tokens)
-    assert (_host(out3.view(torch.int16)) == out[order.cpu().numpy()]).all()
-    # a different split size agrees within tolerance (different merge order)
-    f1 = _host(st.decode(out_dtype=lib.OUT_F32, split_tokens=256)).copy()
-    f2 = _host(st.decode(out_dtype=lib.OUT_F32, split_tokens=16384))
-    assert np.abs(f1 - f2).max() < 1e-5
+                                st.ctx_lens[order].contiguous(), out_dtype=lib.OUT_F32,
+                                num_workers=16)
+    assert np.abs(_host(out3) - f_ref[order.cpu().numpy()]).max() < 1e-5
+    # other partitions agree to rounding
+    for nw in (4, 64, 4096):
+        f2 = _host(st.decode(out_dtype=lib.OUT_F32, num_workers=nw))
+        assert np.abs(f2 - f_ref).max() < 1e-5, nw
 
 
 def test_abort_isolation(lib, dev):
-    """Stale tags: aborted requests get +0 rows and write nothing; the others
-    are bit-identical to a run in which the stale requests never existed."""
+    """Stale tags: aborted requests get +0 rows and write nothing; nothing the
+    other requests produce depends on the aborted requests' pages."""
     w = workloads.make(5, batch=24)
-    st = dev.build(w)
-    K0, V0 = st.K.clone(), st.V.clone()
+    st = dev.build(w, num_workers=64)
+    K0 = _host(st.K).copy()
     out = _host(st.step(check_tags=True).view(torch.int16)).copy()
     ab = _host(st.abort)
-    exp_ab = w.expected_abort
-    assert (ab == exp_ab).all() and 0 < ab.sum() < w.B
+    assert (ab == w.expected_abort).all() and 0 < ab.sum() < w.B
     assert (out[ab == 1] == 0).all()
     # the aborted requests' new-token slots are untouched
-    Kh, K0h = _host(st.K), _host(K0)
-    changed = np.flatnonzero(Kh != K0h)
+    Kh = _host(st.K)
     d = st.desc
     for b in np.flatnonzero(ab):
         L = int(w.ctx_before[b])
@@ -228,13 +242,24 @@ def test_abort_isolation(lib, dev):
         for h in range(w.Hkv):
             for dim in (0, 77, 127):
                 off = lib.cache_offset(d, 0, page, h, L % 16, dim)
-                assert Kh[off] == K0h[off]
-    assert changed.size > 0
-    # survivors equal a batch made of survivors only
+                assert Kh[off] == K0[off]
+    # scramble every page of the aborted requests: the other outputs keep their bits
+    tile = st.K.numel() // w.num_pages
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    for b in np.flatnonzero(ab):
+        pages = torch.from_numpy(w.page_table[b, : w.n_pages[b]].astype(np.int64)).cuda()
+        for X in (st.K, st.V):
+            Xv = X.view(w.num_pages, tile)
+            Xv[pages] = torch.randint(0, 256, (pages.numel(), tile), dtype=torch.uint8,
+                                      device="cuda", generator=gen)
+    out2 = _host(st.decode().view(torch.int16))
+    assert (out2 == out).all()
+    # survivors agree (to rounding) with a batch made of survivors only
     keep = np.flatnonzero(ab == 0)
     kt = torch.from_numpy(keep).cuda()
+    f_all = _host(st.decode(out_dtype=lib.OUT_F32)).copy()
     out_k = lib.decode_attention(st.desc, st.K, st.V, st.k_scale, st.v_scale,
                                  st.q[kt].contiguous(), st.page_table[kt].contiguous(),
-                                 st.ctx_lens[kt].contiguous(), st.max_ctx_len,
-                                 split_tokens=st.split_tokens)
-    assert (_host(out_k.view(torch.int16)) == out[keep]).all()
+                                 st.ctx_lens[kt].contiguous(), out_dtype=lib.OUT_F32,
+                                 num_workers=64)
+    assert np.abs(_host(out_k) - f_all[keep]).max() < 1e-5

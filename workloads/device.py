@@ -42,8 +42,7 @@ class DeviceStep:
     token_seq: torch.Tensor
     token_pos: torch.Tensor     # L_b
     abort: torch.Tensor
-    max_ctx_len: int
-    split_tokens: int
+    num_workers: int
     workspace: Optional[torch.Tensor]
     out: torch.Tensor
 
@@ -60,22 +59,32 @@ class DeviceStep:
                      self.v_new, self.token_seq, self.token_pos, self.page_table,
                      abort=self.abort if use_abort else None, stream=stream)
 
+    def verify_append(self, stream=None):
+        fp8kv.verify_append(self.desc, self.K, self.V, self.k_scale, self.v_scale, self.k_new,
+                            self.v_new, self.token_pos, self.page_table, self.expected_tags,
+                            self.ctx_lens, self.pool_tags, abort=self.abort, stream=stream)
+
     def decode(self, use_abort=True, out_dtype=fp8kv.OUT_BF16, out=None, stream=None,
-               split_tokens=None):
+               num_workers=None):
         if out is None:
             out = self.out if out_dtype == fp8kv.OUT_BF16 else torch.empty(
                 self.out.shape, dtype=torch.float32, device=self.out.device)
+        nw = self.num_workers if num_workers is None else num_workers
         return fp8kv.decode_attention(
             self.desc, self.K, self.V, self.k_scale, self.v_scale, self.q, self.page_table,
-            self.ctx_lens, self.max_ctx_len, abort=self.abort if use_abort else None, out=out,
-            out_dtype=out_dtype, split_tokens=self.split_tokens if split_tokens is None else split_tokens,
-            workspace=self.workspace, stream=stream)
+            self.ctx_lens, abort=self.abort if use_abort else None, out=out,
+            out_dtype=out_dtype, num_workers=nw,
+            workspace=self.workspace if nw == self.num_workers else None, stream=stream)
 
-    def step(self, check_tags=True, out_dtype=fp8kv.OUT_BF16, stream=None):
-        """One decode step: tag check (optional), append, attention."""
-        if check_tags:
-            self.verify(stream)
-        self.append(use_abort=check_tags, stream=stream)
+    def step(self, check_tags=True, out_dtype=fp8kv.OUT_BF16, stream=None, fused=True):
+        """One decode step: tag check + append (one launch when fused), then
+        attention.  check_tags=False is the no-op tracker path."""
+        if check_tags and fused:
+            self.verify_append(stream)
+        else:
+            if check_tags:
+                self.verify(stream)
+            self.append(use_abort=check_tags, stream=stream)
         return self.decode(use_abort=check_tags, out_dtype=out_dtype, stream=stream)
 
 
@@ -92,7 +101,7 @@ def kv_amax(w: Workload, which: str, device) -> np.ndarray:
     return am.cpu().numpy()
 
 
-def build(w: Workload, cache_dtype: int = fp8kv.E4M3, device="cuda", split_tokens: int = 0,
+def build(w: Workload, cache_dtype: int = fp8kv.E4M3, device="cuda", num_workers: int = 0,
           fill: bool = True, fill_chunk_tokens: int = 1 << 20) -> DeviceStep:
     d = fp8kv.desc(w.num_pages, w.Hkv, cache_dtype)
     K, V = fp8kv.new_cache(d, device)
@@ -128,10 +137,9 @@ def build(w: Workload, cache_dtype: int = fp8kv.E4M3, device="cuda", split_token
     q = w.q_bits("torch", device).contiguous()
     k_new = w.new_kv_bits("k", "torch", device).contiguous()
     v_new = w.new_kv_bits("v", "torch", device).contiguous()
-    max_ctx = int(w.ctx_lens.max()) if w.B > 0 else 0
-    T = fp8kv.decode_split_tokens(d, w.B, w.Hq, max_ctx, split_tokens)
-    need = fp8kv.decode_workspace_size(d, w.B, w.Hq, max_ctx, split_tokens)
-    ws = torch.empty(need, dtype=torch.uint8, device=device) if need > 0 else None
+    nw = fp8kv.decode_num_workers(num_workers)
+    need = fp8kv.decode_workspace_size(d, w.B, w.Hq, nw)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
     torch.cuda.synchronize()
     return DeviceStep(
         w=w, desc=d, K=K, V=V, k_scale=ks, v_scale=vs, k_scale_host=ksh, v_scale_host=vsh,
@@ -142,5 +150,5 @@ def build(w: Workload, cache_dtype: int = fp8kv.E4M3, device="cuda", split_token
         token_seq=torch.arange(w.B, dtype=torch.int32, device=device),
         token_pos=torch.from_numpy(w.ctx_before.astype(np.int32)).to(device),
         abort=torch.zeros(w.B, dtype=torch.uint8, device=device),
-        max_ctx_len=max_ctx, split_tokens=T, workspace=ws,
+        num_workers=nw, workspace=ws,
         out=torch.empty((w.B, w.Hq, 128), dtype=torch.bfloat16, device=device))
