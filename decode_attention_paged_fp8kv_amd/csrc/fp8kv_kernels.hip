@@ -208,27 +208,46 @@ struct AppendArgs {
   int32_t num_seqs, max_pages, num_pages, Hkv;
 };
 
-// Quantize 16 consecutive dims [16c, 16c+16) of token `tok`, kv-head h, into
-// slot `slot` of physical page `pid` (K and V).
+// Quantized (or copied) bytes of 16 consecutive dims of one token and kv-head.
+struct Chunk16 {
+  u32x4_t k0, k1, v0, v1;  // e4m3: k0/v0 hold 16 codes; bf16: the 2x16 raw bytes
+};
+
+// Load and encode dims [16c, 16c+16) of token `tok`, kv-head h.
 template <int CACHE>
-__device__ __forceinline__ void append_one(const AppendArgs& a, int64_t tok, int h, int c,
-                                           int32_t pid, int slot) {
+__device__ __forceinline__ Chunk16 append_prepare(const AppendArgs& a, int64_t tok, int h,
+                                                  int c) {
   const int64_t src = (tok * a.Hkv + h) * kHeadDim + 16 * c;
   const u32x4_t* kin = reinterpret_cast<const u32x4_t*>(a.k_new + src);
   const u32x4_t* vin = reinterpret_cast<const u32x4_t*>(a.v_new + src);
-  const u32x4_t k0 = kin[0], k1 = kin[1], v0 = vin[0], v1 = vin[1];
-  uint16_t kb[16], vb[16];
+  Chunk16 r;
+  r.k0 = kin[0];
+  r.k1 = kin[1];
+  r.v0 = vin[0];
+  r.v1 = vin[1];
+  if constexpr (CACHE == FP8KV_E4M3) {
+    const float ks = a.k_scale[h], vs = a.v_scale[h];
+    u32x4_t kq = {0u, 0u, 0u, 0u}, vq = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    kb[2 * i] = k0[i] & 0xFFFF;
-    kb[2 * i + 1] = k0[i] >> 16;
-    kb[8 + 2 * i] = k1[i] & 0xFFFF;
-    kb[8 + 2 * i + 1] = k1[i] >> 16;
-    vb[2 * i] = v0[i] & 0xFFFF;
-    vb[2 * i + 1] = v0[i] >> 16;
-    vb[8 + 2 * i] = v1[i] & 0xFFFF;
-    vb[8 + 2 * i + 1] = v1[i] >> 16;
+    for (int i = 0; i < 16; ++i) {
+      const u32x4_t& ksrc = i < 8 ? r.k0 : r.k1;
+      const u32x4_t& vsrc = i < 8 ? r.v0 : r.v1;
+      const int w = (i & 7) >> 1;
+      const uint16_t kb = (i & 1) ? (ksrc[w] >> 16) : (ksrc[w] & 0xFFFF);
+      const uint16_t vb = (i & 1) ? (vsrc[w] >> 16) : (vsrc[w] & 0xFFFF);
+      kq[i >> 2] |= e4m3_encode(bf16_to_f32(kb) / ks) << (8 * (i & 3));
+      vq[i >> 2] |= e4m3_encode(bf16_to_f32(vb) / vs) << (8 * (i & 3));
+    }
+    r.k0 = kq;
+    r.v0 = vq;
   }
+  return r;
+}
+
+// Store a prepared chunk into slot `slot` of physical page `pid`.
+template <int CACHE>
+__device__ __forceinline__ void append_store(const AppendArgs& a, const Chunk16& r, int h, int c,
+                                             int32_t pid, int slot) {
   const int64_t tile = static_cast<int64_t>(pid) * a.page_stride +
                        static_cast<int64_t>(h) * Tile<CACHE>::kBytes;
   uint8_t* kt = a.k_cache + tile;
@@ -236,29 +255,28 @@ __device__ __forceinline__ void append_one(const AppendArgs& a, int64_t tok, int
   // K: dims d = 16c+i have f = d%32 = 16(c%2)+i and lane 16(c/2)+slot
   const int klane = 16 * (c >> 1) + slot;
   if constexpr (CACHE == FP8KV_E4M3) {
-    const float ks = a.k_scale[h], vs = a.v_scale[h];
-    u32x4_t out = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) out[i >> 2] |= e4m3_encode(bf16_to_f32(kb[i]) / ks) << (8 * (i & 3));
-    *reinterpret_cast<u32x4_t*>(kt + (c & 1) * 1024 + 16 * klane) = out;
+    *reinterpret_cast<u32x4_t*>(kt + (c & 1) * 1024 + 16 * klane) = r.k0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int d = 16 * c + i;
       const int f = 4 * (d & 7) + (slot & 3);
       const int vlane = 16 * (slot >> 2) + (d >> 3);
       vt[(f >> 4) * 1024 + 16 * vlane + (f & 15)] =
-          static_cast<uint8_t>(e4m3_encode(bf16_to_f32(vb[i]) / vs));
+          static_cast<uint8_t>(r.v0[i >> 2] >> (8 * (i & 3)));
     }
   } else {
     // f = 16(c%2)+i; chunk f/8 = 2(c%2) + i/8: two contiguous 16-byte stores
-    *reinterpret_cast<u32x4_t*>(kt + (2 * (c & 1)) * 1024 + 16 * klane) = k0;
-    *reinterpret_cast<u32x4_t*>(kt + (2 * (c & 1) + 1) * 1024 + 16 * klane) = k1;
+    *reinterpret_cast<u32x4_t*>(kt + (2 * (c & 1)) * 1024 + 16 * klane) = r.k0;
+    *reinterpret_cast<u32x4_t*>(kt + (2 * (c & 1) + 1) * 1024 + 16 * klane) = r.k1;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int d = 16 * c + i;
       const int f = 4 * (d & 7) + (slot & 3);
       const int vlane = 16 * (slot >> 2) + (d >> 3);
-      *reinterpret_cast<uint16_t*>(vt + (f >> 3) * 1024 + 16 * vlane + 2 * (f & 7)) = vb[i];
+      const u32x4_t& vsrc = i < 8 ? r.v0 : r.v1;
+      const int w = (i & 7) >> 1;
+      *reinterpret_cast<uint16_t*>(vt + (f >> 3) * 1024 + 16 * vlane + 2 * (f & 7)) =
+          static_cast<uint16_t>((i & 1) ? (vsrc[w] >> 16) : (vsrc[w] & 0xFFFF));
     }
   }
 }
@@ -279,7 +297,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   if (pos < 0 || pos / kPage >= a.max_pages) return;
   const int32_t pid = a.page_table[static_cast<int64_t>(seq) * a.max_pages + pos / kPage];
   if (static_cast<unsigned>(pid) >= static_cast<unsigned>(a.num_pages)) return;
-  append_one<CACHE>(a, tok, h, c, pid, pos % kPage);
+  append_store<CACHE>(a, append_prepare<CACHE>(a, tok, h, c), h, c, pid, pos % kPage);
 }
 
 // ---------------------------------------------------------------------------
@@ -293,16 +311,27 @@ struct VerifyAppendArgs {
 
 // The check still runs as its own batched pass ahead of attention; fusing it
 // with the append only removes a launch: a request's token is written after
-// (and only if) all of that request's pages passed.
+// (and only if) all of that request's pages passed.  The token is loaded and
+// encoded while the check's loads are in flight; only the stores wait.
+constexpr int kVerifyThreads = 512;
+constexpr int kVerifyUnroll = 4;
+
 template <int CACHE>
-__global__ __launch_bounds__(256) void verify_append_kernel(VerifyAppendArgs a) {
+__global__ __launch_bounds__(kVerifyThreads) void verify_append_kernel(VerifyAppendArgs a) {
   const int b = blockIdx.x;
+  const int tid = threadIdx.x;
   const int ctx = a.v.ctx_lens[b];
   const int pos = a.new_pos[b];
-  // the new token's page id and inputs do not depend on the check: load early
   const bool pos_ok = pos >= 0 && pos / kPage < a.w.max_pages;
-  const int32_t pid =
-      pos_ok ? a.w.page_table[static_cast<int64_t>(b) * a.w.max_pages + pos / kPage] : -1;
+  // this thread's share of the append (Hkv * 8 chunks of 16 dims)
+  const bool mine = tid < a.w.Hkv * 8;
+  const int h = tid >> 3, c = tid & 7;
+  int32_t pid = -1;
+  Chunk16 prep;
+  if (mine && pos_ok) {
+    pid = a.w.page_table[static_cast<int64_t>(b) * a.w.max_pages + pos / kPage];
+    prep = append_prepare<CACHE>(a.w, static_cast<int64_t>(b), h, c);
+  }
   int bad = 0;
   if (ctx < 0) {
     bad = 1;
@@ -313,18 +342,18 @@ __global__ __launch_bounds__(256) void verify_append_kernel(VerifyAppendArgs a) 
     } else {
       const int32_t* pt = a.v.page_table + static_cast<int64_t>(b) * a.v.max_pages;
       const uint32_t* et = a.v.expected + static_cast<int64_t>(b) * a.v.max_pages;
-      for (int i0 = threadIdx.x; i0 < n; i0 += 4 * 256) {
-        int32_t id[4];
-        uint32_t ex[4];
+      for (int i0 = tid; i0 < n; i0 += kVerifyUnroll * kVerifyThreads) {
+        int32_t id[kVerifyUnroll];
+        uint32_t ex[kVerifyUnroll];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + u * 256;
+        for (int u = 0; u < kVerifyUnroll; ++u) {
+          const int i = i0 + u * kVerifyThreads;
           id[u] = i < n ? pt[i] : 0;
           ex[u] = i < n ? et[i] : 0;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + u * 256;
+        for (int u = 0; u < kVerifyUnroll; ++u) {
+          const int i = i0 + u * kVerifyThreads;
           if (i < n) {
             if (static_cast<unsigned>(id[u]) >= static_cast<unsigned>(a.v.num_pages))
               bad = 1;
@@ -336,12 +365,10 @@ __global__ __launch_bounds__(256) void verify_append_kernel(VerifyAppendArgs a) 
     }
   }
   bad = __syncthreads_or(bad);
-  if (threadIdx.x == 0) a.v.abort[b] = static_cast<uint8_t>(bad ? 1 : 0);
-  if (bad || !pos_ok) return;
+  if (tid == 0) a.v.abort[b] = static_cast<uint8_t>(bad ? 1 : 0);
+  if (bad || !mine || !pos_ok) return;
   if (static_cast<unsigned>(pid) >= static_cast<unsigned>(a.w.num_pages)) return;
-  const int slot = pos % kPage;
-  for (int item = threadIdx.x; item < a.w.Hkv * 8; item += 256)
-    append_one<CACHE>(a.w, static_cast<int64_t>(b), item >> 3, item & 7, pid, slot);
+  append_store<CACHE>(a.w, prep, h, c, pid, pos % kPage);
 }
 
 // ---------------------------------------------------------------------------
@@ -374,7 +401,7 @@ struct DecodeArgs {
   void* out;
   float* ws_o;     // [slots][G][128] unnormalised weighted V
   float* ws_ml;    // [slots][G][2]   (max in log2 units, sum)
-  int32_t* ws_pre; // [B+1] page prefix sums of live requests (for the merge)
+  int32_t* ws_pre; // [B+1] page prefix sums of live requests
   int64_t page_stride;
   int32_t batch, max_pages, num_pages, Hq, Hkv, G, out_f32;
   float sm_scale;
@@ -498,6 +525,15 @@ struct SeqCursor {
     return static_cast<int>(p.ps - p.sx) + wave + kWaves * i;
   }
 };
+
+// workgroups w in [wf, wl] whose slices hold pages of the segment whose items
+// are [first, last]; the ones with an empty slice are skipped by callers
+__device__ __forceinline__ void segment_workgroups(int64_t first, int64_t last, int64_t W,
+                                                   int64_t NWG, int64_t& wf, int64_t& wl) {
+  // workgroup holding item x: largest w with w*W/NWG <= x
+  wf = ((first + 1) * NWG - 1) / W;
+  wl = ((last + 1) * NWG - 1) / W;
+}
 
 template <int CACHE, int DEPTH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
@@ -814,7 +850,13 @@ void decode_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // 5. merge of the pieces of split segments (fixed order: deterministic)
 // ---------------------------------------------------------------------------
-// one 128-thread workgroup per (request, kv-head, head in group); thread = dim
+// One workgroup of 128 threads per (request, kv-head, head in group); thread =
+// dim.  A separate pass: ordering the partial writes of other workgroups
+// inside the decode kernel would need a device-scope release/acquire per
+// piece, which on this part writes back and invalidates the L2 and costs far
+// more than this launch.
+constexpr int kMergeUnroll = 4;
+
 __global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a, int64_t NWG) {
   const int n = blockIdx.x % a.G;
   const int seg = blockIdx.x / a.G;
@@ -825,38 +867,45 @@ __global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a, int64_t NWG) {
   if (np == 0) return;
   const int64_t W = static_cast<int64_t>(a.Hkv) * a.ws_pre[a.batch];
   const int64_t first = static_cast<int64_t>(a.Hkv) * pre_b + static_cast<int64_t>(g) * np;
-  const int64_t last = first + np - 1;
-  // workgroup holding item x: largest w with w*W/NWG <= x
-  const int64_t wf = ((first + 1) * NWG - 1) / W;
-  const int64_t wl = ((last + 1) * NWG - 1) / W;
+  int64_t wf, wl;
+  segment_workgroups(first, first + np - 1, W, NWG, wf, wl);
   if (wf == wl) return;  // one piece: written by the decode kernel
   const int d = threadIdx.x;
   float M = -INFINITY, L = 0.f, O = 0.f;
-  for (int64_t w = wf; w <= wl; ++w) {
-    // with more workgroups than pages some own nothing and wrote no slot
-    if (w * W / NWG == (w + 1) * W / NWG) continue;
-    const int64_t pidx = (w + seg) * a.G + n;
-    const float m = a.ws_ml[pidx * 2];
-    if (m == -INFINITY) continue;
-    const float l = a.ws_ml[pidx * 2 + 1];
-    const float o = a.ws_o[pidx * kHeadDim + d];
-    if (m > M) {
-      const float r = (M == -INFINITY) ? 0.f : fast_exp2(M - m);
-      L *= r;
-      O *= r;
-      M = m;
+  for (int64_t w0 = wf; w0 <= wl; w0 += kMergeUnroll) {
+    // issue the loads of several pieces before using any of them
+    float m[kMergeUnroll], l[kMergeUnroll], o[kMergeUnroll];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int64_t w = w0 + u;
+      // past the last piece, or a workgroup with an empty slice: no piece
+      const bool has = w <= wl && w * W / NWG != (w + 1) * W / NWG;
+      const int64_t pidx = (w + seg) * a.G + n;
+      m[u] = has ? a.ws_ml[pidx * 2] : -INFINITY;
+      l[u] = has ? a.ws_ml[pidx * 2 + 1] : 0.f;
+      o[u] = has ? a.ws_o[pidx * kHeadDim + d] : 0.f;
     }
-    const float e = fast_exp2(m - M);
-    L += e * l;
-    O += e * o;
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      if (m[u] == -INFINITY) continue;
+      if (m[u] > M) {
+        const float r = (M == -INFINITY) ? 0.f : fast_exp2(M - m[u]);
+        L *= r;
+        O *= r;
+        M = m[u];
+      }
+      const float e = fast_exp2(m[u] - M);
+      L += e * l[u];
+      O += e * o[u];
+    }
   }
   const float vsc = a.v_scale ? a.v_scale[g] : 1.0f;
   const float v = L > 0.f ? O * (vsc / L) : 0.f;
-  const int64_t idx_out = (static_cast<int64_t>(b) * a.Hq + g * a.G + n) * kHeadDim + d;
+  const int64_t io = (static_cast<int64_t>(b) * a.Hq + g * a.G + n) * kHeadDim + d;
   if (a.out_f32)
-    static_cast<float*>(a.out)[idx_out] = v;
+    static_cast<float*>(a.out)[io] = v;
   else
-    static_cast<uint16_t*>(a.out)[idx_out] = __builtin_bit_cast(unsigned short, static_cast<__bf16>(v));
+    static_cast<uint16_t*>(a.out)[io] = __builtin_bit_cast(unsigned short, static_cast<__bf16>(v));
 }
 
 // ---------------------------------------------------------------------------
@@ -1126,6 +1175,7 @@ fp8kv_status fp8kv_verify_append(const fp8kv_cache_desc* desc, void* d_k_cache, 
       !d_abort || !d_pool_tags || (max_pages_per_seq > 0 && (!d_page_table || !d_expected_tags)))
     return FP8KV_INVALID_ARG;
   if (desc->cache_dtype == FP8KV_E4M3 && (!d_k_scale || !d_v_scale)) return FP8KV_INVALID_ARG;
+  if (desc->num_kv_heads * 8 > kVerifyThreads) return FP8KV_UNSUPPORTED;
   VerifyAppendArgs a;
   a.v = VerifyArgs{d_page_table, d_expected_tags, d_ctx_lens, d_pool_tags, d_abort,
                    max_pages_per_seq, desc->num_pages, kPage};
@@ -1147,9 +1197,11 @@ fp8kv_status fp8kv_verify_append(const fp8kv_cache_desc* desc, void* d_k_cache, 
   a.w.Hkv = desc->num_kv_heads;
   a.new_pos = d_new_pos;
   if (desc->cache_dtype == FP8KV_E4M3)
-    hipLaunchKernelGGL(verify_append_kernel<FP8KV_E4M3>, dim3(batch), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(verify_append_kernel<FP8KV_E4M3>, dim3(batch), dim3(kVerifyThreads), 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL(verify_append_kernel<FP8KV_BF16>, dim3(batch), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(verify_append_kernel<FP8KV_BF16>, dim3(batch), dim3(kVerifyThreads), 0,
+                       stream, a);
   return launched();
 }
 

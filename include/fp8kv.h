@@ -202,10 +202,11 @@ fp8kv_status fp8kv_verify_append(const fp8kv_cache_desc *desc, void *d_k_cache, 
 /*   o   = v_scale[g] * sum_j e^{s_j - max s} DEC(V[j][g]) / sum_j e^{s_j-max s}*/
 /* over the d_ctx_lens[b] tokens j of the request (token j at page           */
 /* d_page_table[b][j/16], slot j%16).  The (request, kv-head, page) work is   */
-/* shared equally by num_workers waves; a (request, kv-head) whose pages      */
-/* fall to several waves is finished by a log-sum-exp merge of their partial  */
-/* (max, sum, weighted V) in a fixed order (flash-decoding split-K), so the   */
-/* result is deterministic for a given num_workers.                           */
+/* shared equally by num_workers/4 workgroups of 4 waves; a (request,         */
+/* kv-head) whose pages fall to several workgroups is finished by a          */
+/* log-sum-exp merge of their partial (max, sum, weighted V) in workgroup    */
+/* order (flash-decoding split-K) in a second short kernel, so the result    */
+/* is deterministic for a given batch and num_workers.                       */
 /*   d_q: BF16 bits [batch][Hq][128];  d_out: [batch][Hq][128] of BF16 bits   */
 /*   (out_dtype FP8KV_OUT_BF16, round-to-nearest-even) or fp32 (FP8KV_OUT_F32).*/
 /*   d_abort (nullable): requests flagged 1 produce +0 rows and read nothing  */
@@ -215,9 +216,10 @@ fp8kv_status fp8kv_verify_append(const fp8kv_cache_desc *desc, void *d_k_cache, 
 /*   never dereferenced; their tokens are left out (results for such a        */
 /*   request are unspecified).                                                */
 /*   batch <= 4096.  num_workers: 0 picks the device's resident wave count    */
-/*   (compute units x 16); otherwise rounded up to a multiple of 4.           */
+/*   (compute units x 12); otherwise rounded up to a multiple of 4.           */
 /*   d_workspace: at least fp8kv_decode_workspace_size() bytes for the same   */
-/*   batch, num_q_heads and num_workers on the current device.                */
+/*   batch, num_q_heads and num_workers on the current device.  Calls that    */
+/*   share a workspace must not overlap.                                      */
 /* ------------------------------------------------------------------------ */
 int32_t fp8kv_decode_num_workers(int32_t requested);
 

@@ -139,7 +139,7 @@ def build(w: Workload, cache_dtype: int = fp8kv.E4M3, device="cuda", num_workers
     v_new = w.new_kv_bits("v", "torch", device).contiguous()
     nw = fp8kv.decode_num_workers(num_workers)
     need = fp8kv.decode_workspace_size(d, w.B, w.Hq, nw)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
     torch.cuda.synchronize()
     return DeviceStep(
         w=w, desc=d, K=K, V=V, k_scale=ks, v_scale=vs, k_scale_host=ksh, v_scale_host=vsh,
