@@ -62,3 +62,12 @@ def test_keys_independent_of_integer_type():
     a = w.kv_tokens("k", np.int64(2), 0, 5)
     b = w.kv_tokens("k", 2, 0, 5)
     assert (a == b).all()
+
+
+def test_head_slice_generator_matches():
+    for cfg in (1, 4):
+        w = workloads.make(cfg, batch=2)
+        L = int(w.ctx_before[1])
+        full = w.kv_tokens("v", 1, max(0, L - 40), L + 1)
+        for g in range(w.Hkv):
+            assert (w.kv_tokens_head("v", 1, max(0, L - 40), L + 1, g) == full[:, g, :]).all()

@@ -141,6 +141,22 @@ def draw_bits(key: int, start: int, count: int, backend: str = "numpy",
     return out
 
 
+def draw_bits_at(key: int, counters: np.ndarray, outlier_per_65536: int = 0,
+                 outlier_bits=BF16_20) -> np.ndarray:
+    """numpy backend of draw_bits for an explicit array of counters."""
+    key = int(key)
+    ctr = np.asarray(counters, dtype=np.uint64)
+    x = ((ctr + np.uint64(key)) & np.uint64(_M32)).astype(np.uint32)
+    h = _hash_np(x)
+    out = NORMAL_BF16[(h >> np.uint32(16)).astype(np.int64)]
+    if outlier_per_65536:
+        sel = (h & np.uint32(0xFFFF)) < np.uint32(outlier_per_65536)
+        neg = (h >> np.uint32(15)) & np.uint32(1)
+        ob = np.where(neg == 1, np.uint16(int(outlier_bits) | 0x8000), np.uint16(outlier_bits))
+        out = np.where(sel, ob, out).astype(np.uint16)
+    return out
+
+
 _TABLE_CACHE: dict = {}
 
 
@@ -224,6 +240,21 @@ class Workload:
                     bits[L - t0, 0, d] = v
                 else:
                     bits[L - t0, 0, d] = int(v.view(np.int16))
+        return bits
+
+    def kv_tokens_head(self, which: str, b: int, t0: int, t1: int, g: int,
+                       with_saturation=True) -> np.ndarray:
+        """The same bits as kv_tokens(...)[:, g, :] (numpy), generated for one
+        kv-head only: shape [t][D]."""
+        t = np.arange(t0, t1, dtype=np.uint64)[:, None]
+        d = np.arange(self.D, dtype=np.uint64)[None, :]
+        ctr = (t * np.uint64(self.Hkv) + np.uint64(g)) * np.uint64(self.D) + d
+        bits = draw_bits_at(self._kv_key(which, b), ctr.ravel(), self.outlier_per_65536)
+        bits = bits.reshape(t1 - t0, self.D)
+        L = int(self.ctx_before[b])
+        if with_saturation and self.saturate_new and g == 0 and t0 <= L < t1:
+            for dd, sgn in zip((5, 40, 77, 120), (0, 0x8000, 0, 0x8000)):
+                bits[L - t0, dd] = np.uint16(int(BF16_25) | sgn)
         return bits
 
     def q_bits(self, backend: str = "numpy", device=None):
