@@ -263,3 +263,37 @@ def test_abort_isolation(lib, dev):
                                  st.ctx_lens[kt].contiguous(), out_dtype=lib.OUT_F32,
                                  num_workers=64)
     assert np.abs(_host(out_k) - f_all[keep]).max() < 1e-5
+
+
+def test_pool_sync_and_device_check(lib):
+    """Tags change on the host pool; pool_sync uploads them on the stream; the
+    device check sees the new lifetime of a reclaimed page."""
+    N = 300
+    pool = lib.Pool(N, seed=9)
+    d_tags = torch.zeros(N, dtype=torch.int32, device="cuda")
+    pool.sync(d_tags)
+    assert (_host(d_tags).view(np.uint32) == pool.tags()).all()
+    reqs = [pool.alloc(k) for k in (5, 9, 2, 7)]
+    P = 9
+    pt = np.full((4, P), -1, np.int32)
+    et = np.zeros((4, P), np.uint32)
+    for b, (ids, tg) in enumerate(reqs):
+        pt[b, :ids.size] = ids
+        et[b, :tg.size] = tg
+    cl = np.array([80, 144, 20, 100], np.int32)
+    pool.sync(d_tags)
+    dpt = torch.from_numpy(pt).cuda()
+    det = torch.from_numpy(et.view(np.int32)).cuda()
+    dcl = torch.from_numpy(cl).cuda()
+    ab = lib.verify_tags(dpt, det, dcl, d_tags)
+    assert (_host(ab) == 0).all()
+    # request 1 is cancelled; its pages are reissued to a new request
+    pool.free(reqs[1][0])
+    _ = pool.alloc(pool.num_free - 9)
+    new_ids, _ = pool.alloc(9)
+    assert set(new_ids) == set(reqs[1][0])
+    pool.sync(d_tags)
+    ab = lib.verify_tags(dpt, det, dcl, d_tags)
+    exp = oracle.verify(pt, et, cl, pool.tags())
+    assert (_host(ab) == exp).all() and list(exp) == [0, 1, 0, 0]
+    pool.close()
