@@ -27,6 +27,31 @@ if ROOT not in sys.path:
 
 METRIC = "FP8 paged decode attn: tokens/s and achieved HBM GB/s (% of 8 TB/s) @1 GPU"
 PEAK_GBPS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_paged_fp8kv_amd", "csrc", "fp8kv_kernels.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_ragged64_hbm_counters.txt")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+
+
+def counter_traffic():
+    """HBM bytes per decode call from the committed counter summary, or None
+    when it is missing or was taken on a different kernel source."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    fields = {}
+    for line in open(PMC_SUMMARY):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_decode_call"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def log(msg: str):
@@ -143,6 +168,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip bf16 variant and tag overhead")
     ap.add_argument("--overhead-rounds", type=int, default=20)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus "
@@ -157,6 +184,16 @@ def main():
     from workloads import device
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = 1 << 30
+        x = torch.ones(n, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                          "launches": 3}), flush=True)
+        return
     log("bench: building ragged workload (64 requests, U[1024, 32768])")
     w = workloads.make(3)
     st = device.build(w, num_workers=args.num_workers)
@@ -186,9 +223,10 @@ def main():
                    "decode_waves": st.num_workers, "parallelism": "none (1 GPU)"},
         "hbm_gbps": round(gbps, 1), "pct_of_8tbps": round(100 * gbps / PEAK_GBPS, 2),
         "step_alg_bytes": step_bytes,
-        "roofline": {"bound": "hbm", "kernel": "decode attention (persistent pass + merge)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "fp8kv_decode_attention call (decode_kernel + merge_kernel)",
                      "achieved": round(attn_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(attn_gbps / PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(attn_gbps / PEAK_GBPS, 4), "traffic": counter_traffic(),
                      "alg_bytes_per_launch": attn_bytes,
                      "avg_launch_us": round(t_dec * 1e6, 2)},
         "tag_check_append_us": round(t_ver * 1e6, 2),
