@@ -165,6 +165,10 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--num-workers", type=int, default=0, help="decode waves (0 = device default)")
+    ap.add_argument("--workload", default="ragged",
+                    choices=["tiny", "uniform", "ragged", "long", "capacity"],
+                    help="which synthetic workload (the headline is 'ragged')")
+    ap.add_argument("--cache", default="e4m3", choices=["e4m3", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip bf16 variant and tag overhead")
     ap.add_argument("--overhead-rounds", type=int, default=20)
@@ -194,44 +198,55 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
                           "launches": 3}), flush=True)
         return
-    log("bench: building ragged workload (64 requests, U[1024, 32768])")
-    w = workloads.make(3)
-    st = device.build(w, num_workers=args.num_workers)
-    step_bytes, attn_bytes = alg_bytes(w, 0, True)
+    cfg = {"tiny": 1, "uniform": 2, "ragged": 3, "long": 4, "capacity": 5}[args.workload]
+    cache = 0 if args.cache == "e4m3" else 1
+    w = workloads.make(cfg)
+    log(f"bench: building workload {w.name} ({w.B} requests, {args.cache} cache)")
+    st = device.build(w, cache_dtype=cache, num_workers=args.num_workers)
     step = lambda: st.step(check_tags=True)  # noqa: E731
+    step()
+    torch.cuda.synchronize()
+    live = st.abort.cpu().numpy() == 0        # aborted requests read nothing
+    step_bytes, attn_bytes = alg_bytes(w, cache, True, active=live)
 
     for _ in range(args.warmup):
         step()
     log(f"bench: timing {args.steps} steps")
     t_step = time_steps(step, args.steps)
+    per_step = sorted(event_times([step], args.steps)[0])
+    p50 = per_step[len(per_step) // 2]
+    p95 = per_step[min(len(per_step) - 1, int(0.95 * len(per_step)))]
     # per-kernel HIP-event times on the launch stream
     nev = max(20, args.steps // 2)
     tva, td = event_times([st.verify_append, lambda: st.decode(True)], nev)
     t_dec = statistics.median(td) * 1e-3
     t_ver = statistics.median(tva) * 1e-3
-    tokens_s = w.B / t_step
+    tokens_s = int(live.sum()) / t_step
     gbps = step_bytes / t_step / 1e9
     attn_gbps = attn_bytes / t_dec / 1e9
     res = {
         "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "e4m3 cache; bf16/f16 MFMA, f32 accumulate", "data": "synthetic",
-        "config": {"workload": w.name, "requests": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
-                   "head_dim": 128, "page_tokens": 16, "kv_cache": "e4m3", "tag_check": True,
+        "dtype": f"{args.cache} cache; bf16/f16 MFMA, f32 accumulate", "data": "synthetic",
+        "config": {"workload": w.name, "requests": w.B, "live_requests": int(live.sum()),
+                   "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": 128, "page_tokens": 16, "kv_cache": args.cache, "tag_check": True,
                    "attended_tokens": int(w.ctx_lens.sum()),
                    "decode_waves": st.num_workers, "parallelism": "none (1 GPU)"},
+        "step_us_p50": round(p50 * 1e3, 2), "step_us_p95": round(p95 * 1e3, 2),
         "hbm_gbps": round(gbps, 1), "pct_of_8tbps": round(100 * gbps / PEAK_GBPS, 2),
         "step_alg_bytes": step_bytes,
         "roofline": {"bound": "hbm",
                      "kernel": "fp8kv_decode_attention call (decode_kernel + merge_kernel)",
                      "achieved": round(attn_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(attn_gbps / PEAK_GBPS, 4), "traffic": counter_traffic(),
+                     "frac": round(attn_gbps / PEAK_GBPS, 4),
+                     "traffic": counter_traffic() if (cfg == 3 and cache == 0) else None,
                      "alg_bytes_per_launch": attn_bytes,
                      "avg_launch_us": round(t_dec * 1e6, 2)},
         "tag_check_append_us": round(t_ver * 1e6, 2),
     }
-    if not args.no_extras:
+    if not args.no_extras and cfg == 3:
         log("bench: tag-check overhead (interleaved on/off)")
         off = lambda: st.step(check_tags=False)  # noqa: E731
         deltas = []
@@ -265,7 +280,7 @@ def main():
             del s2
             torch.cuda.empty_cache()
         res["uniform_32x8192"] = var
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and cfg == 3:
         log("bench: CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(res), flush=True)

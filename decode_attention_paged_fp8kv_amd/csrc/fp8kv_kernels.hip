@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fp8kv.h"
 #include "fp8kv_internal.h"
 
@@ -47,7 +49,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 #define FP8KV_DEPTH_E4M3 2
 #endif
 #ifndef FP8KV_DEPTH_BF16
-#define FP8KV_DEPTH_BF16 2
+#define FP8KV_DEPTH_BF16 1
 #endif
 // waves per compute unit the automatic worker count aims for
 #ifndef FP8KV_WAVES_PER_CU
@@ -213,25 +215,22 @@ struct Chunk16 {
   u32x4_t k0, k1, v0, v1;  // e4m3: k0/v0 hold 16 codes; bf16: the 2x16 raw bytes
 };
 
-// Load and encode dims [16c, 16c+16) of token `tok`, kv-head h.
+// Encode 16 consecutive dims of kv-head h (two 16-byte halves of K and of V).
 template <int CACHE>
-__device__ __forceinline__ Chunk16 append_prepare(const AppendArgs& a, int64_t tok, int h,
-                                                  int c) {
-  const int64_t src = (tok * a.Hkv + h) * kHeadDim + 16 * c;
-  const u32x4_t* kin = reinterpret_cast<const u32x4_t*>(a.k_new + src);
-  const u32x4_t* vin = reinterpret_cast<const u32x4_t*>(a.v_new + src);
+__device__ __forceinline__ Chunk16 append_encode(const AppendArgs& a, int h, u32x4_t k0,
+                                                 u32x4_t k1, u32x4_t v0, u32x4_t v1) {
   Chunk16 r;
-  r.k0 = kin[0];
-  r.k1 = kin[1];
-  r.v0 = vin[0];
-  r.v1 = vin[1];
+  r.k0 = k0;
+  r.k1 = k1;
+  r.v0 = v0;
+  r.v1 = v1;
   if constexpr (CACHE == FP8KV_E4M3) {
     const float ks = a.k_scale[h], vs = a.v_scale[h];
     u32x4_t kq = {0u, 0u, 0u, 0u}, vq = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const u32x4_t& ksrc = i < 8 ? r.k0 : r.k1;
-      const u32x4_t& vsrc = i < 8 ? r.v0 : r.v1;
+      const u32x4_t& ksrc = i < 8 ? k0 : k1;
+      const u32x4_t& vsrc = i < 8 ? v0 : v1;
       const int w = (i & 7) >> 1;
       const uint16_t kb = (i & 1) ? (ksrc[w] >> 16) : (ksrc[w] & 0xFFFF);
       const uint16_t vb = (i & 1) ? (vsrc[w] >> 16) : (vsrc[w] & 0xFFFF);
@@ -242,6 +241,16 @@ __device__ __forceinline__ Chunk16 append_prepare(const AppendArgs& a, int64_t t
     r.v0 = vq;
   }
   return r;
+}
+
+// Load and encode dims [16c, 16c+16) of token `tok`, kv-head h.
+template <int CACHE>
+__device__ __forceinline__ Chunk16 append_prepare(const AppendArgs& a, int64_t tok, int h,
+                                                  int c) {
+  const int64_t src = (tok * a.Hkv + h) * kHeadDim + 16 * c;
+  const u32x4_t* kin = reinterpret_cast<const u32x4_t*>(a.k_new + src);
+  const u32x4_t* vin = reinterpret_cast<const u32x4_t*>(a.v_new + src);
+  return append_encode<CACHE>(a, h, kin[0], kin[1], vin[0], vin[1]);
 }
 
 // Store a prepared chunk into slot `slot` of physical page `pid`.
@@ -277,6 +286,67 @@ __device__ __forceinline__ void append_store(const AppendArgs& a, const Chunk16&
       const int w = (i & 7) >> 1;
       *reinterpret_cast<uint16_t*>(vt + (f >> 3) * 1024 + 16 * vlane + 2 * (f & 7)) =
           static_cast<uint16_t>((i & 1) ? (vsrc[w] >> 16) : (vsrc[w] & 0xFFFF));
+    }
+  }
+}
+
+// 4-dim variant for the fused kernel: more lanes share one token's encode.
+// Dims [4c, 4c+4) of kv-head h: one 32-bit K store (e4m3) or 64-bit (bf16),
+// V scattered per element.
+struct Chunk4 {
+  u32x2_t k, v;  // e4m3: k.x / v.x hold 4 codes; bf16: the raw 8 bytes
+};
+
+template <int CACHE>
+__device__ __forceinline__ Chunk4 append_encode4(const AppendArgs& a, int h, u32x2_t k,
+                                                 u32x2_t v) {
+  Chunk4 r;
+  r.k = k;
+  r.v = v;
+  if constexpr (CACHE == FP8KV_E4M3) {
+    const float ks = a.k_scale[h], vs = a.v_scale[h];
+    unsigned kq = 0u, vq = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t kb = (i & 1) ? (k[i >> 1] >> 16) : (k[i >> 1] & 0xFFFF);
+      const uint16_t vb = (i & 1) ? (v[i >> 1] >> 16) : (v[i >> 1] & 0xFFFF);
+      kq |= e4m3_encode(bf16_to_f32(kb) / ks) << (8 * i);
+      vq |= e4m3_encode(bf16_to_f32(vb) / vs) << (8 * i);
+    }
+    r.k.x = kq;
+    r.v.x = vq;
+  }
+  return r;
+}
+
+template <int CACHE>
+__device__ __forceinline__ void append_store4(const AppendArgs& a, const Chunk4& r, int h, int c,
+                                              int32_t pid, int slot) {
+  const int64_t tile = static_cast<int64_t>(pid) * a.page_stride +
+                       static_cast<int64_t>(h) * Tile<CACHE>::kBytes;
+  uint8_t* kt = a.k_cache + tile;
+  uint8_t* vt = a.v_cache + tile;
+  const int d0 = 4 * c;
+  const int f0 = d0 & 31;
+  const int klane = 16 * (d0 >> 5) + slot;
+  if constexpr (CACHE == FP8KV_E4M3) {
+    *reinterpret_cast<unsigned*>(kt + (f0 >> 4) * 1024 + 16 * klane + (f0 & 15)) = r.k.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = d0 + i;
+      const int f = 4 * (d & 7) + (slot & 3);
+      const int vlane = 16 * (slot >> 2) + (d >> 3);
+      vt[(f >> 4) * 1024 + 16 * vlane + (f & 15)] = static_cast<uint8_t>(r.v.x >> (8 * i));
+    }
+  } else {
+    *reinterpret_cast<u32x2_t*>(kt + (f0 >> 3) * 1024 + 16 * klane + 2 * (f0 & 7)) = r.k;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = d0 + i;
+      const int f = 4 * (d & 7) + (slot & 3);
+      const int vlane = 16 * (slot >> 2) + (d >> 3);
+      *reinterpret_cast<uint16_t*>(vt + (f >> 3) * 1024 + 16 * vlane + 2 * (f & 7)) =
+          static_cast<uint16_t>((i & 1) ? (r.v[i >> 1] >> 16) : (r.v[i >> 1] & 0xFFFF));
     }
   }
 }
@@ -323,44 +393,66 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_append_kernel(VerifyApp
   const int ctx = a.v.ctx_lens[b];
   const int pos = a.new_pos[b];
   const bool pos_ok = pos >= 0 && pos / kPage < a.w.max_pages;
-  // this thread's share of the append (Hkv * 8 chunks of 16 dims)
-  const bool mine = tid < a.w.Hkv * 8;
-  const int h = tid >> 3, c = tid & 7;
+  const int n = ctx < 0 ? 0 : (ctx + a.v.page_size - 1) / a.v.page_size;
+  int bad = (ctx < 0 || n > a.v.max_pages) ? 1 : 0;
+  const int nchk = bad ? 0 : n;
+  const int32_t* pt = a.v.page_table + static_cast<int64_t>(b) * a.v.max_pages;
+  const uint32_t* et = a.v.expected + static_cast<int64_t>(b) * a.v.max_pages;
+  // 1. the first round of the check's loads: page ids and expected tags
+  int32_t id[kVerifyUnroll];
+  uint32_t ex[kVerifyUnroll];
+#pragma unroll
+  for (int u = 0; u < kVerifyUnroll; ++u) {
+    const int i = tid + u * kVerifyThreads;
+    id[u] = i < nchk ? pt[i] : 0;
+    ex[u] = i < nchk ? et[i] : 0;
+  }
+  // 2. this thread's share of the append (4 dims of one kv-head): the token's
+  //    inputs and its page id
+  const bool mine = tid < a.w.Hkv * (kHeadDim / 4);
+  const int h = tid >> 5, c = tid & 31;
+  const int64_t src = (static_cast<int64_t>(b) * a.w.Hkv + h) * kHeadDim + 4 * c;
+  u32x2_t kin = {0u, 0u}, vin = {0u, 0u};
   int32_t pid = -1;
-  Chunk16 prep;
   if (mine && pos_ok) {
     pid = a.w.page_table[static_cast<int64_t>(b) * a.w.max_pages + pos / kPage];
-    prep = append_prepare<CACHE>(a.w, static_cast<int64_t>(b), h, c);
+    kin = *reinterpret_cast<const u32x2_t*>(a.w.k_new + src);
+    vin = *reinterpret_cast<const u32x2_t*>(a.w.v_new + src);
   }
-  int bad = 0;
-  if (ctx < 0) {
-    bad = 1;
-  } else {
-    const int n = (ctx + a.v.page_size - 1) / a.v.page_size;
-    if (n > a.v.max_pages) {
-      bad = 1;
-    } else {
-      const int32_t* pt = a.v.page_table + static_cast<int64_t>(b) * a.v.max_pages;
-      const uint32_t* et = a.v.expected + static_cast<int64_t>(b) * a.v.max_pages;
-      for (int i0 = tid; i0 < n; i0 += kVerifyUnroll * kVerifyThreads) {
-        int32_t id[kVerifyUnroll];
-        uint32_t ex[kVerifyUnroll];
+  // 3. current tags of the listed pages
+  uint32_t cur[kVerifyUnroll];
 #pragma unroll
-        for (int u = 0; u < kVerifyUnroll; ++u) {
-          const int i = i0 + u * kVerifyThreads;
-          id[u] = i < n ? pt[i] : 0;
-          ex[u] = i < n ? et[i] : 0;
-        }
+  for (int u = 0; u < kVerifyUnroll; ++u) {
+    const int i = tid + u * kVerifyThreads;
+    const bool valid = static_cast<unsigned>(id[u]) < static_cast<unsigned>(a.v.num_pages);
+    cur[u] = (i < nchk && valid) ? a.v.tags[id[u]] : 0u;
+    if (i < nchk && (!valid)) bad = 1;
+  }
+  // 4. encode while the tag loads are in flight
+  Chunk4 prep;
+  if (mine && pos_ok) prep = append_encode4<CACHE>(a.w, h, kin, vin);
+  // 5. compare; requests longer than one round continue in a loop
 #pragma unroll
-        for (int u = 0; u < kVerifyUnroll; ++u) {
-          const int i = i0 + u * kVerifyThreads;
-          if (i < n) {
-            if (static_cast<unsigned>(id[u]) >= static_cast<unsigned>(a.v.num_pages))
-              bad = 1;
-            else if (a.v.tags[id[u]] != ex[u])
-              bad = 1;
-          }
-        }
+  for (int u = 0; u < kVerifyUnroll; ++u) {
+    const int i = tid + u * kVerifyThreads;
+    if (i < nchk && cur[u] != ex[u]) bad = 1;
+  }
+  for (int i0 = tid + kVerifyUnroll * kVerifyThreads; i0 < nchk;
+       i0 += kVerifyUnroll * kVerifyThreads) {
+#pragma unroll
+    for (int u = 0; u < kVerifyUnroll; ++u) {
+      const int i = i0 + u * kVerifyThreads;
+      id[u] = i < nchk ? pt[i] : 0;
+      ex[u] = i < nchk ? et[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kVerifyUnroll; ++u) {
+      const int i = i0 + u * kVerifyThreads;
+      if (i < nchk) {
+        if (static_cast<unsigned>(id[u]) >= static_cast<unsigned>(a.v.num_pages))
+          bad = 1;
+        else if (a.v.tags[id[u]] != ex[u])
+          bad = 1;
       }
     }
   }
@@ -368,7 +460,7 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_append_kernel(VerifyApp
   if (tid == 0) a.v.abort[b] = static_cast<uint8_t>(bad ? 1 : 0);
   if (bad || !mine || !pos_ok) return;
   if (static_cast<unsigned>(pid) >= static_cast<unsigned>(a.w.num_pages)) return;
-  append_store<CACHE>(a.w, prep, h, c, pid, pos % kPage);
+  append_store4<CACHE>(a.w, prep, h, c, pid, pos % kPage);
 }
 
 // ---------------------------------------------------------------------------
@@ -661,12 +753,27 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int s = 0; s < DEPTH; ++s) pid_ring[s] = fetch_pid();
 
+  // Q fragment (B operand of the QK^T MFMA) of a piece: lane (n, qd) holds,
+  // for step kk, q[head n][32 qd + 8 kk + i], i < 8; heads past the group are 0
+  auto load_q = [&](const Piece& pc, u32x4_t (&dst)[4]) {
+    const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(
+        a.q + (static_cast<int64_t>(pc.b) * a.Hq + pc.g * a.G + n) * kHeadDim + 32 * qd);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) dst[kk] = n < a.G ? qrow[kk] : u32x4_t{0u, 0u, 0u, 0u};
+  };
+  u32x4_t qcur[4], qnext[4];
+  load_q(first, qcur);
+
   Piece P = first;  // piece being processed (all waves visit every piece)
   for (;;) {
     const int cnt = wave_count(P, wave);
     const int iters = (cnt + DEPTH - 1) / DEPTH * DEPTH;
     const int pg0 = static_cast<int>(P.ps - P.sx) + wave;  // my first page in the piece
     const int ctx = a.ctx_lens[P.b];
+    // the next piece's Q is loaded now, behind this piece's pages
+    Piece Pn = P;
+    const bool has_next = next_piece(Pn, s_pre, B, a.Hkv, X1);
+    if (has_next) load_q(Pn, qnext);
 
     f32x4_t acc[8];
 #pragma unroll
@@ -676,15 +783,8 @@ void decode_kernel(DecodeArgs a) {
 
     if (cnt > 0) {
       bf16x8_t qf[4];
-      const int hq = P.g * a.G + n;
-      const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(
-          a.q + (static_cast<int64_t>(P.b) * a.Hq + hq) * kHeadDim + 32 * qd);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (n < a.G) w = qrow[kk];
-        qf[kk] = __builtin_bit_cast(bf16x8_t, w);
-      }
+      for (int kk = 0; kk < 4; ++kk) qf[kk] = __builtin_bit_cast(bf16x8_t, qcur[kk]);
       // scores in log2 units: s = (q.k_code) * sm_scale * k_scale * log2(e)
       const float sc = a.sm_scale * (a.k_scale ? a.k_scale[P.g] : 1.0f) * kLog2e;
 
@@ -843,69 +943,85 @@ void decode_kernel(DecodeArgs a) {
       }
     }
     __syncthreads();  // LDS is reused by the next piece
-    if (!next_piece(P, s_pre, B, a.Hkv, X1)) break;
+    if (!has_next) break;
+    P = Pn;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qcur[kk] = qnext[kk];
   }
 }
 
 // ---------------------------------------------------------------------------
 // 5. merge of the pieces of split segments (fixed order: deterministic)
 // ---------------------------------------------------------------------------
-// One workgroup of 128 threads per (request, kv-head, head in group); thread =
-// dim.  A separate pass: ordering the partial writes of other workgroups
+// Workgroups stride over (request, kv-head) segments; threads take (head, 4
+// dims).  A separate pass: ordering the partial writes of other workgroups
 // inside the decode kernel would need a device-scope release/acquire per
 // piece, which on this part writes back and invalidates the L2 and costs far
 // more than this launch.
 constexpr int kMergeUnroll = 4;
+constexpr int kMergeThreads = 256;
 
-__global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a, int64_t NWG) {
-  const int n = blockIdx.x % a.G;
-  const int seg = blockIdx.x / a.G;
-  const int b = seg / a.Hkv;
-  const int g = seg % a.Hkv;
-  const int pre_b = a.ws_pre[b];
-  const int np = a.ws_pre[b + 1] - pre_b;
-  if (np == 0) return;
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int64_t NWG) {
   const int64_t W = static_cast<int64_t>(a.Hkv) * a.ws_pre[a.batch];
-  const int64_t first = static_cast<int64_t>(a.Hkv) * pre_b + static_cast<int64_t>(g) * np;
-  int64_t wf, wl;
-  segment_workgroups(first, first + np - 1, W, NWG, wf, wl);
-  if (wf == wl) return;  // one piece: written by the decode kernel
-  const int d = threadIdx.x;
-  float M = -INFINITY, L = 0.f, O = 0.f;
-  for (int64_t w0 = wf; w0 <= wl; w0 += kMergeUnroll) {
-    // issue the loads of several pieces before using any of them
-    float m[kMergeUnroll], l[kMergeUnroll], o[kMergeUnroll];
+  for (int seg = blockIdx.x; seg < a.batch * a.Hkv; seg += gridDim.x) {
+    const int b = seg / a.Hkv;
+    const int g = seg % a.Hkv;
+    const int pre_b = a.ws_pre[b];
+    const int np = a.ws_pre[b + 1] - pre_b;
+    if (np == 0) continue;
+    const int64_t first = static_cast<int64_t>(a.Hkv) * pre_b + static_cast<int64_t>(g) * np;
+    int64_t wf, wl;
+    segment_workgroups(first, first + np - 1, W, NWG, wf, wl);
+    if (wf == wl) continue;  // one piece: written by the decode kernel
+    const float vsc = a.v_scale ? a.v_scale[g] : 1.0f;
+    for (int idx = threadIdx.x; idx < a.G * (kHeadDim / 4); idx += kMergeThreads) {
+      const int n = idx / (kHeadDim / 4);
+      const int d = 4 * (idx % (kHeadDim / 4));
+      float M = -INFINITY, L = 0.f;
+      f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+      for (int64_t w0 = wf; w0 <= wl; w0 += kMergeUnroll) {
+        // issue the loads of several pieces before using any of them
+        float m[kMergeUnroll], l[kMergeUnroll];
+        f32x4_t o[kMergeUnroll];
 #pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) {
-      const int64_t w = w0 + u;
-      // past the last piece, or a workgroup with an empty slice: no piece
-      const bool has = w <= wl && w * W / NWG != (w + 1) * W / NWG;
-      const int64_t pidx = (w + seg) * a.G + n;
-      m[u] = has ? a.ws_ml[pidx * 2] : -INFINITY;
-      l[u] = has ? a.ws_ml[pidx * 2 + 1] : 0.f;
-      o[u] = has ? a.ws_o[pidx * kHeadDim + d] : 0.f;
-    }
+        for (int u = 0; u < kMergeUnroll; ++u) {
+          const int64_t w = w0 + u;
+          // past the last piece, or a workgroup with an empty slice: no piece
+          const bool has = w <= wl && w * W / NWG != (w + 1) * W / NWG;
+          const int64_t pidx = (w + seg) * a.G + n;
+          m[u] = has ? a.ws_ml[pidx * 2] : -INFINITY;
+          l[u] = has ? a.ws_ml[pidx * 2 + 1] : 0.f;
+          o[u] = has ? *reinterpret_cast<const f32x4_t*>(a.ws_o + pidx * kHeadDim + d)
+                     : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) {
-      if (m[u] == -INFINITY) continue;
-      if (m[u] > M) {
-        const float r = (M == -INFINITY) ? 0.f : fast_exp2(M - m[u]);
-        L *= r;
-        O *= r;
-        M = m[u];
+        for (int u = 0; u < kMergeUnroll; ++u) {
+          if (m[u] == -INFINITY) continue;
+          if (m[u] > M) {
+            const float r = (M == -INFINITY) ? 0.f : fast_exp2(M - m[u]);
+            L *= r;
+            O *= r;
+            M = m[u];
+          }
+          const float e = fast_exp2(m[u] - M);
+          L += e * l[u];
+          O += e * o[u];
+        }
       }
-      const float e = fast_exp2(m[u] - M);
-      L += e * l[u];
-      O += e * o[u];
+      const float inv = L > 0.f ? vsc / L : 0.f;
+      const int64_t io = (static_cast<int64_t>(b) * a.Hq + g * a.G + n) * kHeadDim + d;
+      if (a.out_f32) {
+        *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + io) = O * inv;
+      } else {
+        u32x2_t w;
+        w.x = __builtin_bit_cast(unsigned short, static_cast<__bf16>(O[0] * inv)) |
+              (static_cast<unsigned>(__builtin_bit_cast(unsigned short, static_cast<__bf16>(O[1] * inv))) << 16);
+        w.y = __builtin_bit_cast(unsigned short, static_cast<__bf16>(O[2] * inv)) |
+              (static_cast<unsigned>(__builtin_bit_cast(unsigned short, static_cast<__bf16>(O[3] * inv))) << 16);
+        *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + io) = w;
+      }
     }
   }
-  const float vsc = a.v_scale ? a.v_scale[g] : 1.0f;
-  const float v = L > 0.f ? O * (vsc / L) : 0.f;
-  const int64_t io = (static_cast<int64_t>(b) * a.Hq + g * a.G + n) * kHeadDim + d;
-  if (a.out_f32)
-    static_cast<float*>(a.out)[io] = v;
-  else
-    static_cast<uint16_t*>(a.out)[io] = __builtin_bit_cast(unsigned short, static_cast<__bf16>(v));
 }
 
 // ---------------------------------------------------------------------------
@@ -949,11 +1065,19 @@ int tile_bytes(const fp8kv_cache_desc* d) {
 
 // Workers (waves) of the decode kernel: all of them resident at once.
 int32_t device_workers() {
+  // compute-unit count per device, queried once
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int32_t> cached[kMaxDevices] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int32_t c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c * FP8KV_WAVES_PER_CU;
+  }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
+  if (dev >= 0 && dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
   return cus * FP8KV_WAVES_PER_CU;
 }
 
@@ -1154,8 +1278,9 @@ fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc* desc, const void* d_
   }
   st = launched();
   if (st != FP8KV_OK) return st;
-  hipLaunchKernelGGL(merge_kernel, dim3(batch * desc->num_kv_heads * G), dim3(128), 0, stream, a,
-                     static_cast<int64_t>(blocks));
+  const int segs = batch * desc->num_kv_heads;
+  hipLaunchKernelGGL(merge_kernel, dim3(segs < 1024 ? segs : 1024), dim3(kMergeThreads), 0, stream,
+                     a, static_cast<int64_t>(blocks));
   return launched();
 }
 
@@ -1175,7 +1300,7 @@ fp8kv_status fp8kv_verify_append(const fp8kv_cache_desc* desc, void* d_k_cache, 
       !d_abort || !d_pool_tags || (max_pages_per_seq > 0 && (!d_page_table || !d_expected_tags)))
     return FP8KV_INVALID_ARG;
   if (desc->cache_dtype == FP8KV_E4M3 && (!d_k_scale || !d_v_scale)) return FP8KV_INVALID_ARG;
-  if (desc->num_kv_heads * 8 > kVerifyThreads) return FP8KV_UNSUPPORTED;
+  if (desc->num_kv_heads * (kHeadDim / 4) > kVerifyThreads) return FP8KV_UNSUPPORTED;
   VerifyAppendArgs a;
   a.v = VerifyArgs{d_page_table, d_expected_tags, d_ctx_lens, d_pool_tags, d_abort,
                    max_pages_per_seq, desc->num_pages, kPage};

@@ -185,6 +185,7 @@ fp8kv_status fp8kv_append(const fp8kv_cache_desc *desc, void *d_k_cache, void *d
 /* quantizes the request's new token (d_k_new/d_v_new row b, BF16             */
 /* [batch][Hkv][128]) into position d_new_pos[b].  The check is still its    */
 /* own batched pass ahead of attention, as the integrity section describes.  */
+/* Hkv <= 16 (one workgroup encodes the whole token).                        */
 /* ------------------------------------------------------------------------ */
 fp8kv_status fp8kv_verify_append(const fp8kv_cache_desc *desc, void *d_k_cache, void *d_v_cache,
                                  const float *d_k_scale, const float *d_v_scale,

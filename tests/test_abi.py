@@ -110,7 +110,7 @@ def test_argument_validation_before_any_device_call():
              ctypes.c_int32(16), None, None) == 0
     # fused check + append: too many kv-heads for one workgroup
     va = lib.fp8kv_verify_append
-    big = fp8kv.desc(8, 65)
+    big = fp8kv.desc(8, 17)
     assert va(ctypes.byref(big), fake, fake, fake, fake, fake, fake, fake, fake, fake,
               ctypes.c_int32(4), fake, ctypes.c_int32(2), fake, fake, None) == -2
 
