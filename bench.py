@@ -105,6 +105,36 @@ def event_times(fns, steps: int):
     return [[ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)] for i in range(len(fns))]
 
 
+def capture_graphs(st, fns):
+    """One captured HIP graph per function; each replay is checked bit for bit
+    against an eager call (with eager work in between) before it is timed."""
+    import torch
+    outs = lambda: (st.out.clone(), st.abort.clone())  # noqa: E731
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    graphs = []
+    for f in fns:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            f()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    fns[0]()
+    ref = outs()
+    for _ in range(3):
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        got = outs()
+        if not all(torch.equal(a, b) for a, b in zip(got, ref)):
+            raise RuntimeError("graph replay of the step differs from the eager step")
+        fns[0]()
+    return [g.replay for g in graphs]
+
+
 def cpu_baseline(w, target_s: float = 15.0):
     """The oracle as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -174,6 +204,9 @@ def main():
     ap.add_argument("--overhead-rounds", type=int, default=20)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM counters)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a captured HIP graph of the step (no host launch "
+                         "cost; for workloads whose GPU time is below the binding's)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus "
@@ -209,6 +242,10 @@ def main():
     live = st.abort.cpu().numpy() == 0        # aborted requests read nothing
     step_bytes, attn_bytes = alg_bytes(w, cache, True, active=live)
 
+    verify_append = st.verify_append
+    decode = lambda: st.decode(True)  # noqa: E731
+    if args.graph:
+        step, verify_append, decode = capture_graphs(st, [step, verify_append, decode])
     for _ in range(args.warmup):
         step()
     log(f"bench: timing {args.steps} steps")
@@ -218,7 +255,7 @@ def main():
     p95 = per_step[min(len(per_step) - 1, int(0.95 * len(per_step)))]
     # per-kernel HIP-event times on the launch stream
     nev = max(20, args.steps // 2)
-    tva, td = event_times([st.verify_append, lambda: st.decode(True)], nev)
+    tva, td = event_times([verify_append, decode], nev)
     t_dec = statistics.median(td) * 1e-3
     t_ver = statistics.median(tva) * 1e-3
     tokens_s = int(live.sum()) / t_step
@@ -245,6 +282,7 @@ def main():
                      "alg_bytes_per_launch": attn_bytes,
                      "avg_launch_us": round(t_dec * 1e6, 2)},
         "tag_check_append_us": round(t_ver * 1e6, 2),
+        "launch": "hip graph replay" if args.graph else "eager",
     }
     if not args.no_extras and cfg == 3:
         log("bench: tag-check overhead (interleaved on/off)")

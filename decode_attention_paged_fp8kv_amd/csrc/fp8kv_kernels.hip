@@ -567,6 +567,16 @@ struct SeqCursor {
   }
 };
 
+// Slices get at least this many pages (one per wave): with fewer pages than
+// workgroups, one page per slice would cut every segment into pieces that the
+// merge then walks one by one, and longer slices chain more dependent loads per
+// workgroup.  Both kernels derive the count from the page total alone.
+constexpr int64_t kMinSlice = 4;
+__device__ __forceinline__ int64_t slice_count(int64_t W, int64_t grid) {
+  const int64_t want = (W + kMinSlice - 1) / kMinSlice;
+  return want < 1 ? 1 : (want < grid ? want : grid);
+}
+
 // workgroups w in [wf, wl] whose slices hold pages of the segment whose items
 // are [first, last]; the ones with an empty slice are skipped by callers
 __device__ __forceinline__ void segment_workgroups(int64_t first, int64_t last, int64_t W,
@@ -652,11 +662,12 @@ void decode_kernel(DecodeArgs a) {
 
   // ---- this workgroup's slice --------------------------------------------
   const int64_t W = static_cast<int64_t>(a.Hkv) * s_pre[B];
-  const int64_t NWG = gridDim.x;
+  const int64_t NWG = slice_count(W, gridDim.x);
   const int64_t bw = blockIdx.x;
+  if (bw >= NWG) return;  // fewer slices than workgroups (uniform: no barrier follows)
   const int64_t X0 = bw * W / NWG;
   const int64_t X1 = (bw + 1) * W / NWG;
-  if (X0 >= X1) return;  // uniform over the workgroup: no barrier follows
+  if (X0 >= X1) return;
 
   const Piece first = first_piece(s_pre, B, a.Hkv, X0, X1);
   SeqCursor<DEPTH> I{first, 0, wave_count(first, wave), false};  // next page to load
@@ -914,11 +925,12 @@ void decode_kernel(DecodeArgs a) {
 // inside the decode kernel would need a device-scope release/acquire per
 // piece, which on this part writes back and invalidates the L2 and costs far
 // more than this launch.
-constexpr int kMergeUnroll = 4;
+constexpr int kMergeUnroll = 8;
 constexpr int kMergeThreads = 256;
 
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int64_t NWG) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int64_t grid) {
   const int64_t W = static_cast<int64_t>(a.Hkv) * a.ws_pre[a.batch];
+  const int64_t NWG = slice_count(W, grid);
   for (int seg = blockIdx.x; seg < a.batch * a.Hkv; seg += gridDim.x) {
     const int b = seg / a.Hkv;
     const int g = seg % a.Hkv;
@@ -926,8 +938,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int6
     const int np = a.ws_pre[b + 1] - pre_b;
     if (np == 0) continue;
     const int64_t first = static_cast<int64_t>(a.Hkv) * pre_b + static_cast<int64_t>(g) * np;
+    const int64_t last = first + np - 1;
     int64_t wf, wl;
-    segment_workgroups(first, first + np - 1, W, NWG, wf, wl);
+    segment_workgroups(first, last, W, NWG, wf, wl);
     if (wf == wl) continue;  // one piece: written by the decode kernel
     const float vsc = a.v_scale ? a.v_scale[g] : 1.0f;
     for (int idx = threadIdx.x; idx < a.G * (kHeadDim / 4); idx += kMergeThreads) {
@@ -935,15 +948,18 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int6
       const int d = 4 * (idx % (kHeadDim / 4));
       float M = -INFINITY, L = 0.f;
       f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-      for (int64_t w0 = wf; w0 <= wl; w0 += kMergeUnroll) {
+      // pieces in workgroup order: from the workgroup holding item x, jump to
+      // the start of the next slice, so workgroups with empty slices (more
+      // workgroups than pages) are never visited
+      for (int64_t x = first; x <= last;) {
         // issue the loads of several pieces before using any of them
         float m[kMergeUnroll], l[kMergeUnroll];
         f32x4_t o[kMergeUnroll];
 #pragma unroll
         for (int u = 0; u < kMergeUnroll; ++u) {
-          const int64_t w = w0 + u;
-          // past the last piece, or a workgroup with an empty slice: no piece
-          const bool has = w <= wl && w * W / NWG != (w + 1) * W / NWG;
+          const bool has = x <= last;
+          const int64_t w = ((x + 1) * NWG - 1) / W;
+          if (has) x = (w + 1) * W / NWG;
           const int64_t pidx = (w + seg) * a.G + n;
           m[u] = has ? a.ws_ml[pidx * 2] : -INFINITY;
           l[u] = has ? a.ws_ml[pidx * 2 + 1] : 0.f;

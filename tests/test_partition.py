@@ -3,15 +3,20 @@
 The persistent decode gives wave w of NW the items [w*W/NW, (w+1)*W/NW) of
 the (request, kv-head, page) list; a piece that is not a whole segment goes to
 slot w + segment, and the merge pass collects, for each segment, the slots of
-the non-empty waves between the waves holding its first and last item.  This
+the non-empty waves between the waves holding its first and last item (found by
+jumping from slice to slice, so empty slices cost nothing).  This
 checks, in integers, that every slot is written once and that each segment's
 pieces tile its pages exactly -- for empty requests, more waves than pages and
-fewer waves than segments alike.
+fewer waves than segments alike.  Slices hold at least 4 pages: with less work
+than that per workgroup, only ceil(W / 4) workgroups take slices.
 """
 import random
 
 
-def _check(pages, Hkv, NW):
+MIN_SLICE = 4  # pages per slice at least: the slice count is min(grid, ceil(W / 4))
+
+
+def _check(pages, Hkv, grid):
     pre = [0]
     for n in pages:
         pre.append(pre[-1] + n)
@@ -19,6 +24,8 @@ def _check(pages, Hkv, NW):
     W = Hkv * pre[-1]
     if W == 0:
         return
+    NW = max(1, min(grid, -(-W // MIN_SLICE)))
+    assert NW == grid or W < grid * MIN_SLICE
     slots = {}
     for w in range(NW):
         x0, x1 = w * W // NW, (w + 1) * W // NW
@@ -48,7 +55,16 @@ def _check(pages, Hkv, NW):
             if wf == wl:
                 assert all(v[0] != seg for v in slots.values())
                 continue
-            got = [slots[w + seg] for w in range(wf, wl + 1) if w * W // NW != (w + 1) * W // NW]
+            nonempty = [w for w in range(wf, wl + 1) if w * W // NW != (w + 1) * W // NW]
+            # the merge pass enumerates them by jumping from the workgroup holding
+            # item x to the start of the next slice (empty slices never visited)
+            jumped, x = [], first
+            while x <= last:
+                w = ((x + 1) * NW - 1) // W
+                jumped.append(w)
+                x = (w + 1) * W // NW
+            assert jumped == nonempty
+            got = [slots[w + seg] for w in nonempty]
             assert all(p[0] == seg for p in got)
             cov = sorted((p[1], p[2]) for p in got)
             assert cov[0][0] == first and cov[-1][1] == last + 1
@@ -61,13 +77,13 @@ def test_partition_random():
         B = rng.randint(1, 7)
         Hkv = rng.randint(1, 4)
         pages = [rng.choice([0, 0, 1, 2, 3, 5, 17, 40]) for _ in range(B)]
-        for NW in (4, 8, 12, 64, 4096):
-            _check(pages, Hkv, NW)
+        for grid in (4, 8, 12, 64, 4096):
+            _check(pages, Hkv, grid)
 
 
 def test_partition_workload_shapes():
     import workloads
     for cfg in (1, 3):
         w = workloads.make(cfg)
-        for NW in (64, 4096):
-            _check([int(n) for n in w.n_pages], w.Hkv, NW)
+        for grid in (64, 768, 4096):
+            _check([int(n) for n in w.n_pages], w.Hkv, grid)
