@@ -192,8 +192,8 @@ def cpu_baseline(w, target_s: float = 15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--num-workers", type=int, default=0, help="decode waves (0 = device default)")
     ap.add_argument("--workload", default="ragged",
                     choices=["tiny", "uniform", "ragged", "long", "capacity"],
@@ -204,6 +204,10 @@ def main():
     ap.add_argument("--overhead-rounds", type=int, default=20)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM counters)")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="cycle the steps over R copies of the workload's device state so a "
+                         "step's reads are not served by the 256 MB last-level cache (0 = 2 for "
+                         "the uniform workload, whose cache is 538 MB, else 1)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a captured HIP graph of the step (no host launch "
                          "cost; for workloads whose GPU time is below the binding's)")
@@ -234,18 +238,33 @@ def main():
     cfg = {"tiny": 1, "uniform": 2, "ragged": 3, "long": 4, "capacity": 5}[args.workload]
     cache = 0 if args.cache == "e4m3" else 1
     w = workloads.make(cfg)
-    log(f"bench: building workload {w.name} ({w.B} requests, {args.cache} cache)")
-    st = device.build(w, cache_dtype=cache, num_workers=args.num_workers)
-    step = lambda: st.step(check_tags=True)  # noqa: E731
-    step()
+    R = args.rotate if args.rotate > 0 else (2 if cfg == 2 else 1)
+    log(f"bench: building workload {w.name} ({w.B} requests, {args.cache} cache, {R} cop"
+        f"{'y' if R == 1 else 'ies'})")
+    states = [device.build(w, cache_dtype=cache, num_workers=args.num_workers) for _ in range(R)]
+    st = states[0]
+    st.step(check_tags=True)
     torch.cuda.synchronize()
     live = st.abort.cpu().numpy() == 0        # aborted requests read nothing
     step_bytes, attn_bytes = alg_bytes(w, cache, True, active=live)
 
-    verify_append = st.verify_append
-    decode = lambda: st.decode(True)  # noqa: E731
+    def cycle(fns):
+        """A callable that runs the next copy's function on each call."""
+        k = [0]
+
+        def run():
+            fns[k[0] % len(fns)]()
+            k[0] += 1
+        return run
+
+    steps_ = [lambda s=s: s.step(check_tags=True) for s in states]
+    vas = [s.verify_append for s in states]
+    decs = [lambda s=s: s.decode(True) for s in states]
     if args.graph:
-        step, verify_append, decode = capture_graphs(st, [step, verify_append, decode])
+        caps = [capture_graphs(s, [a, b, c]) for s, a, b, c in zip(states, steps_, vas, decs)]
+        steps_, vas, decs = ([c[i] for c in caps] for i in range(3))
+    step, verify_append, decode = cycle(steps_), cycle(vas), cycle(decs)
+    verify_only = cycle([s.verify for s in states])
     for _ in range(args.warmup):
         step()
     log(f"bench: timing {args.steps} steps")
@@ -256,6 +275,7 @@ def main():
     # per-kernel HIP-event times on the launch stream
     nev = max(20, args.steps // 2)
     tva, td = event_times([verify_append, decode], nev)
+    tv = event_times([verify_only], nev)[0]
     t_dec = statistics.median(td) * 1e-3
     t_ver = statistics.median(tva) * 1e-3
     tokens_s = int(live.sum()) / t_step
@@ -282,10 +302,15 @@ def main():
                      "alg_bytes_per_launch": attn_bytes,
                      "avg_launch_us": round(t_dec * 1e6, 2)},
         "tag_check_append_us": round(t_ver * 1e6, 2),
+        # HIP events around one call: for kernels this short the figure includes the
+        # host's launch time; the kernel-trace summaries hold the GPU times
+        "tag_check_alone_us": round(statistics.median(tv) * 1e3, 2),
+        "state_copies": R,
         "launch": "hip graph replay" if args.graph else "eager",
     }
     if not args.no_extras and cfg == 3:
         log("bench: tag-check overhead (interleaved on/off)")
+        step = lambda: st.step(check_tags=True)  # noqa: E731
         off = lambda: st.step(check_tags=False)  # noqa: E731
         deltas = []
         M = 10
@@ -300,22 +325,25 @@ def main():
                                      "ci95_pct": [round(100 * float(np.percentile(boots, 2.5)), 3),
                                                   round(100 * float(np.percentile(boots, 97.5)), 3)],
                                      "rounds": args.overhead_rounds, "steps_per_round": M}
-        del st
+        del st, states, steps_, vas, decs, step, verify_append, decode, verify_only
         torch.cuda.empty_cache()
         log("bench: uniform 32x8192, e4m3 vs bf16 cache")
         w2 = workloads.make(2)
         var = {}
         for cd, name in ((0, "e4m3"), (1, "bf16")):
-            s2 = device.build(w2, cache_dtype=cd)
-            for _ in range(5):
-                s2.step(True)
-            t2 = time_steps(lambda: s2.step(True), 50)
+            # two copies, alternated, as in the uniform workload's own line
+            c2 = [device.build(w2, cache_dtype=cd) for _ in range(2)]
+            st2 = cycle([lambda s=s: s.step(True) for s in c2])
+            for _ in range(10):
+                st2()
+            t2 = time_steps(st2, 100)
             b2, a2 = alg_bytes(w2, cd, True)
-            td2 = statistics.median(event_times([lambda: s2.decode(True)], 30)[0]) * 1e-3
+            td2 = statistics.median(
+                event_times([cycle([lambda s=s: s.decode(True) for s in c2])], 50)[0]) * 1e-3
             var[name] = {"ms_per_step": round(t2 * 1e3, 4), "tokens_s": round(w2.B / t2, 1),
                          "hbm_gbps": round(b2 / t2 / 1e9, 1),
                          "attn_gbps": round(a2 / td2 / 1e9, 1)}
-            del s2
+            del c2, st2
             torch.cuda.empty_cache()
         res["uniform_32x8192"] = var
     if not args.no_cpu_baseline and cfg == 3:

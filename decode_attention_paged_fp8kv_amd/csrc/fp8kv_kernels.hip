@@ -156,42 +156,50 @@ struct VerifyArgs {
   int32_t max_pages, num_pages, page_size;
 };
 
-__global__ __launch_bounds__(256) void verify_tags_kernel(VerifyArgs a) {
+// One workgroup per request; each thread takes kVerifyUnroll entries per round
+// and issues all of their loads (page ids and expected tags, then the current
+// tags) before comparing any, so a round costs two dependent load latencies.
+constexpr int kVerifyThreads = 512;
+constexpr int kVerifyUnroll = 4;
+
+// Entries i0 + u*kVerifyThreads (u < kVerifyUnroll) of a request's list of n:
+// nonzero if one of them names a page outside the pool or a stale tag.
+__device__ __forceinline__ int check_round(const VerifyArgs& a, const int32_t* pt,
+                                           const uint32_t* et, int n, int i0) {
+  int32_t id[kVerifyUnroll];
+  uint32_t ex[kVerifyUnroll], cur[kVerifyUnroll];
+#pragma unroll
+  for (int u = 0; u < kVerifyUnroll; ++u) {
+    const int i = i0 + u * kVerifyThreads;
+    id[u] = i < n ? pt[i] : 0;
+    ex[u] = i < n ? et[i] : 0;
+  }
+  int bad = 0;
+#pragma unroll
+  for (int u = 0; u < kVerifyUnroll; ++u) {
+    const int i = i0 + u * kVerifyThreads;
+    const bool valid = static_cast<unsigned>(id[u]) < static_cast<unsigned>(a.num_pages);
+    cur[u] = (i < n && valid) ? a.tags[id[u]] : 0u;
+    if (i < n && !valid) bad = 1;
+  }
+#pragma unroll
+  for (int u = 0; u < kVerifyUnroll; ++u) {
+    const int i = i0 + u * kVerifyThreads;
+    if (i < n && cur[u] != ex[u]) bad = 1;
+  }
+  return bad;
+}
+
+__global__ __launch_bounds__(kVerifyThreads) void verify_tags_kernel(VerifyArgs a) {
   const int b = blockIdx.x;
   const int ctx = a.ctx_lens[b];
-  int bad = 0;
-  if (ctx < 0) {
-    bad = 1;
-  } else {
-    const int n = (ctx + a.page_size - 1) / a.page_size;
-    if (n > a.max_pages) {
-      bad = 1;
-    } else {
-      const int32_t* pt = a.page_table + static_cast<int64_t>(b) * a.max_pages;
-      const uint32_t* et = a.expected + static_cast<int64_t>(b) * a.max_pages;
-      // four independent entries per thread per round keep loads in flight
-      for (int i0 = threadIdx.x; i0 < n; i0 += 4 * 256) {
-        int32_t id[4];
-        uint32_t ex[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + u * 256;
-          id[u] = i < n ? pt[i] : 0;
-          ex[u] = i < n ? et[i] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + u * 256;
-          if (i < n) {
-            if (static_cast<unsigned>(id[u]) >= static_cast<unsigned>(a.num_pages))
-              bad = 1;
-            else if (a.tags[id[u]] != ex[u])
-              bad = 1;
-          }
-        }
-      }
-    }
-  }
+  const int n = ctx < 0 ? 0 : (ctx + a.page_size - 1) / a.page_size;
+  int bad = (ctx < 0 || n > a.max_pages) ? 1 : 0;
+  const int nchk = bad ? 0 : n;
+  const int32_t* pt = a.page_table + static_cast<int64_t>(b) * a.max_pages;
+  const uint32_t* et = a.expected + static_cast<int64_t>(b) * a.max_pages;
+  for (int i0 = threadIdx.x; i0 < nchk; i0 += kVerifyUnroll * kVerifyThreads)
+    bad |= check_round(a, pt, et, nchk, i0);
   bad = __syncthreads_or(bad);
   if (threadIdx.x == 0) a.abort[b] = static_cast<uint8_t>(bad ? 1 : 0);
 }
@@ -312,8 +320,6 @@ struct VerifyAppendArgs {
 // with the append only removes a launch: a request's token is written after
 // (and only if) all of that request's pages passed.  The token is loaded and
 // encoded while the check's loads are in flight; only the stores wait.
-constexpr int kVerifyThreads = 512;
-constexpr int kVerifyUnroll = 4;
 
 template <int CACHE>
 __global__ __launch_bounds__(kVerifyThreads) void verify_append_kernel(VerifyAppendArgs a) {
@@ -367,24 +373,8 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_append_kernel(VerifyApp
     if (i < nchk && cur[u] != ex[u]) bad = 1;
   }
   for (int i0 = tid + kVerifyUnroll * kVerifyThreads; i0 < nchk;
-       i0 += kVerifyUnroll * kVerifyThreads) {
-#pragma unroll
-    for (int u = 0; u < kVerifyUnroll; ++u) {
-      const int i = i0 + u * kVerifyThreads;
-      id[u] = i < nchk ? pt[i] : 0;
-      ex[u] = i < nchk ? et[i] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < kVerifyUnroll; ++u) {
-      const int i = i0 + u * kVerifyThreads;
-      if (i < nchk) {
-        if (static_cast<unsigned>(id[u]) >= static_cast<unsigned>(a.v.num_pages))
-          bad = 1;
-        else if (a.v.tags[id[u]] != ex[u])
-          bad = 1;
-      }
-    }
-  }
+       i0 += kVerifyUnroll * kVerifyThreads)
+    bad |= check_round(a.v, pt, et, nchk, i0);
   bad = __syncthreads_or(bad);
   if (tid == 0) a.v.abort[b] = static_cast<uint8_t>(bad ? 1 : 0);
   if (bad || !mine || !pos_ok) return;
@@ -1127,7 +1117,7 @@ fp8kv_status fp8kv_verify_tags(const int32_t* d_page_table, const uint32_t* d_ex
     return FP8KV_INVALID_ARG;
   VerifyArgs a{d_page_table, d_expected_tags, d_ctx_lens, d_pool_tags, d_abort,
                max_pages_per_seq, num_pages, page_size};
-  hipLaunchKernelGGL(verify_tags_kernel, dim3(batch), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(verify_tags_kernel, dim3(batch), dim3(kVerifyThreads), 0, stream, a);
   return launched();
 }
 
