@@ -135,6 +135,69 @@ def capture_graphs(st, fns):
     return [g.replay for g in graphs]
 
 
+def loop_study(args):
+    """Multi-step decode with the tag tracker on vs the no-op tracker: prompts of
+    8,192 tokens, 1,000 generated tokens, concurrency 1/2/4/8, one layer of the
+    ragged workload's shape (64 q-heads / 8 kv-heads).  Runs of the two modes
+    alternate; each run restarts from the prompt.  A step's latency is its wall
+    time including the host work (page allocation, tag upload, launches) and the
+    read-back of the abort flags, synchronized at the end of every step."""
+    import numpy as np
+    import torch
+    from workloads.decode_loop import DecodeLoop
+
+    rng = np.random.default_rng(0)
+    per = {}
+    for nl, c in [(nl, c) for nl in args.loop_layers for c in args.loop_concurrency]:
+        log(f"bench: decode loop, {nl} layer(s), concurrency {c}")
+        loops = {m: DecodeLoop(c, args.loop_prompt, args.loop_steps, tracker=(m == "on"), seed=c,
+                               step_sets=16, layers=nl) for m in ("on", "off")}
+        for lp in loops.values():
+            lp.run(min(20, args.loop_steps))
+            lp.reset()
+        tot = {"on": [], "off": []}
+        lat = {"on": [], "off": []}
+        for r in range(args.loop_rounds):
+            for m in (("on", "off") if r % 2 == 0 else ("off", "on")):
+                x = loops[m].run()
+                loops[m].reset()
+                tot[m].append(float(x.sum()))
+                lat[m].append(x)
+        d = np.array([(a - b) / b for a, b in zip(tot["on"], tot["off"])])
+        boots = [rng.choice(d, d.size).mean() for _ in range(2000)]
+        res = {}
+        for m in ("on", "off"):
+            allx = np.concatenate(lat[m])
+            res[m] = {"tokens_s": round(c * args.loop_steps / float(np.median(tot[m])), 1),
+                      "step_ms_p50": round(float(np.percentile(allx, 50)) * 1e3, 4),
+                      "step_ms_p95": round(float(np.percentile(allx, 95)) * 1e3, 4)}
+        res["overhead_pct"] = {"mean": round(100 * float(d.mean()), 3),
+                               "ci95": [round(100 * float(np.percentile(boots, 2.5)), 3),
+                                        round(100 * float(np.percentile(boots, 97.5)), 3)]}
+        res["overhead_us_per_step"] = round(
+            1e6 * (float(np.median(tot["on"])) - float(np.median(tot["off"]))) / args.loop_steps, 2)
+        res["p95_overhead_pct"] = round(
+            100 * (res["on"]["step_ms_p95"] / res["off"]["step_ms_p95"] - 1), 3)
+        per.setdefault(f"{nl}_layers", {})[str(c)] = res
+        for lp in loops.values():
+            lp.close()
+        del loops
+        torch.cuda.empty_cache()
+    top = per[f"{args.loop_layers[0]}_layers"][str(max(args.loop_concurrency))]
+    print(json.dumps({
+        "metric": "decode loop (8192-token prompts, 1000 generated tokens): tokens/s and p95 "
+                  "step latency, tag tracker on vs the no-op tracker",
+        "value": top["on"]["tokens_s"], "unit": "tokens/s", "n_gpus": 1,
+        "higher_is_better": True, "data": "synthetic",
+        "config": {"workload": "decode_loop", "prompt_tokens": args.loop_prompt,
+                   "generated_tokens": args.loop_steps, "q_heads": 64, "kv_heads": 8,
+                   "head_dim": 128, "page_tokens": 16, "kv_cache": "e4m3",
+                   "rounds": args.loop_rounds, "layers": args.loop_layers},
+        "value_is": f"tracker on, {args.loop_layers[0]} layer(s), concurrency "
+                    f"{max(args.loop_concurrency)}",
+        "by_layers_and_concurrency": per}), flush=True)
+
+
 def cpu_baseline(w, target_s: float = 15.0):
     """The oracle as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -211,6 +274,14 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a captured HIP graph of the step (no host launch "
                          "cost; for workloads whose GPU time is below the binding's)")
+    ap.add_argument("--loop", action="store_true",
+                    help="run the multi-step decode study (tracker on vs off) instead")
+    ap.add_argument("--loop-concurrency", type=int, nargs="+", default=[1, 2, 4, 8])
+    ap.add_argument("--loop-prompt", type=int, default=8192)
+    ap.add_argument("--loop-steps", type=int, default=1000)
+    ap.add_argument("--loop-rounds", type=int, default=6)
+    ap.add_argument("--loop-layers", type=int, nargs="+", default=[1, 32],
+                    help="layers per model step (one tag check per step, attention per layer)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus "
@@ -225,6 +296,9 @@ def main():
     from workloads import device
 
     torch.cuda.set_device(0)
+    if args.loop:
+        loop_study(args)
+        return
     if args.calibrate_copy:
         n = 1 << 30
         x = torch.ones(n, dtype=torch.uint8, device="cuda")

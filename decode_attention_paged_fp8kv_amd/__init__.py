@@ -200,52 +200,84 @@ class Pool:
 # ---------------------------------------------------------------------------
 # hot path
 # ---------------------------------------------------------------------------
-def verify_tags(page_table, expected_tags, ctx_lens, pool_tags, abort=None, stream=None):
-    """Batched page-tag check; returns the uint8 abort tensor [B]."""
+class Launch:
+    """One entry point with its arguments checked and marshalled once: calling
+    it calls the C function again with the same pointers and sizes (nothing is
+    checked or allocated).  It holds the tensors it points into, which must keep
+    their storage; their contents may change between calls.  Made by the hot-path
+    functions below with prepare=True, for loops whose per-call host time
+    matters."""
+    __slots__ = ("_fn", "_args", "_what", "_result", "_keep")
+
+    def __init__(self, fn, args, what, result, keep):
+        self._fn, self._args, self._what, self._result, self._keep = fn, args, what, result, keep
+
+    def __call__(self):
+        _check(self._fn(*self._args), self._what)
+        return self._result
+
+
+def _run(fn, args, what, result, keep, prepare):
+    if prepare:
+        return Launch(fn, tuple(args), what, result, keep)
+    _check(fn(*args), what)
+    return result
+
+
+def verify_tags(page_table, expected_tags, ctx_lens, pool_tags, abort=None, stream=None,
+                prepare: bool = False):
+    """Batched page-tag check; returns the uint8 abort tensor [B] (or, with
+    prepare=True, a Launch that runs the check and returns it)."""
     B = ctx_lens.shape[0]
     if abort is None:
         abort = torch.empty(B, dtype=torch.uint8, device=ctx_lens.device)
     P = page_table.shape[1] if page_table.dim() == 2 else 0
-    _check(_verify(_dev(page_table, _I32, "page_table"), _dev(expected_tags, _U32, "expected_tags"),
-                   P, _dev(ctx_lens, _I32, "ctx_lens"), B, _dev(pool_tags, _U32, "pool_tags"),
-                   pool_tags.shape[0], PAGE_SIZE, _dev(abort, _U8, "abort"), _stream(stream)),
-           "verify_tags")
-    return abort
+    args = (_dev(page_table, _I32, "page_table"), _dev(expected_tags, _U32, "expected_tags"),
+            P, _dev(ctx_lens, _I32, "ctx_lens"), B, _dev(pool_tags, _U32, "pool_tags"),
+            pool_tags.shape[0], PAGE_SIZE, _dev(abort, _U8, "abort"), _stream(stream))
+    return _run(_verify, args, "verify_tags", abort,
+                (page_table, expected_tags, ctx_lens, pool_tags, abort), prepare)
 
 
 def append(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, k_new, v_new, token_seq, token_pos,
-           page_table, abort=None, stream=None):
+           page_table, abort=None, stream=None, prepare: bool = False):
     """Quantize-on-append of num_tokens new K/V rows ([T][Hkv][128] BF16)."""
     T = token_seq.shape[0]
     fp8 = d.cache_dtype == E4M3
-    _check(_append(ctypes.byref(d), _dev(k_cache, _U8 + _BITS16, "k_cache"),
-                   _dev(v_cache, _U8 + _BITS16, "v_cache"),
-                   _dev(k_scale, _F32, "k_scale", allow_none=not fp8),
-                   _dev(v_scale, _F32, "v_scale", allow_none=not fp8),
-                   _dev(k_new, _BITS16, "k_new"), _dev(v_new, _BITS16, "v_new"), T,
-                   _dev(token_seq, _I32, "token_seq"), _dev(token_pos, _I32, "token_pos"),
-                   page_table.shape[0], _dev(page_table, _I32, "page_table"), page_table.shape[1],
-                   _dev(abort, _U8, "abort", allow_none=True), _stream(stream)), "append")
+    args = (ctypes.byref(d), _dev(k_cache, _U8 + _BITS16, "k_cache"),
+            _dev(v_cache, _U8 + _BITS16, "v_cache"),
+            _dev(k_scale, _F32, "k_scale", allow_none=not fp8),
+            _dev(v_scale, _F32, "v_scale", allow_none=not fp8),
+            _dev(k_new, _BITS16, "k_new"), _dev(v_new, _BITS16, "v_new"), T,
+            _dev(token_seq, _I32, "token_seq"), _dev(token_pos, _I32, "token_pos"),
+            page_table.shape[0], _dev(page_table, _I32, "page_table"), page_table.shape[1],
+            _dev(abort, _U8, "abort", allow_none=True), _stream(stream))
+    return _run(_append, args, "append", None,
+                (d, k_cache, v_cache, k_scale, v_scale, k_new, v_new, token_seq, token_pos,
+                 page_table, abort), prepare)
 
 
 def verify_append(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, k_new, v_new, new_pos,
-                  page_table, expected_tags, ctx_lens, pool_tags, abort=None, stream=None):
+                  page_table, expected_tags, ctx_lens, pool_tags, abort=None, stream=None,
+                  prepare: bool = False):
     """Tag check + the step's append in one launch (one new token per request);
     returns the uint8 abort tensor [B]."""
     B = ctx_lens.shape[0]
     if abort is None:
         abort = torch.empty(B, dtype=torch.uint8, device=ctx_lens.device)
     fp8 = d.cache_dtype == E4M3
-    _check(_verify_append(ctypes.byref(d), _dev(k_cache, _U8 + _BITS16, "k_cache"),
-                          _dev(v_cache, _U8 + _BITS16, "v_cache"),
-                          _dev(k_scale, _F32, "k_scale", allow_none=not fp8),
-                          _dev(v_scale, _F32, "v_scale", allow_none=not fp8),
-                          _dev(k_new, _BITS16, "k_new"), _dev(v_new, _BITS16, "v_new"),
-                          _dev(new_pos, _I32, "new_pos"), _dev(page_table, _I32, "page_table"),
-                          _dev(expected_tags, _U32, "expected_tags"), page_table.shape[1],
-                          _dev(ctx_lens, _I32, "ctx_lens"), B, _dev(pool_tags, _U32, "pool_tags"),
-                          _dev(abort, _U8, "abort"), _stream(stream)), "verify_append")
-    return abort
+    args = (ctypes.byref(d), _dev(k_cache, _U8 + _BITS16, "k_cache"),
+            _dev(v_cache, _U8 + _BITS16, "v_cache"),
+            _dev(k_scale, _F32, "k_scale", allow_none=not fp8),
+            _dev(v_scale, _F32, "v_scale", allow_none=not fp8),
+            _dev(k_new, _BITS16, "k_new"), _dev(v_new, _BITS16, "v_new"),
+            _dev(new_pos, _I32, "new_pos"), _dev(page_table, _I32, "page_table"),
+            _dev(expected_tags, _U32, "expected_tags"), page_table.shape[1],
+            _dev(ctx_lens, _I32, "ctx_lens"), B, _dev(pool_tags, _U32, "pool_tags"),
+            _dev(abort, _U8, "abort"), _stream(stream))
+    return _run(_verify_append, args, "verify_append", abort,
+                (d, k_cache, v_cache, k_scale, v_scale, k_new, v_new, new_pos, page_table,
+                 expected_tags, ctx_lens, pool_tags, abort), prepare)
 
 
 def decode_num_workers(requested: int = 0) -> int:
@@ -259,7 +291,7 @@ def decode_workspace_size(d: CacheDesc, batch: int, num_q_heads: int, num_worker
 def decode_attention(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, page_table, ctx_lens,
                      abort=None, out=None, out_dtype: int = OUT_BF16,
                      sm_scale: Optional[float] = None, num_workers: int = 0, workspace=None,
-                     stream=None):
+                     stream=None, prepare: bool = False):
     """Paged decode attention; returns out [B][Hq][128] (bf16 or f32)."""
     B, Hq, D = q.shape
     if sm_scale is None:
@@ -271,17 +303,19 @@ def decode_attention(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, page_t
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     fp8 = d.cache_dtype == E4M3
-    _check(_decode(ctypes.byref(d), _dev(k_cache, _U8 + _BITS16, "k_cache"),
-                   _dev(v_cache, _U8 + _BITS16, "v_cache"),
-                   _dev(k_scale, _F32, "k_scale", allow_none=not fp8),
-                   _dev(v_scale, _F32, "v_scale", allow_none=not fp8),
-                   _dev(q, _BITS16, "q"), Hq, _dev(page_table, _I32, "page_table"),
-                   page_table.shape[1], _dev(ctx_lens, _I32, "ctx_lens"), B,
-                   float(sm_scale), _dev(abort, _U8, "abort", allow_none=True),
-                   _dev(out, (torch.bfloat16, torch.int16, torch.float32), "out"), out_dtype,
-                   num_workers, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                   _stream(stream)), "decode_attention")
-    return out
+    args = (ctypes.byref(d), _dev(k_cache, _U8 + _BITS16, "k_cache"),
+            _dev(v_cache, _U8 + _BITS16, "v_cache"),
+            _dev(k_scale, _F32, "k_scale", allow_none=not fp8),
+            _dev(v_scale, _F32, "v_scale", allow_none=not fp8),
+            _dev(q, _BITS16, "q"), Hq, _dev(page_table, _I32, "page_table"),
+            page_table.shape[1], _dev(ctx_lens, _I32, "ctx_lens"), B,
+            float(sm_scale), _dev(abort, _U8, "abort", allow_none=True),
+            _dev(out, (torch.bfloat16, torch.int16, torch.float32), "out"), out_dtype,
+            num_workers, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    return _run(_decode, args, "decode_attention", out,
+                (d, k_cache, v_cache, k_scale, v_scale, q, page_table, ctx_lens, abort, out,
+                 workspace), prepare)
 
 
 def debug_convert_e4m3(codes: torch.Tensor, which: int, stream=None) -> torch.Tensor:

@@ -231,14 +231,13 @@ struct Chunk4 {
   u32x2_t k, v;  // e4m3: k.x / v.x hold 4 codes; bf16: the raw 8 bytes
 };
 
+// ks, vs: the kv-head's scales (unused for a bf16 cache)
 template <int CACHE>
-__device__ __forceinline__ Chunk4 append_encode4(const AppendArgs& a, int h, u32x2_t k,
-                                                 u32x2_t v) {
+__device__ __forceinline__ Chunk4 append_encode4(u32x2_t k, u32x2_t v, float ks, float vs) {
   Chunk4 r;
   r.k = k;
   r.v = v;
   if constexpr (CACHE == FP8KV_E4M3) {
-    const float ks = a.k_scale[h], vs = a.v_scale[h];
     unsigned kq = 0u, vq = 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -285,7 +284,10 @@ __device__ __forceinline__ void append_store4(const AppendArgs& a, const Chunk4&
   }
 }
 
-// One thread per (token, kv-head, 4-dim chunk).
+// One thread per (token, kv-head, 4-dim chunk).  The new values and the
+// token's request and position are loaded together, then the request's abort
+// flag and page id together; the encode runs while those are in flight, so a
+// thread waits for two load latencies before its store.
 template <int CACHE>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int64_t item = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -294,17 +296,30 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int64_t th = item >> 5;
   const int h = static_cast<int>(th % a.Hkv);
   const int64_t tok = th / a.Hkv;
-  const int seq = a.token_seq[tok];
-  const int pos = a.token_pos[tok];
-  if (seq < 0 || seq >= a.num_seqs) return;
-  if (a.abort && a.abort[seq]) return;
-  if (pos < 0 || pos / kPage >= a.max_pages) return;
-  const int32_t pid = a.page_table[static_cast<int64_t>(seq) * a.max_pages + pos / kPage];
-  if (static_cast<unsigned>(pid) >= static_cast<unsigned>(a.num_pages)) return;
   const int64_t src = (tok * a.Hkv + h) * kHeadDim + 4 * c;
+  // level 1: everything indexed by the item alone
   const u32x2_t kin = *reinterpret_cast<const u32x2_t*>(a.k_new + src);
   const u32x2_t vin = *reinterpret_cast<const u32x2_t*>(a.v_new + src);
-  append_store4<CACHE>(a, append_encode4<CACHE>(a, h, kin, vin), h, c, pid, pos % kPage);
+  const int seq = a.token_seq[tok];
+  const int pos = a.token_pos[tok];
+  float ks = 1.0f, vs = 1.0f;
+  if constexpr (CACHE == FP8KV_E4M3) {
+    ks = a.k_scale[h];
+    vs = a.v_scale[h];
+  }
+  // level 2: indexed by the request (clamped, so the loads need no branch)
+  const bool ok = seq >= 0 && seq < a.num_seqs && pos >= 0 && pos / kPage < a.max_pages;
+  const int sq = ok ? seq : 0;
+  const int pg = ok ? pos / kPage : 0;
+  const int32_t pid = a.page_table[static_cast<int64_t>(sq) * a.max_pages + pg];
+  // without an abort array the load reads a byte of the token's request id
+  // (valid memory) and the value is ignored: no branch around the load
+  const uint8_t flag =
+      *(a.abort ? a.abort + sq : reinterpret_cast<const uint8_t*>(a.token_seq + tok));
+  const bool aborted = a.abort != nullptr && flag != 0;
+  const Chunk4 r = append_encode4<CACHE>(kin, vin, ks, vs);
+  if (!ok || aborted || static_cast<unsigned>(pid) >= static_cast<unsigned>(a.num_pages)) return;
+  append_store4<CACHE>(a, r, h, c, pid, pos % kPage);
 }
 
 // ---------------------------------------------------------------------------
@@ -365,7 +380,9 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_append_kernel(VerifyApp
   }
   // 4. encode while the tag loads are in flight
   Chunk4 prep;
-  if (mine && pos_ok) prep = append_encode4<CACHE>(a.w, h, kin, vin);
+  if (mine && pos_ok)
+    prep = append_encode4<CACHE>(kin, vin, CACHE == FP8KV_E4M3 ? a.w.k_scale[h] : 1.0f,
+                                 CACHE == FP8KV_E4M3 ? a.w.v_scale[h] : 1.0f);
   // 5. compare; requests longer than one round continue in a loop
 #pragma unroll
   for (int u = 0; u < kVerifyUnroll; ++u) {
@@ -441,12 +458,16 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 __device__ __forceinline__ int live_pages(const DecodeArgs& a, int b) {
+  // the flag is loaded next to the length (without an abort array, from a
+  // byte of the length itself, and ignored), not after it
   const int ctx = a.ctx_lens[b];
-  if (ctx <= 0) return 0;
-  const int n = (ctx + kPage - 1) / kPage;
-  if (n > a.max_pages) return 0;                        // does not fit the table: fail closed
-  if (a.abort != nullptr && a.abort[b] != 0) return 0;  // aborted: +0 rows, nothing read
-  return n;
+  const uint8_t flag =
+      *(a.abort ? a.abort + b : reinterpret_cast<const uint8_t*>(a.ctx_lens + b));
+  const int n = ctx > 0 ? (ctx + kPage - 1) / kPage : 0;
+  // nothing read for: no context, a length that does not fit the table (fail
+  // closed), an aborted request (+0 rows)
+  const bool none = n == 0 || n > a.max_pages || (a.abort != nullptr && flag != 0);
+  return none ? 0 : n;
 }
 
 __device__ __forceinline__ void store_out8(const DecodeArgs& a, int64_t idx, const float* v) {
@@ -910,66 +931,88 @@ void decode_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // 5. merge of the pieces of split segments (fixed order: deterministic)
 // ---------------------------------------------------------------------------
-// Workgroups stride over (request, kv-head) segments; threads take (head, 4
-// dims).  A separate pass: ordering the partial writes of other workgroups
-// inside the decode kernel would need a device-scope release/acquire per
-// piece, which on this part writes back and invalidates the L2 and costs far
-// more than this launch.
+// Workgroups stride over (request, kv-head) segments.  A thread takes one
+// (head, 4 dims) pair and one group of consecutive pieces; the groups' states
+// are then merged through LDS in group order, so a segment cut into many
+// pieces (few long requests) costs a few rounds of loads, not one per piece.
+// A separate pass: ordering the partial writes of other workgroups inside the
+// decode kernel would need a device-scope release/acquire per piece, which on
+// this part writes back and invalidates the L2 and costs far more than this
+// launch.
 constexpr int kMergeUnroll = 8;
-constexpr int kMergeThreads = 256;
+constexpr int kMergeThreads = 1024;
+
+// fold one piece's (max, sum, weighted V) into a running state
+__device__ __forceinline__ void merge_state(float& M, float& L, f32x4_t& O, float m, float l,
+                                            f32x4_t o) {
+  if (m == -INFINITY) return;
+  if (m > M) {
+    const float r = (M == -INFINITY) ? 0.f : fast_exp2(M - m);
+    L *= r;
+    O *= r;
+    M = m;
+  }
+  const float e = fast_exp2(m - M);
+  L += e * l;
+  O += e * o;
+}
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int64_t grid) {
+  __shared__ float s_m[kMergeThreads];
+  __shared__ float s_l[kMergeThreads];
+  __shared__ f32x4_t s_o[kMergeThreads];
   const int64_t W = static_cast<int64_t>(a.Hkv) * a.ws_pre[a.batch];
   const int64_t NWG = slice_count(W, grid);
+  const int items = a.G * (kHeadDim / 4);        // (head, 4 dims) pairs, at most 512
+  const int groups = kMergeThreads / items;      // at least 2
+  const int t = threadIdx.x;
+  const bool active = t < items * groups;
+  const int idx = t % items, grp = t / items;
+  const int n = idx / (kHeadDim / 4);
+  const int d = 4 * (idx % (kHeadDim / 4));
   for (int seg = blockIdx.x; seg < a.batch * a.Hkv; seg += gridDim.x) {
     const int b = seg / a.Hkv;
     const int g = seg % a.Hkv;
     const int pre_b = a.ws_pre[b];
     const int np = a.ws_pre[b + 1] - pre_b;
-    if (np == 0) continue;
+    if (np == 0) continue;  // uniform over the workgroup, like the test below
     const int64_t first = static_cast<int64_t>(a.Hkv) * pre_b + static_cast<int64_t>(g) * np;
-    const int64_t last = first + np - 1;
     int64_t wf, wl;
-    segment_workgroups(first, last, W, NWG, wf, wl);
+    segment_workgroups(first, first + np - 1, W, NWG, wf, wl);
     if (wf == wl) continue;  // one piece: written by the decode kernel
-    const float vsc = a.v_scale ? a.v_scale[g] : 1.0f;
-    for (int idx = threadIdx.x; idx < a.G * (kHeadDim / 4); idx += kMergeThreads) {
-      const int n = idx / (kHeadDim / 4);
-      const int d = 4 * (idx % (kHeadDim / 4));
-      float M = -INFINITY, L = 0.f;
-      f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-      // pieces in workgroup order: from the workgroup holding item x, jump to
-      // the start of the next slice, so workgroups with empty slices (more
-      // workgroups than pages) are never visited
-      for (int64_t x = first; x <= last;) {
+    // every workgroup in [wf, wl] holds a piece: with at least one page per
+    // workgroup no slice is empty
+    const int64_t chunk = (wl - wf + groups) / groups;
+    const int64_t w0 = wf + grp * chunk;
+    const int64_t w1 = (w0 + chunk < wl + 1) ? w0 + chunk : wl + 1;
+    float M = -INFINITY, L = 0.f;
+    f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+    if (active) {
+      for (int64_t w = w0; w < w1; w += kMergeUnroll) {
         // issue the loads of several pieces before using any of them
         float m[kMergeUnroll], l[kMergeUnroll];
         f32x4_t o[kMergeUnroll];
 #pragma unroll
         for (int u = 0; u < kMergeUnroll; ++u) {
-          const bool has = x <= last;
-          const int64_t w = ((x + 1) * NWG - 1) / W;
-          if (has) x = (w + 1) * W / NWG;
-          const int64_t pidx = (w + seg) * a.G + n;
+          const bool has = w + u < w1;
+          const int64_t pidx = (w + u + seg) * a.G + n;
           m[u] = has ? a.ws_ml[pidx * 2] : -INFINITY;
           l[u] = has ? a.ws_ml[pidx * 2 + 1] : 0.f;
           o[u] = has ? *reinterpret_cast<const f32x4_t*>(a.ws_o + pidx * kHeadDim + d)
                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) {
-          if (m[u] == -INFINITY) continue;
-          if (m[u] > M) {
-            const float r = (M == -INFINITY) ? 0.f : fast_exp2(M - m[u]);
-            L *= r;
-            O *= r;
-            M = m[u];
-          }
-          const float e = fast_exp2(m[u] - M);
-          L += e * l[u];
-          O += e * o[u];
-        }
+        for (int u = 0; u < kMergeUnroll; ++u) merge_state(M, L, O, m[u], l[u], o[u]);
       }
+    }
+    s_m[t] = M;
+    s_l[t] = L;
+    s_o[t] = O;
+    __syncthreads();
+    if (active && grp == 0) {
+      for (int k = 1; k < groups; ++k)
+        merge_state(M, L, O, s_m[k * items + idx], s_l[k * items + idx], s_o[k * items + idx]);
+      const float vsc = a.v_scale ? a.v_scale[g] : 1.0f;
       const float inv = L > 0.f ? vsc / L : 0.f;
       const int64_t io = (static_cast<int64_t>(b) * a.Hq + g * a.G + n) * kHeadDim + d;
       if (a.out_f32) {
@@ -983,6 +1026,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int6
         *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + io) = w;
       }
     }
+    __syncthreads();  // LDS is reused for the next segment
   }
 }
 

@@ -127,3 +127,17 @@ def test_workspace_size_grows_with_workers_and_batch():
     assert s1 >= slots * G * 130 * 4 + 65 * 4
     assert fp8kv.decode_num_workers(10) == 12
     assert fp8kv.decode_workspace_size(fp8kv.desc(100, 8), 4, 60, 64) == 0  # Hq % Hkv != 0
+
+
+def test_prepared_launch_checks_once_and_keeps_its_tensors():
+    import torch
+    # arguments are checked when the launch is prepared, before any device call
+    cpu = torch.zeros(4, dtype=torch.int32)
+    try:
+        fp8kv.verify_tags(cpu.view(1, 4), cpu.view(1, 4), cpu[:1], cpu, prepare=True)
+    except ValueError as e:
+        assert "device tensor" in str(e)
+    else:
+        raise AssertionError("a host tensor was accepted")
+    # a prepared launch holds the tensors its pointers refer to
+    assert "_keep" in fp8kv.Launch.__slots__

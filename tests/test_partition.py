@@ -3,8 +3,8 @@
 The persistent decode gives wave w of NW the items [w*W/NW, (w+1)*W/NW) of
 the (request, kv-head, page) list; a piece that is not a whole segment goes to
 slot w + segment, and the merge pass collects, for each segment, the slots of
-the non-empty waves between the waves holding its first and last item (found by
-jumping from slice to slice, so empty slices cost nothing).  This
+the waves between the waves holding its first and last item (none of them has
+an empty slice).  This
 checks, in integers, that every slot is written once and that each segment's
 pieces tile its pages exactly -- for empty requests, more waves than pages and
 fewer waves than segments alike.  Slices hold at least 4 pages: with less work
@@ -55,16 +55,10 @@ def _check(pages, Hkv, grid):
             if wf == wl:
                 assert all(v[0] != seg for v in slots.values())
                 continue
-            nonempty = [w for w in range(wf, wl + 1) if w * W // NW != (w + 1) * W // NW]
-            # the merge pass enumerates them by jumping from the workgroup holding
-            # item x to the start of the next slice (empty slices never visited)
-            jumped, x = [], first
-            while x <= last:
-                w = ((x + 1) * NW - 1) // W
-                jumped.append(w)
-                x = (w + 1) * W // NW
-            assert jumped == nonempty
-            got = [slots[w + seg] for w in nonempty]
+            # the merge pass reads every workgroup between them: with at least one
+            # page per workgroup no slice is empty
+            assert all(w * W // NW != (w + 1) * W // NW for w in range(wf, wl + 1))
+            got = [slots[w + seg] for w in range(wf, wl + 1)]
             assert all(p[0] == seg for p in got)
             cov = sorted((p[1], p[2]) for p in got)
             assert cov[0][0] == first and cov[-1][1] == last + 1

@@ -71,3 +71,16 @@ def test_head_slice_generator_matches():
         full = w.kv_tokens("v", 1, max(0, L - 40), L + 1)
         for g in range(w.Hkv):
             assert (w.kv_tokens_head("v", 1, max(0, L - 40), L + 1, g) == full[:, g, :]).all()
+
+
+def test_loop_token_streams_slice_and_backends_agree():
+    import torch
+    from workloads.decode_loop import token_bits
+    full = token_bits(3, "k", 2, 0, 40, 4)
+    part = token_bits(3, "k", 2, 17, 29, 4)
+    assert full.shape == (40, 4, 128) and (full[17:29] == part).all()
+    dev = token_bits(3, "k", 2, 17, 29, 4, "torch", "cpu")
+    assert (dev.numpy().view(np.uint16) == part).all()
+    # requests and tensors draw different streams
+    assert not (token_bits(3, "k", 1, 0, 4, 4) == full[:4]).all()
+    assert not (token_bits(3, "v", 2, 0, 4, 4) == full[:4]).all()
