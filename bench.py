@@ -198,6 +198,58 @@ def loop_study(args):
         "by_layers_and_concurrency": per}), flush=True)
 
 
+def accuracy_study(args):
+    """FP8 cache vs BF16 cache on the same inputs through the same kernel (f32
+    outputs): the difference is the error the e4m3 storage adds, since the
+    BF16-cache output agrees with binary64 attention to ~1e-6 (parity tests).
+    Uniform, ragged and long-context workloads (the last with ±20 outliers,
+    so scale = 20/448, and ±25 values on the new token that saturate)."""
+    import numpy as np
+    import torch
+
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    import workloads
+    from workloads import device
+
+    res = {}
+    for cfg in args.accuracy_configs:
+        w = workloads.make(cfg)
+        log(f"bench: accuracy, workload {w.name}")
+        outs = {}
+        for cd in (fp8kv.E4M3, fp8kv.BF16):
+            st = device.build(w, cache_dtype=cd)
+            st.step(check_tags=True)
+            outs[cd] = st.decode(True, out_dtype=fp8kv.OUT_F32).double()
+            torch.cuda.synchronize()
+            del st
+            torch.cuda.empty_cache()
+        def metrics(ref, got):
+            err = got - ref
+            cos = torch.nn.functional.cosine_similarity(got.reshape(-1, got.shape[-1]),
+                                                        ref.reshape(-1, ref.shape[-1]), dim=1)
+            return {"max_abs_err": float(err.abs().max()),
+                    "mean_abs_err": float(err.abs().mean()),
+                    "rel_l2_err": float(err.norm() / ref.norm()),
+                    "min_cosine": float(cos.min()),
+                    "output_rms": float(ref.pow(2).mean().sqrt()),
+                    "output_max_abs": float(ref.abs().max())}
+        ref, got = outs[fp8kv.BF16], outs[fp8kv.E4M3]
+        res[w.name] = metrics(ref, got)
+        # kv-head 0 carries the long workload's saturating values on the new token;
+        # the other kv-heads' q-heads show the error of in-range values alone
+        res[w.name]["kv_head_0"] = metrics(ref[:, :w.G], got[:, :w.G])
+        res[w.name]["other_kv_heads"] = metrics(ref[:, w.G:], got[:, w.G:])
+        del outs, ref, got
+        torch.cuda.empty_cache()
+    print(json.dumps({
+        "metric": "FP8 e4m3 cache vs BF16 cache: attention output error (same inputs, same "
+                  "kernel, f32 outputs)",
+        "value": max(r["rel_l2_err"] for r in res.values()), "unit": "relative L2 error (max over "
+                 "workloads)", "n_gpus": 1, "higher_is_better": False, "data": "synthetic",
+        "config": {"workload": "accuracy", "workloads": list(res)},
+        "by_workload": res}), flush=True)
+
+
 def cpu_baseline(w, target_s: float = 15.0):
     """The oracle as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -274,6 +326,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a captured HIP graph of the step (no host launch "
                          "cost; for workloads whose GPU time is below the binding's)")
+    ap.add_argument("--accuracy", action="store_true",
+                    help="measure the FP8 cache's output error against the BF16 cache instead")
+    ap.add_argument("--accuracy-configs", type=int, nargs="+", default=[2, 3, 4])
     ap.add_argument("--loop", action="store_true",
                     help="run the multi-step decode study (tracker on vs off) instead")
     ap.add_argument("--loop-concurrency", type=int, nargs="+", default=[1, 2, 4, 8])
@@ -298,6 +353,9 @@ def main():
     torch.cuda.set_device(0)
     if args.loop:
         loop_study(args)
+        return
+    if args.accuracy:
+        accuracy_study(args)
         return
     if args.calibrate_copy:
         n = 1 << 30
