@@ -62,6 +62,8 @@ _pool_create = _sig("fp8kv_pool_create", _i32, [_i32, ctypes.c_uint64, ctypes.PO
 _pool_destroy = _sig("fp8kv_pool_destroy", None, [_p])
 _pool_alloc = _sig("fp8kv_pool_alloc", _i32, [_p, _i32, _p, _p])
 _pool_free = _sig("fp8kv_pool_free", _i32, [_p, _i32, _p])
+_pool_share = _sig("fp8kv_pool_share", _i32, [_p, _i32, _p])
+_pool_refcount = _sig("fp8kv_pool_refcount", _i32, [_p, _i32])
 _pool_tag = _sig("fp8kv_pool_tag", ctypes.c_uint32, [_p, _i32])
 _pool_num_free = _sig("fp8kv_pool_num_free", _i32, [_p])
 _pool_read_tags = _sig("fp8kv_pool_read_tags", _i32, [_p, _p])
@@ -178,6 +180,17 @@ class Pool:
         import numpy as np
         a = np.ascontiguousarray(ids, np.int32)
         _check(_pool_free(self._h, a.size, a.ctypes.data), "pool_free")
+
+    def share(self, ids):
+        """Add one holder to each page (a request mapping a shared prefix); returns
+        the pages' current tags, which the new holder records."""
+        import numpy as np
+        a = np.ascontiguousarray(ids, np.int32)
+        _check(_pool_share(self._h, a.size, a.ctypes.data), "pool_share")
+        return np.array([_pool_tag(self._h, int(i)) for i in a], np.uint32)
+
+    def refcount(self, page_id: int) -> int:
+        return int(_pool_refcount(self._h, page_id))
 
     def tag(self, page_id: int) -> int:
         return int(_pool_tag(self._h, page_id))

@@ -8,6 +8,11 @@
 // random at creation, +1 (mod 2^32) on every allocation; freed pages are
 // reused first-in first-out so a stale mapping lives as long as possible
 // before its page is reissued (and then it is caught by the tag).
+//
+// Pages can be shared (a common prefix mapped by several requests, the cache
+// reuse the same pages warn widens the reach of a bad mapping): every holder
+// records the same tag; a page goes back to the free list when its last
+// holder releases it, and only its next allocation changes the tag.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -21,7 +26,8 @@
 struct fp8kv_pool {
   int32_t n = 0;
   std::vector<uint32_t> tags;
-  std::vector<uint8_t> live;
+  std::vector<int32_t> refs;   // holders of the page (0: free)
+  std::vector<uint8_t> seen;   // scratch of one call: duplicate ids
   std::vector<int32_t> ring;  // free ids, FIFO
   int64_t head = 0;           // index of the oldest free id
   int64_t count = 0;          // free ids in the ring
@@ -64,7 +70,8 @@ fp8kv_status fp8kv_pool_create(int32_t num_pages, uint64_t seed, fp8kv_pool** ou
   if (!p) return FP8KV_INVALID_ARG;
   p->n = num_pages;
   p->tags.resize(num_pages);
-  p->live.assign(num_pages, 0);
+  p->refs.assign(num_pages, 0);
+  p->seen.assign(num_pages, 0);
   p->ring.resize(num_pages);
   uint64_t s = seed;
   for (int32_t i = 0; i < num_pages; ++i) {
@@ -97,7 +104,7 @@ fp8kv_status fp8kv_pool_alloc(fp8kv_pool* p, int32_t n, int32_t* ids, uint32_t* 
     p->head = (p->head + 1) % p->n;
     --p->count;
     p->tags[id] += 1u;  // a new lifetime of this page
-    p->live[id] = 1;
+    p->refs[id] = 1;
     mark_dirty(p, id);
     ids[k] = id;
     tags[k] = p->tags[id];
@@ -105,24 +112,50 @@ fp8kv_status fp8kv_pool_alloc(fp8kv_pool* p, int32_t n, int32_t* ids, uint32_t* 
   return FP8KV_OK;
 }
 
+namespace {
+
+// Every id in range, currently held, listed once (and, when adding a holder,
+// not at the counter's limit); on failure nothing is marked.
+bool valid_held_list(fp8kv_pool* p, int32_t n, const int32_t* ids, bool adding) {
+  bool ok = true;
+  int32_t k = 0;
+  for (; k < n; ++k) {
+    const int32_t id = ids[k];
+    if (id < 0 || id >= p->n || p->refs[id] <= 0 || p->seen[id] ||
+        (adding && p->refs[id] == INT32_MAX)) {
+      ok = false;
+      break;
+    }
+    p->seen[id] = 1;
+  }
+  for (int32_t j = 0; j < k; ++j) p->seen[ids[j]] = 0;
+  return ok;
+}
+
+}  // namespace
+
+fp8kv_status fp8kv_pool_share(fp8kv_pool* p, int32_t n, const int32_t* ids) {
+  if (!p || n < 0 || (n > 0 && !ids)) return FP8KV_INVALID_ARG;
+  if (!valid_held_list(p, n, ids, true)) return FP8KV_INVALID_ARG;
+  for (int32_t k = 0; k < n; ++k) ++p->refs[ids[k]];
+  return FP8KV_OK;
+}
+
 fp8kv_status fp8kv_pool_free(fp8kv_pool* p, int32_t n, const int32_t* ids) {
   if (!p || n < 0 || (n > 0 && !ids)) return FP8KV_INVALID_ARG;
-  // validate everything first: all-or-nothing
+  if (!valid_held_list(p, n, ids, false)) return FP8KV_INVALID_ARG;  // all-or-nothing
   for (int32_t k = 0; k < n; ++k) {
     const int32_t id = ids[k];
-    if (id < 0 || id >= p->n || p->live[id] != 1) {
-      for (int32_t j = 0; j < k; ++j) p->live[ids[j]] = 1;  // undo duplicate marks
-      return FP8KV_INVALID_ARG;
-    }
-    p->live[id] = 2;  // seen in this call (catches duplicates)
-  }
-  for (int32_t k = 0; k < n; ++k) {
-    const int32_t id = ids[k];
-    p->live[id] = 0;
+    if (--p->refs[id] > 0) continue;  // other holders keep it
     p->ring[(p->head + p->count) % p->n] = id;
     ++p->count;
   }
   return FP8KV_OK;
+}
+
+int32_t fp8kv_pool_refcount(const fp8kv_pool* p, int32_t id) {
+  if (!p || id < 0 || id >= p->n) return -1;
+  return p->refs[id];
 }
 
 uint32_t fp8kv_pool_tag(const fp8kv_pool* p, int32_t id) {

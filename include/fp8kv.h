@@ -115,10 +115,27 @@ void fp8kv_pool_destroy(fp8kv_pool *pool);
 fp8kv_status fp8kv_pool_alloc(fp8kv_pool *pool, int32_t n, int32_t *h_page_ids,
                               uint32_t *h_tags);
 
-/* Return n pages.  Every id must be in range, currently allocated and listed
- * once; otherwise nothing is freed and FP8KV_INVALID_ARG is returned.  Tags are
- * not changed on free; they change at the next allocation. */
+/* Release n pages: each listed page loses one holder, and a page without
+ * holders returns to the free list.  Every id must be in range, currently
+ * held and listed once; otherwise nothing changes and FP8KV_INVALID_ARG is
+ * returned.  Tags are not changed on free; they change at the next allocation. */
 fp8kv_status fp8kv_pool_free(fp8kv_pool *pool, int32_t n, const int32_t *h_page_ids);
+
+/* Add one holder to each of n pages that are currently held: a request that
+ * maps pages another request already holds (a shared prefix) records their
+ * current tags (fp8kv_pool_tag) as its expected tags.  The tags do not change;
+ * a shared page returns to the free list only when every holder has freed it.
+ * Shared pages are read-only for their holders: a request writes its new
+ * tokens into pages it holds alone (the library does not enforce this; an
+ * append into a shared page is visible to every holder).  Every id must be in
+ * range, currently held and listed once; otherwise nothing changes and
+ * FP8KV_INVALID_ARG is returned.  Cache reuse across requests is what the
+ * integrity section of the Cloudflare post names as the reason a bad mapping
+ * reaches further. */
+fp8kv_status fp8kv_pool_share(fp8kv_pool *pool, int32_t n, const int32_t *h_page_ids);
+
+/* Number of holders of a page (0: free; -1 for an id out of range). */
+int32_t fp8kv_pool_refcount(const fp8kv_pool *pool, int32_t page_id);
 
 /* Current tag of a page (0 for an id out of range). */
 uint32_t fp8kv_pool_tag(const fp8kv_pool *pool, int32_t page_id);

@@ -120,3 +120,86 @@ def test_tag_wraps_around():
         ids, tg = pool.alloc(1)
         assert int(tg[0]) == (t0 + k + 1) & 0xFFFFFFFF
         pool.free(ids)
+
+
+def test_random_alloc_share_free_against_model():
+    """Reference counts: a page returns to the free list when its last holder
+    frees it; sharing never changes a tag; only re-allocation does."""
+    rng = random.Random(7)
+    for trial in range(20):
+        N = rng.randint(1, 40)
+        pool = fp8kv.Pool(N, seed=100 + trial)
+        tags = {i: int(t) for i, t in enumerate(pool.tags())}
+        refs = {i: 0 for i in range(N)}
+        free = list(range(N))
+        for step in range(400):
+            op = rng.random()
+            held = [i for i in range(N) if refs[i] > 0]
+            if op < 0.35:
+                n = rng.randint(0, 4)
+                if n > len(free):
+                    with pytest.raises(fp8kv.Fp8kvError):
+                        pool.alloc(n)
+                    continue
+                ids, tg = pool.alloc(n)
+                assert list(ids) == free[:n]
+                del free[:n]
+                for i, t in zip(ids, tg):
+                    tags[int(i)] = (tags[int(i)] + 1) & 0xFFFFFFFF
+                    refs[int(i)] = 1
+                    assert int(t) == tags[int(i)]
+            elif op < 0.65 and held:
+                ids = rng.sample(held, rng.randint(1, len(held)))
+                got = pool.share(ids)
+                for i, t in zip(ids, got):
+                    refs[i] += 1
+                    assert int(t) == tags[i]            # same tag for the new holder
+            elif held and rng.random() < 0.85:
+                ids = rng.sample(held, rng.randint(1, len(held)))
+                pool.free(ids)
+                for i in ids:
+                    refs[i] -= 1
+                    if refs[i] == 0:
+                        free.append(i)
+            else:
+                bad = rng.choice([[-1], [N], [i for i in range(N) if refs[i] == 0][:1],
+                                  held[:1] * 2])
+                if not bad or (len(bad) == 1 and 0 <= bad[0] < N and refs[bad[0]] > 0):
+                    continue
+                before = [pool.refcount(i) for i in range(N)]
+                with pytest.raises(fp8kv.Fp8kvError):
+                    (pool.share if rng.random() < 0.5 else pool.free)(bad)
+                assert [pool.refcount(i) for i in range(N)] == before   # all-or-nothing
+            assert pool.num_free == len(free)
+            assert all(pool.refcount(i) == refs[i] for i in range(N))
+            assert all(int(pool.tag(i)) == tags[i] for i in range(N))
+        pool.close()
+
+
+def test_shared_prefix_isolation():
+    """Two requests share a prefix; cancelling one leaves the other valid; once
+    the last holder is gone the page is reissued with a new tag and any stale
+    holder aborts while the new owner does not."""
+    pool = fp8kv.Pool(16, seed=9)
+    pre_ids, pre_tags = pool.alloc(2)                 # request A: prefix (2 full pages)
+    a_tail, a_ttag = pool.alloc(1)                    # ... and its own last page
+    b_tags = pool.share(pre_ids)                      # request B maps the same prefix
+    assert (b_tags == pre_tags).all()
+    b_tail, b_ttag = pool.alloc(1)
+    A = (np.r_[pre_ids, a_tail], np.r_[pre_tags, a_ttag], 40)
+    B = (np.r_[pre_ids, b_tail], np.r_[b_tags, b_ttag], 36)
+    assert list(_check(pool, [A, B], 3)) == [0, 0]
+    # A is cancelled: its pages are released, the shared ones stay with B
+    pool.free(np.r_[pre_ids, a_tail])
+    assert [pool.refcount(int(i)) for i in pre_ids] == [1, 1]
+    assert list(_check(pool, [B], 3)) == [0]
+    # B finishes too: the prefix pages go back to the pool ...
+    pool.free(np.r_[pre_ids, b_tail])
+    assert pool.num_free == 16
+    # ... and are handed out again with new tags (FIFO: drain down to them)
+    pool.alloc(pool.num_free - 4)
+    c_ids, c_tags = pool.alloc(4)
+    assert set(int(i) for i in pre_ids) <= set(int(i) for i in c_ids)
+    C = (c_ids[:3], c_tags[:3], 48)
+    # a holder that kept its old view of the prefix is caught; the new owner is not
+    assert list(_check(pool, [B, C], 3)) == [1, 0]
