@@ -427,7 +427,7 @@ def main():
         "hbm_gbps": round(gbps, 1), "pct_of_8tbps": round(100 * gbps / PEAK_GBPS, 2),
         "step_alg_bytes": step_bytes,
         "roofline": {"bound": "hbm",
-                     "kernel": "fp8kv_decode_attention call (decode_kernel + merge_kernel)",
+                     "kernel": "fp8kv_decode_attention call (decode_kernel + merge pass)",
                      "achieved": round(attn_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attn_gbps / PEAK_GBPS, 4),
                      "traffic": counter_traffic() if (cfg == 3 and cache == 0) else None,

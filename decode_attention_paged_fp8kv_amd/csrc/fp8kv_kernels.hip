@@ -411,7 +411,7 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_append_kernel(VerifyApp
 // each with its own online softmax, and are merged through LDS at the end of
 // the piece.  A piece that is a whole segment writes the output; any other
 // piece leaves (max, sum, weighted V) in slot  w + segment  (unique per
-// (workgroup, segment) pair) for merge_kernel.
+// (workgroup, segment) pair) for the merge pass.
 //
 // Each wave walks its own padded sequence of pages (per piece, its pages
 // rounded up to a multiple of DEPTH with masked dummies), so the register
@@ -931,16 +931,20 @@ void decode_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // 5. merge of the pieces of split segments (fixed order: deterministic)
 // ---------------------------------------------------------------------------
-// Workgroups stride over (request, kv-head) segments.  A thread takes one
-// (head, 4 dims) pair and one group of consecutive pieces; the groups' states
-// are then merged through LDS in group order, so a segment cut into many
-// pieces (few long requests) costs a few rounds of loads, not one per piece.
-// A separate pass: ordering the partial writes of other workgroups inside the
-// decode kernel would need a device-scope release/acquire per piece, which on
-// this part writes back and invalidates the L2 and costs far more than this
-// launch.
+// Workgroups stride over (request, kv-head) segments.  Two forms: a flat one
+// (a thread per (head, 4 dims) pair walks all of the segment's pieces) for
+// segments of a few pieces, and a grouped one for segments cut into many
+// pieces (few long requests): there a thread takes one (head, 4 dims) pair and
+// one group of consecutive pieces, and the groups' states meet in LDS in group
+// order.  Both are deterministic.  A separate pass: ordering the partial
+// writes of other workgroups inside the decode kernel would need a device-scope
+// release/acquire per piece, which on this part writes back and invalidates
+// the L2 and costs far more than this launch.
 constexpr int kMergeUnroll = 8;
-constexpr int kMergeThreads = 1024;
+constexpr int kMergeFlatThreads = 256;
+constexpr int kMergeGroupedThreads = 1024;
+// segments average at least this many pieces: the grouped form
+constexpr int kMergeGroupedMinPieces = 4;
 
 // fold one piece's (max, sum, weighted V) into a running state
 __device__ __forceinline__ void merge_state(float& M, float& L, f32x4_t& O, float m, float l,
@@ -957,54 +961,100 @@ __device__ __forceinline__ void merge_state(float& M, float& L, f32x4_t& O, floa
   O += e * o;
 }
 
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int64_t grid) {
-  __shared__ float s_m[kMergeThreads];
-  __shared__ float s_l[kMergeThreads];
-  __shared__ f32x4_t s_o[kMergeThreads];
+// the pieces of workgroups [w0, w1) of segment seg, for head n, dims d..d+3
+__device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int64_t seg, int n, int d,
+                                             int64_t w0, int64_t w1, float& M, float& L,
+                                             f32x4_t& O) {
+  for (int64_t w = w0; w < w1; w += kMergeUnroll) {
+    // issue the loads of several pieces before using any of them
+    float m[kMergeUnroll], l[kMergeUnroll];
+    f32x4_t o[kMergeUnroll];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const bool has = w + u < w1;
+      const int64_t pidx = (w + u + seg) * a.G + n;
+      m[u] = has ? a.ws_ml[pidx * 2] : -INFINITY;
+      l[u] = has ? a.ws_ml[pidx * 2 + 1] : 0.f;
+      o[u] = has ? *reinterpret_cast<const f32x4_t*>(a.ws_o + pidx * kHeadDim + d)
+                 : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) merge_state(M, L, O, m[u], l[u], o[u]);
+  }
+}
+
+__device__ __forceinline__ void merge_store(const DecodeArgs& a, int b, int g, int n, int d,
+                                            float L, f32x4_t O) {
+  const float vsc = a.v_scale ? a.v_scale[g] : 1.0f;
+  const float inv = L > 0.f ? vsc / L : 0.f;
+  const int64_t io = (static_cast<int64_t>(b) * a.Hq + g * a.G + n) * kHeadDim + d;
+  if (a.out_f32) {
+    *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + io) = O * inv;
+  } else {
+    u32x2_t w;
+    w.x = __builtin_bit_cast(unsigned short, static_cast<__bf16>(O[0] * inv)) |
+          (static_cast<unsigned>(__builtin_bit_cast(unsigned short, static_cast<__bf16>(O[1] * inv))) << 16);
+    w.y = __builtin_bit_cast(unsigned short, static_cast<__bf16>(O[2] * inv)) |
+          (static_cast<unsigned>(__builtin_bit_cast(unsigned short, static_cast<__bf16>(O[3] * inv))) << 16);
+    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + io) = w;
+  }
+}
+
+// The workgroups holding pieces of segment seg (false: nothing to merge, the
+// segment is empty or one workgroup wrote it whole).  With at least one page
+// per workgroup no slice is empty, so every workgroup in [wf, wl] holds one.
+__device__ __forceinline__ bool segment_span(const DecodeArgs& a, int seg, int64_t W,
+                                             int64_t NWG, int64_t& wf, int64_t& wl) {
+  const int b = seg / a.Hkv;
+  const int g = seg % a.Hkv;
+  const int pre_b = a.ws_pre[b];
+  const int np = a.ws_pre[b + 1] - pre_b;
+  if (np == 0) return false;
+  const int64_t first = static_cast<int64_t>(a.Hkv) * pre_b + static_cast<int64_t>(g) * np;
+  segment_workgroups(first, first + np - 1, W, NWG, wf, wl);
+  return wf != wl;
+}
+
+__global__ __launch_bounds__(kMergeFlatThreads) void merge_flat_kernel(DecodeArgs a, int64_t grid) {
   const int64_t W = static_cast<int64_t>(a.Hkv) * a.ws_pre[a.batch];
   const int64_t NWG = slice_count(W, grid);
-  const int items = a.G * (kHeadDim / 4);        // (head, 4 dims) pairs, at most 512
-  const int groups = kMergeThreads / items;      // at least 2
+  for (int seg = blockIdx.x; seg < a.batch * a.Hkv; seg += gridDim.x) {
+    int64_t wf, wl;
+    if (!segment_span(a, seg, W, NWG, wf, wl)) continue;
+    for (int idx = threadIdx.x; idx < a.G * (kHeadDim / 4); idx += kMergeFlatThreads) {
+      const int n = idx / (kHeadDim / 4);
+      const int d = 4 * (idx % (kHeadDim / 4));
+      float M = -INFINITY, L = 0.f;
+      f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+      merge_pieces(a, seg, n, d, wf, wl + 1, M, L, O);
+      merge_store(a, seg / a.Hkv, seg % a.Hkv, n, d, L, O);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kMergeGroupedThreads) void merge_grouped_kernel(DecodeArgs a,
+                                                                             int64_t grid) {
+  __shared__ float s_m[kMergeGroupedThreads];
+  __shared__ float s_l[kMergeGroupedThreads];
+  __shared__ f32x4_t s_o[kMergeGroupedThreads];
+  const int64_t W = static_cast<int64_t>(a.Hkv) * a.ws_pre[a.batch];
+  const int64_t NWG = slice_count(W, grid);
+  const int items = a.G * (kHeadDim / 4);            // (head, 4 dims) pairs, at most 512
+  const int groups = kMergeGroupedThreads / items;   // at least 2
   const int t = threadIdx.x;
   const bool active = t < items * groups;
   const int idx = t % items, grp = t / items;
   const int n = idx / (kHeadDim / 4);
   const int d = 4 * (idx % (kHeadDim / 4));
   for (int seg = blockIdx.x; seg < a.batch * a.Hkv; seg += gridDim.x) {
-    const int b = seg / a.Hkv;
-    const int g = seg % a.Hkv;
-    const int pre_b = a.ws_pre[b];
-    const int np = a.ws_pre[b + 1] - pre_b;
-    if (np == 0) continue;  // uniform over the workgroup, like the test below
-    const int64_t first = static_cast<int64_t>(a.Hkv) * pre_b + static_cast<int64_t>(g) * np;
     int64_t wf, wl;
-    segment_workgroups(first, first + np - 1, W, NWG, wf, wl);
-    if (wf == wl) continue;  // one piece: written by the decode kernel
-    // every workgroup in [wf, wl] holds a piece: with at least one page per
-    // workgroup no slice is empty
+    if (!segment_span(a, seg, W, NWG, wf, wl)) continue;  // uniform: no barrier skipped
     const int64_t chunk = (wl - wf + groups) / groups;
     const int64_t w0 = wf + grp * chunk;
     const int64_t w1 = (w0 + chunk < wl + 1) ? w0 + chunk : wl + 1;
     float M = -INFINITY, L = 0.f;
     f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-    if (active) {
-      for (int64_t w = w0; w < w1; w += kMergeUnroll) {
-        // issue the loads of several pieces before using any of them
-        float m[kMergeUnroll], l[kMergeUnroll];
-        f32x4_t o[kMergeUnroll];
-#pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) {
-          const bool has = w + u < w1;
-          const int64_t pidx = (w + u + seg) * a.G + n;
-          m[u] = has ? a.ws_ml[pidx * 2] : -INFINITY;
-          l[u] = has ? a.ws_ml[pidx * 2 + 1] : 0.f;
-          o[u] = has ? *reinterpret_cast<const f32x4_t*>(a.ws_o + pidx * kHeadDim + d)
-                     : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) merge_state(M, L, O, m[u], l[u], o[u]);
-      }
-    }
+    if (active) merge_pieces(a, seg, n, d, w0, w1, M, L, O);
     s_m[t] = M;
     s_l[t] = L;
     s_o[t] = O;
@@ -1012,19 +1062,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int6
     if (active && grp == 0) {
       for (int k = 1; k < groups; ++k)
         merge_state(M, L, O, s_m[k * items + idx], s_l[k * items + idx], s_o[k * items + idx]);
-      const float vsc = a.v_scale ? a.v_scale[g] : 1.0f;
-      const float inv = L > 0.f ? vsc / L : 0.f;
-      const int64_t io = (static_cast<int64_t>(b) * a.Hq + g * a.G + n) * kHeadDim + d;
-      if (a.out_f32) {
-        *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + io) = O * inv;
-      } else {
-        u32x2_t w;
-        w.x = __builtin_bit_cast(unsigned short, static_cast<__bf16>(O[0] * inv)) |
-              (static_cast<unsigned>(__builtin_bit_cast(unsigned short, static_cast<__bf16>(O[1] * inv))) << 16);
-        w.y = __builtin_bit_cast(unsigned short, static_cast<__bf16>(O[2] * inv)) |
-              (static_cast<unsigned>(__builtin_bit_cast(unsigned short, static_cast<__bf16>(O[3] * inv))) << 16);
-        *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + io) = w;
-      }
+      merge_store(a, seg / a.Hkv, seg % a.Hkv, n, d, L, O);
     }
     __syncthreads();  // LDS is reused for the next segment
   }
@@ -1285,8 +1323,13 @@ fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc* desc, const void* d_
   st = launched();
   if (st != FP8KV_OK) return st;
   const int segs = batch * desc->num_kv_heads;
-  hipLaunchKernelGGL(merge_kernel, dim3(segs < 1024 ? segs : 1024), dim3(kMergeThreads), 0, stream,
-                     a, static_cast<int64_t>(blocks));
+  const dim3 mgrid(segs < 1024 ? segs : 1024);
+  if (blocks >= static_cast<int64_t>(kMergeGroupedMinPieces) * segs)
+    hipLaunchKernelGGL(merge_grouped_kernel, mgrid, dim3(kMergeGroupedThreads), 0, stream, a,
+                       static_cast<int64_t>(blocks));
+  else
+    hipLaunchKernelGGL(merge_flat_kernel, mgrid, dim3(kMergeFlatThreads), 0, stream, a,
+                       static_cast<int64_t>(blocks));
   return launched();
 }
 
