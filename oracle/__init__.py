@@ -147,5 +147,29 @@ def attention(k_cache, v_cache, k_scale, v_scale, q, page_table, ctx_lens, sm_sc
     return out, ob
 
 
+def attention_multi(k_cache, v_cache, k_scale, v_scale, q, page_table, ctx_lens, sm_scale,
+                    abort=None, cache_dtype: int = 0):
+    """Several new tokens per request verified in one step (speculative decoding:
+    a draft proposes tokens, the main model checks them together -- page "Kimi
+    and GLM Reasoning Slimming: Hands-On Test", section "It Follows the Same
+    Path as Cloudflare's Earlier Infire Optimizations").  q is [B][T][Hq][D];
+    ctx_lens counts the tokens after all T new ones were appended.  Query i
+    stands for the new token at position ctx-T+i and sees the tokens up to and
+    including it: it is single-query attention over the first ctx-(T-1-i)
+    tokens (a query with no token to see gives +0, as an empty context does).
+    Returns (out64 [B][T][Hq][D] float64, out_bf16 bits [B][T][Hq][D])."""
+    qq = _c(q, np.uint16)
+    B, T, Hq, D = qq.shape
+    cl = _c(ctx_lens, np.int32)
+    out = np.zeros((B, T, Hq, D), np.float64)
+    ob = np.zeros((B, T, Hq, D), np.uint16)
+    for i in range(T):
+        ci = np.maximum(cl - (T - 1 - i), 0).astype(np.int32)
+        out[:, i], ob[:, i] = attention(k_cache, v_cache, k_scale, v_scale,
+                                        np.ascontiguousarray(qq[:, i]), page_table, ci, sm_scale,
+                                        abort=abort, cache_dtype=cache_dtype)
+    return out, ob
+
+
 def num_threads() -> int:
     return int(lib().oracle_num_threads())

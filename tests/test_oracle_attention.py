@@ -212,3 +212,54 @@ def test_workload_step_end_to_end():
                              for j in range(int(w.ctx_lens[b]))])
             assert (out[b, h] <= vals.max(0) + 1e-12).all()
             assert (out[b, h] >= vals.min(0) - 1e-12).all()
+
+
+# ---------------------------------------------------------------------------
+# several new tokens per request (speculative verification): query i sees the
+# cached tokens and the new tokens up to its own
+# ---------------------------------------------------------------------------
+def _multi_case(T, seed=5, lens=(3, 16, 17, 33), Hq=4, Hkv=2):
+    K, V, ks, vs, _, pt, L = _case(seed=seed, lens=lens, Hq=Hq, Hkv=Hkv)
+    q = workloads.draw_bits(seed + 7, 0, len(lens) * T * Hq * D).reshape(len(lens), T, Hq, D)
+    return K, V, ks, vs, q, pt, L
+
+
+def test_multi_one_query_is_single_query_attention():
+    K, V, ks, vs, q, pt, L = _multi_case(1)
+    got, gb = oracle.attention_multi(K, V, ks, vs, q, pt, L, SM)
+    ref, rb = oracle.attention(K, V, ks, vs, np.ascontiguousarray(q[:, 0]), pt, L, SM)
+    assert (got[:, 0] == ref).all() and (gb[:, 0] == rb).all()
+
+
+def test_multi_rows_agree_with_brute_force_over_their_prefix():
+    T = 3
+    K, V, ks, vs, q, pt, L = _multi_case(T)
+    got, _ = oracle.attention_multi(K, V, ks, vs, q, pt, L, SM)
+    for i in range(T):
+        seen = L - (T - 1 - i)                     # query i: tokens 0 .. L-T+i
+        ref = brute_force(K, V, ks, vs, np.ascontiguousarray(q[:, i]), pt, seen, SM)
+        assert np.allclose(got[:, i], ref, rtol=1e-12, atol=1e-15), i
+
+
+def test_multi_is_causal_among_the_new_tokens():
+    """Changing the last new token's K and V changes only the last query."""
+    T = 4
+    K, V, ks, vs, q, pt, L = _multi_case(T, lens=(20, 35))
+    a, _ = oracle.attention_multi(K, V, ks, vs, q, pt, L, SM)
+    K2, V2 = K.copy(), V.copy()
+    for b in range(len(L)):
+        j = int(L[b]) - 1                          # position of the last new token
+        p, s = pt[b, j // S], j % S
+        K2[p, :, s] ^= 0x11
+        V2[p, :, s] ^= 0x22
+    b_, _ = oracle.attention_multi(K2, V2, ks, vs, q, pt, L, SM)
+    assert (a[:, :T - 1] == b_[:, :T - 1]).all()
+    assert not (a[:, T - 1] == b_[:, T - 1]).all()
+
+
+def test_multi_queries_beyond_the_context_are_zero():
+    T = 3
+    K, V, ks, vs, q, pt, L = _multi_case(T, lens=(1, 2, 5))
+    got, gb = oracle.attention_multi(K, V, ks, vs, q, pt, L, SM)
+    assert (got[0, :2] == 0).all() and (got[1, :1] == 0).all() and (gb[0, :2] == 0).all()
+    assert (got[0, 2] != 0).any() and (got[1, 1] != 0).any()
