@@ -77,6 +77,11 @@ _ws_size = _sig("fp8kv_decode_workspace_size", ctypes.c_size_t,
 _decode = _sig("fp8kv_decode_attention", _i32,
                [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _i32,
                 ctypes.c_float, _p, _p, _i32, _i32, _p, ctypes.c_size_t, _p])
+_ws_size_q = _sig("fp8kv_decode_workspace_size_q", ctypes.c_size_t,
+                  [ctypes.POINTER(CacheDesc), _i32, _i32, _i32, _i32])
+_decode_q = _sig("fp8kv_decode_attention_q", _i32,
+                 [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _i32, _i32, _p, _i32, _p, _i32,
+                  ctypes.c_float, _p, _p, _i32, _i32, _p, ctypes.c_size_t, _p])
 _verify_append = _sig("fp8kv_verify_append", _i32,
                       [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _p,
                        _i32, _p, _p, _p])
@@ -327,6 +332,43 @@ def decode_attention(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, page_t
             num_workers, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
             _stream(stream))
     return _run(_decode, args, "decode_attention", out,
+                (d, k_cache, v_cache, k_scale, v_scale, q, page_table, ctx_lens, abort, out,
+                 workspace), prepare)
+
+
+def decode_workspace_size_q(d: CacheDesc, batch: int, num_q_heads: int, q_len: int,
+                            num_workers: int = 0) -> int:
+    return int(_ws_size_q(ctypes.byref(d), batch, num_q_heads, q_len, num_workers))
+
+
+def decode_attention_q(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, page_table, ctx_lens,
+                       abort=None, out=None, out_dtype: int = OUT_BF16,
+                       sm_scale: Optional[float] = None, num_workers: int = 0, workspace=None,
+                       stream=None, prepare: bool = False):
+    """Decode attention with q_len queries per request (several new tokens checked
+    at once; query i attends the cache up to its own token).  q [B][q_len][Hq][128];
+    ctx_lens counts tokens after all q_len new ones; returns out [B][q_len][Hq][128]."""
+    B, T, Hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, T, Hq, D), device=q.device,
+                          dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32)
+    need = decode_workspace_size_q(d, B, Hq, T, num_workers)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    fp8 = d.cache_dtype == E4M3
+    args = (ctypes.byref(d), _dev(k_cache, _U8 + _BITS16, "k_cache"),
+            _dev(v_cache, _U8 + _BITS16, "v_cache"),
+            _dev(k_scale, _F32, "k_scale", allow_none=not fp8),
+            _dev(v_scale, _F32, "v_scale", allow_none=not fp8),
+            _dev(q, _BITS16, "q"), Hq, T, _dev(page_table, _I32, "page_table"),
+            page_table.shape[1], _dev(ctx_lens, _I32, "ctx_lens"), B,
+            float(sm_scale), _dev(abort, _U8, "abort", allow_none=True),
+            _dev(out, (torch.bfloat16, torch.int16, torch.float32), "out"), out_dtype,
+            num_workers, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    return _run(_decode_q, args, "decode_attention_q", out,
                 (d, k_cache, v_cache, k_scale, v_scale, q, page_table, ctx_lens, abort, out,
                  workspace), prepare)
 

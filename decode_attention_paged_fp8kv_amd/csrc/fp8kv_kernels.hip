@@ -427,13 +427,24 @@ struct DecodeArgs {
   const int32_t* ctx_lens;
   const uint8_t* abort;
   void* out;
-  float* ws_o;     // [slots][G][128] unnormalised weighted V
-  float* ws_ml;    // [slots][G][2]   (max in log2 units, sum)
+  float* ws_o;     // [slots][C][128] unnormalised weighted V
+  float* ws_ml;    // [slots][C][2]   (max in log2 units, sum)
   int32_t* ws_pre; // [B+1] page prefix sums of live requests
   int64_t page_stride;
-  int32_t batch, max_pages, num_pages, Hq, Hkv, G, out_f32;
+  // qlen: new tokens (queries) per request; C = G * qlen MFMA columns used
+  int32_t batch, max_pages, num_pages, Hq, Hkv, G, qlen, C, out_f32;
   float sm_scale;
 };
+
+// Q and the output are [B][qlen][Hq][128].  Column n < C of the MFMA tiles of
+// (request b, kv-head g) holds query n / G of q-head g*G + n % G: this is the
+// row of Q and of the output it reads and writes.  With several queries per
+// request (several new tokens checked at once, speculative decoding) query i
+// sees the cache up to its own token: it ignores the last qlen-1-i tokens.
+__device__ __forceinline__ int64_t column_row(const DecodeArgs& a, int b, int g, int n) {
+  const int qi = n / a.G;
+  return (static_cast<int64_t>(b) * a.qlen + qi) * a.Hq + g * a.G + (n - qi * a.G);
+}
 
 constexpr int kMaxBatch = 4096;
 
@@ -610,9 +621,11 @@ void decode_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15;   // head within the group (MFMA column)
+  const int n = lane & 15;   // (query, head) of the group: the MFMA column
   const int qd = lane >> 4;  // lane quarter
   const int B = a.batch;
+  // trailing tokens of the context this column's query does not see
+  const int lag = n < a.C ? a.qlen - 1 - n / a.G : 0;
 
   // ---- prologue: page prefix sums of the live requests ------------------
   {
@@ -661,8 +674,8 @@ void decode_kernel(DecodeArgs a) {
     // requests with nothing to read get +0 rows (aborted, empty, invalid)
     for (int b = blockIdx.x; b < B; b += gridDim.x) {
       if (s_pre[b + 1] != s_pre[b]) continue;
-      const int64_t base = static_cast<int64_t>(b) * a.Hq * kHeadDim;
-      for (int i = threadIdx.x; i < a.Hq * kHeadDim; i += kThreads) {
+      const int64_t base = static_cast<int64_t>(b) * a.qlen * a.Hq * kHeadDim;
+      for (int i = threadIdx.x; i < a.qlen * a.Hq * kHeadDim; i += kThreads) {
         if (a.out_f32)
           static_cast<float*>(a.out)[base + i] = 0.0f;
         else
@@ -728,12 +741,12 @@ void decode_kernel(DecodeArgs a) {
   for (int s = 0; s < DEPTH; ++s) pid_ring[s] = fetch_pid();
 
   // Q fragment (B operand of the QK^T MFMA) of a piece: lane (n, qd) holds,
-  // for step kk, q[head n][32 qd + 8 kk + i], i < 8; heads past the group are 0
+  // for step kk, q[column n][32 qd + 8 kk + i], i < 8; columns past C are 0
   auto load_q = [&](const Piece& pc, u32x4_t (&dst)[4]) {
     const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(
-        a.q + (static_cast<int64_t>(pc.b) * a.Hq + pc.g * a.G + n) * kHeadDim + 32 * qd);
+        a.q + column_row(a, pc.b, pc.g, n < a.C ? n : 0) * kHeadDim + 32 * qd);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) dst[kk] = n < a.G ? qrow[kk] : u32x4_t{0u, 0u, 0u, 0u};
+    for (int kk = 0; kk < 4; ++kk) dst[kk] = n < a.C ? qrow[kk] : u32x4_t{0u, 0u, 0u, 0u};
   };
   Piece P = first;  // piece being processed (all waves visit every piece)
   for (;;) {
@@ -773,7 +786,10 @@ void decode_kernel(DecodeArgs a) {
         for (int s = 0; s < DEPTH; ++s) {
           const int i = i0 + s;
           const int page = pg0 + kWaves * i;
-          const int valid = (i < cnt && okp[s]) ? min(ctx - page * kPage, kPage) : 0;
+          // context tokens from this page on (not clamped to the page: a column's
+          // limit ctx - lag can fall on this page even when ctx lies beyond it)
+          const int left = (i < cnt && okp[s]) ? ctx - page * kPage : 0;
+          const int valid = min(left, kPage);
 
           // ---- S^T = K Q^T : rows = 16 tokens, cols = 16 heads ------------
           f32x4_t st = {0.f, 0.f, 0.f, 0.f};
@@ -793,10 +809,10 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) sv[r] = st[r] * sc;
           u32x4_t vmask = {~0u, ~0u, ~0u, ~0u};
-          if (valid < kPage) {
+          if (left - (a.qlen - 1) < kPage) {  // some column stops inside this page
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              if (4 * qd + r >= valid) sv[r] = -INFINITY;
+              if (4 * qd + r >= left - lag) sv[r] = -INFINITY;
             // tokens past the end may hold any bytes: clear their V so 0*x stays 0
             const int keep = min(max(valid - 4 * qd, 0), 4);  // tokens 4qd+j, j<keep
             if constexpr (CACHE == FP8KV_E4M3) {
@@ -899,7 +915,7 @@ void decode_kernel(DecodeArgs a) {
         for (int w = 0; w < kWaves; ++w) o += e[w] * s_acc[w][t * 4 + wave][lane];
         O[t] = o;
       }
-      if (n < a.G) {
+      if (n < a.C) {
         const int d0 = 32 * qd + 8 * wave;
         if (P.ps == P.sx && P.pe == P.sx + P.n) {
           // the whole segment sits in this slice: write the output
@@ -908,10 +924,9 @@ void decode_kernel(DecodeArgs a) {
           float v[8];
 #pragma unroll
           for (int t = 0; t < 8; ++t) v[t] = O[t] * inv;
-          const int64_t row = static_cast<int64_t>(P.b) * a.Hq + P.g * a.G + n;
-          store_out8(a, row * kHeadDim + d0, v);
+          store_out8(a, column_row(a, P.b, P.g, n) * kHeadDim + d0, v);
         } else {
-          const int64_t pidx = (bw + static_cast<int64_t>(P.b) * a.Hkv + P.g) * a.G + n;
+          const int64_t pidx = (bw + static_cast<int64_t>(P.b) * a.Hkv + P.g) * a.C + n;
           f32x4_t* po = reinterpret_cast<f32x4_t*>(a.ws_o + pidx * kHeadDim + d0);
           po[0] = f32x4_t{O[0], O[1], O[2], O[3]};
           po[1] = f32x4_t{O[4], O[5], O[6], O[7]};
@@ -972,7 +987,7 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int64_t seg, i
 #pragma unroll
     for (int u = 0; u < kMergeUnroll; ++u) {
       const bool has = w + u < w1;
-      const int64_t pidx = (w + u + seg) * a.G + n;
+      const int64_t pidx = (w + u + seg) * a.C + n;
       m[u] = has ? a.ws_ml[pidx * 2] : -INFINITY;
       l[u] = has ? a.ws_ml[pidx * 2 + 1] : 0.f;
       o[u] = has ? *reinterpret_cast<const f32x4_t*>(a.ws_o + pidx * kHeadDim + d)
@@ -987,7 +1002,7 @@ __device__ __forceinline__ void merge_store(const DecodeArgs& a, int b, int g, i
                                             float L, f32x4_t O) {
   const float vsc = a.v_scale ? a.v_scale[g] : 1.0f;
   const float inv = L > 0.f ? vsc / L : 0.f;
-  const int64_t io = (static_cast<int64_t>(b) * a.Hq + g * a.G + n) * kHeadDim + d;
+  const int64_t io = column_row(a, b, g, n) * kHeadDim + d;
   if (a.out_f32) {
     *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + io) = O * inv;
   } else {
@@ -1021,7 +1036,7 @@ __global__ __launch_bounds__(kMergeFlatThreads) void merge_flat_kernel(DecodeArg
   for (int seg = blockIdx.x; seg < a.batch * a.Hkv; seg += gridDim.x) {
     int64_t wf, wl;
     if (!segment_span(a, seg, W, NWG, wf, wl)) continue;
-    for (int idx = threadIdx.x; idx < a.G * (kHeadDim / 4); idx += kMergeFlatThreads) {
+    for (int idx = threadIdx.x; idx < a.C * (kHeadDim / 4); idx += kMergeFlatThreads) {
       const int n = idx / (kHeadDim / 4);
       const int d = 4 * (idx % (kHeadDim / 4));
       float M = -INFINITY, L = 0.f;
@@ -1039,7 +1054,7 @@ __global__ __launch_bounds__(kMergeGroupedThreads) void merge_grouped_kernel(Dec
   __shared__ f32x4_t s_o[kMergeGroupedThreads];
   const int64_t W = static_cast<int64_t>(a.Hkv) * a.ws_pre[a.batch];
   const int64_t NWG = slice_count(W, grid);
-  const int items = a.G * (kHeadDim / 4);            // (head, 4 dims) pairs, at most 512
+  const int items = a.C * (kHeadDim / 4);            // (column, 4 dims) pairs, at most 512
   const int groups = kMergeGroupedThreads / items;   // at least 2
   const int t = threadIdx.x;
   const bool active = t < items * groups;
@@ -1129,13 +1144,15 @@ struct WorkspaceLayout {
   size_t o, ml, pre, total;
 };
 
-WorkspaceLayout workspace_layout(int64_t batch, int64_t Hq, int64_t Hkv, int64_t workers) {
-  const int64_t G = Hq / Hkv;
+// C = (Hq / Hkv) * qlen columns per partial
+WorkspaceLayout workspace_layout(int64_t batch, int64_t Hq, int64_t Hkv, int64_t qlen,
+                                 int64_t workers) {
+  const int64_t C = Hq / Hkv * qlen;
   const int64_t slots = workers / kWaves + batch * Hkv;  // (workgroup + segment) slots
   WorkspaceLayout L;
   L.o = 0;
-  L.ml = L.o + static_cast<size_t>(slots * G * kHeadDim) * sizeof(float);
-  L.pre = L.ml + static_cast<size_t>(slots * G * 2) * sizeof(float);
+  L.ml = L.o + static_cast<size_t>(slots * C * kHeadDim) * sizeof(float);
+  L.pre = L.ml + static_cast<size_t>(slots * C * 2) * sizeof(float);
   L.pre = (L.pre + 255) / 256 * 256;
   L.total = L.pre + static_cast<size_t>(batch + 1) * sizeof(int32_t);
   return L;
@@ -1251,32 +1268,37 @@ int32_t fp8kv_decode_num_workers(int32_t requested) {
   return (w + kWaves - 1) / kWaves * kWaves;
 }
 
-size_t fp8kv_decode_workspace_size(const fp8kv_cache_desc* desc, int32_t batch,
-                                   int32_t num_q_heads, int32_t num_workers) {
-  if (check_desc(desc) != FP8KV_OK || batch < 0 || num_q_heads <= 0 ||
-      num_q_heads % desc->num_kv_heads != 0)
+}  // extern "C"
+
+namespace {
+
+size_t decode_workspace(const fp8kv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
+                        int32_t q_len, int32_t num_workers) {
+  if (check_desc(desc) != FP8KV_OK || batch < 0 || num_q_heads <= 0 || q_len <= 0 ||
+      num_q_heads % desc->num_kv_heads != 0 ||
+      num_q_heads / desc->num_kv_heads * q_len > kMaxGroup)
     return 0;
   const int32_t w = fp8kv_decode_num_workers(num_workers);
   if (w <= 0) return 0;
-  return workspace_layout(batch, num_q_heads, desc->num_kv_heads, w).total;
+  return workspace_layout(batch, num_q_heads, desc->num_kv_heads, q_len, w).total;
 }
 
-fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc* desc, const void* d_k_cache,
-                                    const void* d_v_cache, const float* d_k_scale,
-                                    const float* d_v_scale, const uint16_t* d_q,
-                                    int32_t num_q_heads, const int32_t* d_page_table,
-                                    int32_t max_pages_per_seq, const int32_t* d_ctx_lens,
-                                    int32_t batch, float sm_scale, const uint8_t* d_abort,
-                                    void* d_out, int32_t out_dtype, int32_t num_workers,
-                                    void* d_workspace, size_t workspace_bytes,
-                                    hipStream_t stream) {
+fp8kv_status decode_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
+                         const void* d_v_cache, const float* d_k_scale, const float* d_v_scale,
+                         const uint16_t* d_q, int32_t num_q_heads, int32_t q_len,
+                         const int32_t* d_page_table, int32_t max_pages_per_seq,
+                         const int32_t* d_ctx_lens, int32_t batch, float sm_scale,
+                         const uint8_t* d_abort, void* d_out, int32_t out_dtype,
+                         int32_t num_workers, void* d_workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
   fp8kv_status st = check_desc(desc);
   if (st != FP8KV_OK) return st;
-  if (batch < 0 || max_pages_per_seq < 0 || num_q_heads <= 0 || num_workers < 0)
+  if (batch < 0 || max_pages_per_seq < 0 || num_q_heads <= 0 || num_workers < 0 || q_len <= 0)
     return FP8KV_INVALID_ARG;
   if (num_q_heads % desc->num_kv_heads != 0) return FP8KV_UNSUPPORTED;
   const int G = num_q_heads / desc->num_kv_heads;
-  if (G > kMaxGroup || batch > kMaxBatch) return FP8KV_UNSUPPORTED;
+  // all (query, head) pairs of a kv-head share one 16-column MFMA tile
+  if (G * q_len > kMaxGroup || batch > kMaxBatch) return FP8KV_UNSUPPORTED;
   if (out_dtype != FP8KV_OUT_BF16 && out_dtype != FP8KV_OUT_F32) return FP8KV_INVALID_ARG;
   if (batch == 0) return FP8KV_OK;
   if (!d_k_cache || !d_v_cache || !d_q || !d_ctx_lens || !d_out ||
@@ -1285,9 +1307,9 @@ fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc* desc, const void* d_
   if (desc->cache_dtype == FP8KV_E4M3 && (!d_k_scale || !d_v_scale)) return FP8KV_INVALID_ARG;
   const int32_t workers = fp8kv_decode_num_workers(num_workers);
   if (workers <= 0) return FP8KV_HIP_ERROR;
-  const WorkspaceLayout L = workspace_layout(batch, num_q_heads, desc->num_kv_heads, workers);
+  const WorkspaceLayout L =
+      workspace_layout(batch, num_q_heads, desc->num_kv_heads, q_len, workers);
   if (!d_workspace || workspace_bytes < L.total) return FP8KV_WORKSPACE_TOO_SMALL;
-
   DecodeArgs a;
   a.k_cache = static_cast<const uint8_t*>(d_k_cache);
   a.v_cache = static_cast<const uint8_t*>(d_v_cache);
@@ -1310,6 +1332,8 @@ fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc* desc, const void* d_
   a.Hq = num_q_heads;
   a.Hkv = desc->num_kv_heads;
   a.G = G;
+  a.qlen = q_len;
+  a.C = G * q_len;
   a.out_f32 = out_dtype == FP8KV_OUT_F32 ? 1 : 0;
   a.sm_scale = sm_scale;
   const int blocks = workers / kWaves;
@@ -1331,6 +1355,48 @@ fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc* desc, const void* d_
     hipLaunchKernelGGL(merge_flat_kernel, mgrid, dim3(kMergeFlatThreads), 0, stream, a,
                        static_cast<int64_t>(blocks));
   return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fp8kv_decode_workspace_size(const fp8kv_cache_desc* desc, int32_t batch,
+                                   int32_t num_q_heads, int32_t num_workers) {
+  return decode_workspace(desc, batch, num_q_heads, 1, num_workers);
+}
+
+size_t fp8kv_decode_workspace_size_q(const fp8kv_cache_desc* desc, int32_t batch,
+                                     int32_t num_q_heads, int32_t q_len, int32_t num_workers) {
+  return decode_workspace(desc, batch, num_q_heads, q_len, num_workers);
+}
+
+fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc* desc, const void* d_k_cache,
+                                    const void* d_v_cache, const float* d_k_scale,
+                                    const float* d_v_scale, const uint16_t* d_q,
+                                    int32_t num_q_heads, const int32_t* d_page_table,
+                                    int32_t max_pages_per_seq, const int32_t* d_ctx_lens,
+                                    int32_t batch, float sm_scale, const uint8_t* d_abort,
+                                    void* d_out, int32_t out_dtype, int32_t num_workers,
+                                    void* d_workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  return decode_impl(desc, d_k_cache, d_v_cache, d_k_scale, d_v_scale, d_q, num_q_heads, 1,
+                     d_page_table, max_pages_per_seq, d_ctx_lens, batch, sm_scale, d_abort,
+                     d_out, out_dtype, num_workers, d_workspace, workspace_bytes, stream);
+}
+
+fp8kv_status fp8kv_decode_attention_q(const fp8kv_cache_desc* desc, const void* d_k_cache,
+                                      const void* d_v_cache, const float* d_k_scale,
+                                      const float* d_v_scale, const uint16_t* d_q,
+                                      int32_t num_q_heads, int32_t q_len,
+                                      const int32_t* d_page_table, int32_t max_pages_per_seq,
+                                      const int32_t* d_ctx_lens, int32_t batch, float sm_scale,
+                                      const uint8_t* d_abort, void* d_out, int32_t out_dtype,
+                                      int32_t num_workers, void* d_workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(desc, d_k_cache, d_v_cache, d_k_scale, d_v_scale, d_q, num_q_heads, q_len,
+                     d_page_table, max_pages_per_seq, d_ctx_lens, batch, sm_scale, d_abort,
+                     d_out, out_dtype, num_workers, d_workspace, workspace_bytes, stream);
 }
 
 fp8kv_status fp8kv_verify_append(const fp8kv_cache_desc* desc, void* d_k_cache, void* d_v_cache,

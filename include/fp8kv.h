@@ -255,6 +255,35 @@ fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc *desc, const void *d_
                                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Several new tokens per request checked in one step: speculative decoding, */
+/* where a draft proposes tokens and the main model verifies them together   */
+/* (page "Kimi and GLM Reasoning Slimming: Hands-On Test", section "It       */
+/* Follows the Same Path as Cloudflare's Earlier Infire Optimizations").     */
+/* Same as fp8kv_decode_attention with q_len queries per request:            */
+/*   d_q: BF16 bits [batch][q_len][Hq][128]; d_out: [batch][q_len][Hq][128]. */
+/*   d_ctx_lens[b] counts the request's tokens after all q_len new ones were */
+/*   appended (fp8kv_append with q_len tokens per request); query i stands   */
+/*   for the new token at position ctx-q_len+i and attends tokens            */
+/*   0..ctx-q_len+i (causal among the new tokens; a query with no token to   */
+/*   see gives +0).  (Hq / Hkv) * q_len <= 16: the (query, head) pairs of a  */
+/*   kv-head share one 16-wide MFMA tile, so checking q_len tokens reads the */
+/*   cache once.  q_len = 1 is fp8kv_decode_attention.                        */
+/*   d_workspace: at least fp8kv_decode_workspace_size_q() bytes.             */
+/* ------------------------------------------------------------------------ */
+size_t fp8kv_decode_workspace_size_q(const fp8kv_cache_desc *desc, int32_t batch,
+                                     int32_t num_q_heads, int32_t q_len, int32_t num_workers);
+
+fp8kv_status fp8kv_decode_attention_q(const fp8kv_cache_desc *desc, const void *d_k_cache,
+                                      const void *d_v_cache, const float *d_k_scale,
+                                      const float *d_v_scale, const uint16_t *d_q,
+                                      int32_t num_q_heads, int32_t q_len,
+                                      const int32_t *d_page_table, int32_t max_pages_per_seq,
+                                      const int32_t *d_ctx_lens, int32_t batch, float sm_scale,
+                                      const uint8_t *d_abort, void *d_out, int32_t out_dtype,
+                                      int32_t num_workers, void *d_workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Self-test of the on-read conversion: d_out[i] = the value the attention   */
 /* kernel's e4m3 -> bf16 (which = 0) or e4m3 -> f16 (which = 1) conversion   */
 /* gives for code d_codes[i], widened to fp32.  n a multiple of 4.           */

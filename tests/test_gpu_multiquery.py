@@ -1,0 +1,151 @@
+"""GPU: several new tokens per request checked in one step (speculative
+verification) -- fp8kv_append of the q_len new tokens, then
+fp8kv_decode_attention_q -- against the oracle's multi-query attention.
+
+Query i of a request sees the cache up to its own new token.  Covered: the
+(query, head) layouts G*q_len = 16, 12 and 5 columns, histories whose new
+tokens cross page boundaries, several work partitions, an aborted request,
+q_len = 1 against the single-query entry point (bitwise), each row against a
+one-token decode over its own prefix, and the G*q_len > 16 rejection.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _helpers import SM_SCALE, check_outputs, unswizzle
+from workloads import bf16_bits_to_f32, scales_from_amax
+from workloads.decode_loop import token_bits
+
+pytestmark = pytest.mark.gpu
+
+SEED = 31
+
+
+def _setup(fp8kv, hist, T, Hq, Hkv, seed=SEED):
+    """History of hist[b] tokens in the cache, the T new tokens appended by one
+    fp8kv_append call; returns everything both sides need."""
+    dev = "cuda"
+    B = len(hist)
+    ctx = np.array(hist, np.int32) + T
+    n = [-(-int(c) // 16) for c in ctx]
+    N = sum(n) + 5
+    perm = np.random.default_rng(seed).permutation(N).astype(np.int32)
+    pt = np.full((B, max(n)), -1, np.int32)
+    k = 0
+    for b in range(B):
+        pt[b, :n[b]] = perm[k:k + n[b]]
+        k += n[b]
+    toks = {w: [token_bits(seed, w, b, 0, int(ctx[b]), Hkv) for b in range(B)] for w in "kv"}
+    scale = {w: scales_from_amax(np.max([np.abs(bf16_bits_to_f32(t)).max(axis=(0, 2))
+                                         for t in toks[w]], axis=0)) for w in "kv"}
+    q = np.stack([token_bits(seed, "q", b, 0, T, Hq) for b in range(B)])   # [B][T][Hq][128]
+    d = fp8kv.desc(N, Hkv)
+    K, V = fp8kv.new_cache(d, dev)
+    st = dict(fp8kv=fp8kv, d=d, K=K, V=V, pt=pt, ctx=ctx, q=q, toks=toks, scale=scale, B=B, T=T,
+              Hq=Hq, Hkv=Hkv, N=N,
+              ks=torch.from_numpy(scale["k"]).to(dev), vs=torch.from_numpy(scale["v"]).to(dev),
+              pt_d=torch.from_numpy(pt).to(dev), ctx_d=torch.from_numpy(ctx).to(dev),
+              q_d=torch.from_numpy(q.view(np.int16)).to(dev))
+
+    def append(rows):   # rows: (b, t0, t1)
+        rows = [r for r in rows if r[2] > r[1]]
+        if not rows:
+            return
+        kb = np.concatenate([toks["k"][b][t0:t1] for b, t0, t1 in rows])
+        vb = np.concatenate([toks["v"][b][t0:t1] for b, t0, t1 in rows])
+        seq = np.concatenate([np.full(t1 - t0, b, np.int32) for b, t0, t1 in rows])
+        pos = np.concatenate([np.arange(t0, t1, dtype=np.int32) for b, t0, t1 in rows])
+        fp8kv.append(d, K, V, st["ks"], st["vs"],
+                     torch.from_numpy(np.ascontiguousarray(kb).view(np.int16)).to(dev),
+                     torch.from_numpy(np.ascontiguousarray(vb).view(np.int16)).to(dev),
+                     torch.from_numpy(seq).to(dev), torch.from_numpy(pos).to(dev), st["pt_d"])
+    append([(b, 0, hist[b]) for b in range(B)])                 # the cached history
+    append([(b, hist[b], hist[b] + T) for b in range(B)])       # the step's q_len new tokens
+    return st
+
+
+def _oracle(st, abort=None):
+    Ko, Vo = oracle.new_cache(st["N"], st["Hkv"])
+    for b in range(st["B"]):
+        c = int(st["ctx"][b])
+        if abort is not None and abort[b]:
+            c -= st["T"]                         # the aborted request's new tokens: not written
+        if c > 0:
+            oracle.append(Ko, Vo, st["scale"]["k"], st["scale"]["v"], st["toks"]["k"][b][:c],
+                          st["toks"]["v"][b][:c], np.full(c, b, np.int32),
+                          np.arange(c, dtype=np.int32), st["pt"])
+    ref, _ = oracle.attention_multi(Ko, Vo, st["scale"]["k"], st["scale"]["v"], st["q"], st["pt"],
+                                    st["ctx"], SM_SCALE, abort=abort)
+    return Ko, Vo, ref
+
+
+def _run(st, out_dtype, num_workers=0, abort=None):
+    f = st["fp8kv"]
+    ab = None if abort is None else torch.from_numpy(abort).cuda()
+    out = f.decode_attention_q(st["d"], st["K"], st["V"], st["ks"], st["vs"], st["q_d"],
+                               st["pt_d"], st["ctx_d"], abort=ab, out_dtype=out_dtype,
+                               num_workers=num_workers)
+    torch.cuda.synchronize()
+    return (out.view(torch.int16) if out.dtype == torch.bfloat16 else out).cpu().numpy()
+
+
+@pytest.mark.parametrize("Hq,Hkv,T", [(64, 8, 2), (8, 2, 3), (4, 4, 5)])
+@pytest.mark.parametrize("hist", [[1, 14, 15, 30, 47, 100], [0, 13, 16, 31]])
+def test_multi_query_matches_oracle(Hq, Hkv, T, hist):
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    st = _setup(fp8kv, hist, T, Hq, Hkv)
+    Ko, Vo, ref = _oracle(st)
+    used = np.unique(st["pt"][st["pt"] >= 0])
+    assert (unswizzle(st["K"].cpu().numpy(), Hkv, 0, used, False) == Ko[used]).all()
+    assert (unswizzle(st["V"].cpu().numpy(), Hkv, 0, used, True) == Vo[used]).all()
+    for nw in (0, 8, 64):
+        o32 = _run(st, fp8kv.OUT_F32, nw)
+        o16 = _run(st, fp8kv.OUT_BF16, nw).view(np.uint16)
+        err = check_outputs(o32, o16, ref)
+        print(f"Hq={Hq} Hkv={Hkv} T={T} hist={hist} workers={nw}: max abs err {err:.3e}")
+
+
+def test_one_query_equals_the_single_query_entry_point():
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    st = _setup(fp8kv, [5, 40, 77], 1, 64, 8)
+    a = _run(st, fp8kv.OUT_F32)
+    b = fp8kv.decode_attention(st["d"], st["K"], st["V"], st["ks"], st["vs"], st["q_d"][:, 0],
+                               st["pt_d"], st["ctx_d"], out_dtype=fp8kv.OUT_F32)
+    torch.cuda.synchronize()
+    assert np.array_equal(a[:, 0], b.cpu().numpy())
+
+
+def test_rows_equal_one_token_decodes_over_their_prefix():
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    T = 2
+    st = _setup(fp8kv, [9, 31, 64, 200], T, 64, 8)
+    multi = _run(st, fp8kv.OUT_F32)
+    for i in range(T):
+        ctx_i = torch.from_numpy(st["ctx"] - (T - 1 - i)).cuda()
+        one = fp8kv.decode_attention(st["d"], st["K"], st["V"], st["ks"], st["vs"],
+                                     st["q_d"][:, i].contiguous(), st["pt_d"], ctx_i,
+                                     out_dtype=fp8kv.OUT_F32)
+        torch.cuda.synchronize()
+        assert np.abs(one.cpu().numpy() - multi[:, i]).max() <= 1e-5, i
+
+
+def test_aborted_request_gives_zero_rows():
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    st = _setup(fp8kv, [20, 33, 50], 2, 8, 2)
+    ab = np.array([0, 1, 0], np.uint8)
+    o = _run(st, fp8kv.OUT_F32, abort=ab)
+    _, _, ref = _oracle(st)
+    assert (o[1] == 0).all()
+    check_outputs(o[[0, 2]], None, ref[[0, 2]])
+
+
+def test_too_many_columns_is_rejected():
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    st = _setup(fp8kv, [3], 3, 64, 8)              # G = 8, q_len = 3: 24 columns
+    assert fp8kv.decode_workspace_size_q(st["d"], 1, 64, 3) == 0
+    with pytest.raises(fp8kv.Fp8kvError) as e:
+        _run(st, fp8kv.OUT_F32)
+    assert e.value.status == -2
