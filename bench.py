@@ -250,6 +250,71 @@ def accuracy_study(args):
         "by_workload": res}), flush=True)
 
 
+def spec_study(args):
+    """q_len new tokens per request checked in one step (speculative
+    verification) on the chosen workload: tag check, append of the q_len
+    tokens, one multi-query attention launch.  The request's context after the
+    step is the workload's own (L_b + 1), so the pages read are the same as the
+    one-token step's; verified tokens per second count live requests x q_len.
+    The one-token step over the same cache is timed in the same run."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from workloads import device
+
+    cfg = {"tiny": 1, "uniform": 2, "ragged": 3, "long": 4, "capacity": 5}[args.workload]
+    cache = 0 if args.cache == "e4m3" else 1
+    w = workloads.make(cfg)
+    log(f"bench: speculative verification, workload {w.name}, q_len {args.qlen}")
+    base = device.build(w, cache_dtype=cache, num_workers=args.num_workers)
+    sp = device.build_spec(base, args.qlen)
+    sp.step(True)
+    torch.cuda.synchronize()
+    live = base.abort.cpu().numpy() == 0
+    one_bytes, one_attn = alg_bytes(w, cache, True, active=live)
+    # extra bytes of the q_len-token step: q_len-1 more Q rows and O rows per live
+    # request, q_len-1 more appended tokens (2 reads of bf16, 1 write of E per value)
+    E = 1 if cache == 0 else 2
+    nl = int(live.sum())
+    extra_qo = nl * (args.qlen - 1) * w.Hq * 128 * 2 * 2
+    extra_app = nl * (args.qlen - 1) * 2 * w.Hkv * 128 * (2 + E)
+    attn_bytes = one_attn + extra_qo
+    step_bytes = one_bytes + extra_qo + extra_app
+    for _ in range(args.warmup):
+        sp.step(True)
+        base.step(True)
+    t_spec = time_steps(lambda: sp.step(True), args.steps)
+    t_one = time_steps(lambda: base.step(True), args.steps)
+    nev = max(20, args.steps // 2)
+    td_spec, td_one = event_times([lambda: sp.decode(True), lambda: base.decode(True)], nev)
+    ta = event_times([lambda: sp.append(True)], nev)[0]
+    td_spec = statistics.median(td_spec) * 1e-3
+    td_one = statistics.median(td_one) * 1e-3
+    gbps = attn_bytes / td_spec / 1e9
+    print(json.dumps({
+        "metric": "speculative verification step: new tokens checked per second (q_len per "
+                  "request; tag check + append + multi-query attention)",
+        "value": round(nl * args.qlen / t_spec, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_spec * 1e3, 4),
+        "higher_is_better": True, "data": "synthetic",
+        "dtype": f"{args.cache} cache; bf16/f16 MFMA, f32 accumulate",
+        "config": {"workload": w.name, "requests": w.B, "live_requests": nl, "q_len": args.qlen,
+                   "q_heads": w.Hq, "kv_heads": w.Hkv, "columns": w.G * args.qlen,
+                   "head_dim": 128, "page_tokens": 16, "kv_cache": args.cache,
+                   "attended_tokens_last_query": int(w.ctx_lens.sum())},
+        "step_alg_bytes": step_bytes, "hbm_gbps": round(step_bytes / t_spec / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": "fp8kv_decode_attention_q call",
+                     "achieved": round(gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_GBPS, 4), "traffic": None,
+                     "alg_bytes_per_launch": attn_bytes, "avg_launch_us": round(td_spec * 1e6, 2)},
+        "append_us": round(statistics.median(ta) * 1e3, 2),
+        "one_token_step": {"ms_per_step": round(t_one * 1e3, 4),
+                           "tokens_s": round(nl / t_one, 1),
+                           "decode_us": round(td_one * 1e6, 2)},
+        "step_time_ratio_vs_one_token": round(t_spec / t_one, 4)}), flush=True)
+
+
 def cpu_baseline(w, target_s: float = 15.0):
     """The oracle as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -329,6 +394,9 @@ def main():
     ap.add_argument("--accuracy", action="store_true",
                     help="measure the FP8 cache's output error against the BF16 cache instead")
     ap.add_argument("--accuracy-configs", type=int, nargs="+", default=[2, 3, 4])
+    ap.add_argument("--qlen", type=int, default=1,
+                    help="q_len > 1: speculative-verification study (q_len new tokens per "
+                         "request checked in one step)")
     ap.add_argument("--loop", action="store_true",
                     help="run the multi-step decode study (tracker on vs off) instead")
     ap.add_argument("--loop-concurrency", type=int, nargs="+", default=[1, 2, 4, 8])
@@ -356,6 +424,9 @@ def main():
         return
     if args.accuracy:
         accuracy_study(args)
+        return
+    if args.qlen > 1:
+        spec_study(args)
         return
     if args.calibrate_copy:
         n = 1 << 30

@@ -149,3 +149,41 @@ def test_too_many_columns_is_rejected():
     with pytest.raises(fp8kv.Fp8kvError) as e:
         _run(st, fp8kv.OUT_F32)
     assert e.value.status == -2
+
+
+def test_ragged_64_two_queries_full_size():
+    """The 64-request ragged workload with q_len 2 (G*q_len = 16 columns), in the
+    launch configuration the speculative-verification study times: sampled
+    (request, kv-head) pairs against the oracle, and the newest query's rows
+    against the one-token decode over the same cache."""
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    import workloads
+    from workloads import device
+    T = 2
+    w = workloads.make(3)
+    st = device.build(w)
+    sp = device.build_spec(st, T)
+    o16 = sp.step(True).view(torch.int16)
+    torch.cuda.synchronize()
+    o16 = o16.cpu().numpy().view(np.uint16)
+    o32 = sp.decode(out_dtype=fp8kv.OUT_F32)
+    one = st.decode(out_dtype=fp8kv.OUT_F32)
+    torch.cuda.synchronize()
+    o32, one = o32.cpu().numpy(), one.cpu().numpy()
+    assert (st.abort.cpu().numpy() == 0).all()
+    assert np.abs(o32[:, -1] - one).max() <= 1e-6
+    q = w.q_bits_multi(T)
+    assert np.array_equal(q[:, -1], w.q_bits())
+    G, L = w.G, w.ctx_lens
+    for b, g in [(int(L.argmax()), 0), (int(L.argmin()), 7), (11, 4)]:
+        n = int(L[b])
+        K, V = oracle.new_cache(w.num_pages, 1)
+        sk, sv = st.k_scale_host[g:g + 1], st.v_scale_host[g:g + 1]
+        oracle.append(K, V, sk, sv, w.kv_tokens_head("k", b, 0, n, g)[:, None, :],
+                      w.kv_tokens_head("v", b, 0, n, g)[:, None, :], np.zeros(n, np.int32),
+                      np.arange(n, dtype=np.int32), w.page_table[b:b + 1])
+        ref, _ = oracle.attention_multi(K, V, sk, sv, q[b:b + 1, :, g * G:(g + 1) * G],
+                                        w.page_table[b:b + 1], L[b:b + 1], SM_SCALE)
+        cols = slice(g * G, (g + 1) * G)
+        err = check_outputs(o32[b, :, cols], o16[b, :, cols], ref[0])
+        print(f"ragged q_len={T} b={b} g={g} ctx={n} max abs err {err:.3e}")

@@ -84,3 +84,15 @@ def test_loop_token_streams_slice_and_backends_agree():
     # requests and tensors draw different streams
     assert not (token_bits(3, "k", 1, 0, 4, 4) == full[:4]).all()
     assert not (token_bits(3, "v", 2, 0, 4, 4) == full[:4]).all()
+
+
+def test_multi_query_stream():
+    """Speculative-verification queries: both backends agree, the newest query is
+    the one-token step's Q, and the older ones continue the same Q stream."""
+    w = workloads.make(1)
+    q = w.q_bits_multi(3)
+    assert q.shape == (w.B, 3, w.Hq, w.D)
+    assert (q.view(np.int16) == w.q_bits_multi(3, "torch", "cpu").numpy()).all()
+    assert (q[:, 2] == w.q_bits()).all()
+    assert (q[:, :2] == w.q_bits_multi(3)[:, :2]).all()
+    assert not (q[:, 0] == q[:, 2]).all()

@@ -268,6 +268,19 @@ class Workload:
         import torch
         return torch.stack(rows).view(self.B, self.Hq, self.D)
 
+    def q_bits_multi(self, q_len: int, backend: str = "numpy", device=None):
+        """BF16 bits of q_len queries per request (speculative verification),
+        shape [B][q_len][Hq][D].  Query i belongs to the new token at position
+        L_b + 1 - q_len + i and is token q_len-1-i of the request's Q stream, so
+        the newest query (i = q_len-1) is the one q_bits gives."""
+        n = self.Hq * self.D
+        rows = [draw_bits(stream_key(self.seed, _T_Q, b), 0, q_len * n, backend, device)
+                for b in range(self.B)]
+        if backend == "numpy":
+            return np.stack(rows).reshape(self.B, q_len, self.Hq, self.D)[:, ::-1].copy()
+        import torch
+        return torch.stack(rows).view(self.B, q_len, self.Hq, self.D).flip(1).contiguous()
+
     def new_kv_bits(self, which: str, backend: str = "numpy", device=None):
         """BF16 bits of the appended token (position L_b) per request, [B][Hkv][D]."""
         rows = [self.kv_tokens(which, b, int(self.ctx_before[b]), int(self.ctx_before[b]) + 1,

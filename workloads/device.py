@@ -88,6 +88,72 @@ class DeviceStep:
         return self.decode(use_abort=check_tags, out_dtype=out_dtype, stream=stream)
 
 
+@dataclasses.dataclass
+class SpecStep:
+    """A step that checks q_len new tokens per request at once (speculative
+    verification) over a DeviceStep's cache: the request's context after the
+    step is still L_b + 1, its newest q_len tokens (positions L_b+1-q_len ..
+    L_b, fewer when the context is shorter) are appended by the step, and
+    query i attends to the tokens up to its own.  Tag check and append are
+    separate launches (the fused launch appends one token per request)."""
+    base: DeviceStep
+    q_len: int
+    q: torch.Tensor             # [B][q_len][Hq][128]
+    k_new: torch.Tensor         # [rows][Hkv][128]
+    v_new: torch.Tensor
+    token_seq: torch.Tensor
+    token_pos: torch.Tensor
+    workspace: torch.Tensor
+    out: torch.Tensor
+
+    def verify(self, stream=None):
+        self.base.verify(stream)
+
+    def append(self, use_abort=True, stream=None):
+        s = self.base
+        fp8kv.append(s.desc, s.K, s.V, s.k_scale, s.v_scale, self.k_new, self.v_new,
+                     self.token_seq, self.token_pos, s.page_table,
+                     abort=s.abort if use_abort else None, stream=stream)
+
+    def decode(self, use_abort=True, out_dtype=fp8kv.OUT_BF16, stream=None):
+        s = self.base
+        out = self.out if out_dtype == fp8kv.OUT_BF16 else torch.empty(
+            self.out.shape, dtype=torch.float32, device=self.out.device)
+        return fp8kv.decode_attention_q(
+            s.desc, s.K, s.V, s.k_scale, s.v_scale, self.q, s.page_table, s.ctx_lens,
+            abort=s.abort if use_abort else None, out=out, out_dtype=out_dtype,
+            num_workers=s.num_workers, workspace=self.workspace, stream=stream)
+
+    def step(self, check_tags=True, out_dtype=fp8kv.OUT_BF16, stream=None):
+        if check_tags:
+            self.verify(stream)
+        self.append(use_abort=check_tags, stream=stream)
+        return self.decode(use_abort=check_tags, out_dtype=out_dtype, stream=stream)
+
+
+def build_spec(s: DeviceStep, q_len: int) -> SpecStep:
+    """The q_len-token step over an already built (history-filled) DeviceStep."""
+    w, dev = s.w, s.K.device
+    t0 = np.maximum(w.ctx_lens - q_len, 0)
+    t1 = w.ctx_lens
+    kn = torch.cat([w.kv_tokens("k", b, int(t0[b]), int(t1[b]), "torch", dev)
+                    for b in range(w.B)]).contiguous()
+    vn = torch.cat([w.kv_tokens("v", b, int(t0[b]), int(t1[b]), "torch", dev)
+                    for b in range(w.B)]).contiguous()
+    seq = np.repeat(np.arange(w.B, dtype=np.int32), t1 - t0)
+    pos = np.concatenate([np.arange(a, c, dtype=np.int32) for a, c in zip(t0, t1)])
+    need = fp8kv.decode_workspace_size_q(s.desc, w.B, w.Hq, q_len, s.num_workers)
+    if need == 0:
+        raise ValueError(f"{w.Hq // w.Hkv} q-heads per kv-head x q_len {q_len} exceeds the "
+                         "decode kernel's 16 columns")
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    return SpecStep(base=s, q_len=q_len, q=w.q_bits_multi(q_len, "torch", dev), k_new=kn,
+                    v_new=vn, token_seq=torch.from_numpy(seq).to(dev),
+                    token_pos=torch.from_numpy(pos).to(dev), workspace=ws,
+                    out=torch.empty((w.B, q_len, w.Hq, 128), dtype=torch.bfloat16, device=dev))
+
+
 def _bf16(t: torch.Tensor) -> torch.Tensor:
     return t.view(torch.bfloat16)
 
