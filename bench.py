@@ -137,21 +137,25 @@ def capture_graphs(st, fns):
 
 def loop_study(args):
     """Multi-step decode with the tag tracker on vs the no-op tracker: prompts of
-    8,192 tokens, 1,000 generated tokens, concurrency 1/2/4/8, one layer of the
-    ragged workload's shape (64 q-heads / 8 kv-heads).  Runs of the two modes
-    alternate; each run restarts from the prompt.  A step's latency is its wall
-    time including the host work (page allocation, tag upload, launches) and the
-    read-back of the abort flags, synchronized at the end of every step."""
+    8,192 tokens, 1,000 generated tokens, concurrency 1/2/4/8, 1 and 32 layers of
+    the ragged workload's shape (64 q-heads / 8 kv-heads), launched eagerly or as
+    one captured HIP graph per step.  Runs of the two tracker modes alternate;
+    each run restarts from the prompt.  A step's latency is its wall time
+    including the host work (page allocation, tag upload, launches or graph
+    replay) and the read-back of the abort flags, synchronized at the end of
+    every step."""
     import numpy as np
     import torch
     from workloads.decode_loop import DecodeLoop
 
     rng = np.random.default_rng(0)
     per = {}
-    for nl, c in [(nl, c) for nl in args.loop_layers for c in args.loop_concurrency]:
-        log(f"bench: decode loop, {nl} layer(s), concurrency {c}")
+    for launch, nl, c in [(g, nl, c) for g in args.loop_launch for nl in args.loop_layers
+                          for c in args.loop_concurrency]:
+        log(f"bench: decode loop, {launch} launches, {nl} layer(s), concurrency {c}")
         loops = {m: DecodeLoop(c, args.loop_prompt, args.loop_steps, tracker=(m == "on"), seed=c,
-                               step_sets=16, layers=nl) for m in ("on", "off")}
+                               step_sets=16, layers=nl, graph=(launch == "graph"))
+                 for m in ("on", "off")}
         for lp in loops.values():
             lp.run(min(20, args.loop_steps))
             lp.reset()
@@ -178,12 +182,12 @@ def loop_study(args):
             1e6 * (float(np.median(tot["on"])) - float(np.median(tot["off"]))) / args.loop_steps, 2)
         res["p95_overhead_pct"] = round(
             100 * (res["on"]["step_ms_p95"] / res["off"]["step_ms_p95"] - 1), 3)
-        per.setdefault(f"{nl}_layers", {})[str(c)] = res
+        per.setdefault(launch, {}).setdefault(f"{nl}_layers", {})[str(c)] = res
         for lp in loops.values():
             lp.close()
         del loops
         torch.cuda.empty_cache()
-    top = per[f"{args.loop_layers[0]}_layers"][str(max(args.loop_concurrency))]
+    top = per[args.loop_launch[0]][f"{args.loop_layers[0]}_layers"][str(max(args.loop_concurrency))]
     print(json.dumps({
         "metric": "decode loop (8192-token prompts, 1000 generated tokens): tokens/s and p95 "
                   "step latency, tag tracker on vs the no-op tracker",
@@ -193,9 +197,9 @@ def loop_study(args):
                    "generated_tokens": args.loop_steps, "q_heads": 64, "kv_heads": 8,
                    "head_dim": 128, "page_tokens": 16, "kv_cache": "e4m3",
                    "rounds": args.loop_rounds, "layers": args.loop_layers},
-        "value_is": f"tracker on, {args.loop_layers[0]} layer(s), concurrency "
-                    f"{max(args.loop_concurrency)}",
-        "by_layers_and_concurrency": per}), flush=True)
+        "value_is": f"tracker on, {args.loop_launch[0]} launches, {args.loop_layers[0]} "
+                    f"layer(s), concurrency {max(args.loop_concurrency)}",
+        "by_launch_layers_and_concurrency": per}), flush=True)
 
 
 def accuracy_study(args):
@@ -403,6 +407,9 @@ def main():
     ap.add_argument("--loop-prompt", type=int, default=8192)
     ap.add_argument("--loop-steps", type=int, default=1000)
     ap.add_argument("--loop-rounds", type=int, default=6)
+    ap.add_argument("--loop-launch", nargs="+", default=["graph", "eager"],
+                    choices=["graph", "eager"],
+                    help="each step replays one captured HIP graph, or launches eagerly")
     ap.add_argument("--loop-layers", type=int, nargs="+", default=[1, 32],
                     help="layers per model step (one tag check per step, attention per layer)")
     args = ap.parse_args()

@@ -960,6 +960,8 @@ constexpr int kMergeFlatThreads = 256;
 constexpr int kMergeGroupedThreads = 1024;
 // segments average at least this many pieces: the grouped form
 constexpr int kMergeGroupedMinPieces = 4;
+// workgroups per (request, kv-head) segment at most, with the default grid
+constexpr int kDefaultPiecesPerSegment = 24;
 
 // fold one piece's (max, sum, weighted V) into a running state
 __device__ __forceinline__ void merge_state(float& M, float& L, f32x4_t& O, float m, float l,
@@ -1336,7 +1338,15 @@ fp8kv_status decode_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
   a.C = G * q_len;
   a.out_f32 = out_dtype == FP8KV_OUT_F32 ? 1 : 0;
   a.sm_scale = sm_scale;
-  const int blocks = workers / kWaves;
+  const int segs = batch * desc->num_kv_heads;
+  // With the device's default grid, long segments shared by many workgroups
+  // leave the merge a long chain of pieces per segment (one request of 8k
+  // tokens: ~100), which costs more than the extra workgroups gain; the
+  // default grid is capped at kDefaultPiecesPerSegment workgroups per segment.
+  // An explicit worker count is used as given.
+  int blocks = workers / kWaves;
+  if (num_workers == 0 && static_cast<int64_t>(kDefaultPiecesPerSegment) * segs < blocks)
+    blocks = kDefaultPiecesPerSegment * segs;
   if (desc->cache_dtype == FP8KV_E4M3) {
     hipLaunchKernelGGL((decode_kernel<FP8KV_E4M3, FP8KV_DEPTH_E4M3>), dim3(blocks),
                        dim3(kThreads), 0, stream, a);
@@ -1346,7 +1356,6 @@ fp8kv_status decode_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
   }
   st = launched();
   if (st != FP8KV_OK) return st;
-  const int segs = batch * desc->num_kv_heads;
   const dim3 mgrid(segs < 1024 ? segs : 1024);
   if (blocks >= static_cast<int64_t>(kMergeGroupedMinPieces) * segs)
     hipLaunchKernelGGL(merge_grouped_kernel, mgrid, dim3(kMergeGroupedThreads), 0, stream, a,

@@ -143,3 +143,51 @@ def test_layers_share_the_page_table(fp8kv):
     ref, _ = oracle.attention(K, V, ks, vs, q, pt, np.full(B, P + T, np.int32), SM_SCALE)
     check_outputs(loop.out.cpu().numpy(), None, ref)
     loop.close()
+
+
+def _pair(fp8kv, tracker, layers=2):
+    from workloads.decode_loop import DecodeLoop
+    return [DecodeLoop(B, P, T, HQ, HKV, tracker=tracker, seed=SEED, out_dtype=fp8kv.OUT_F32,
+                       layers=layers, graph=g) for g in (False, True)]
+
+
+def _same_state(a, b):
+    assert all(x == y for x, y in zip(a.pages, b.pages))
+    for ka, kb, va, vb in zip(a.Ks, b.Ks, a.Vs, b.Vs):
+        assert torch.equal(ka, kb) and torch.equal(va, vb)
+    assert torch.equal(a.abort, b.abort)
+
+
+@pytest.mark.parametrize("tracker", [True, False])
+def test_graph_replay_gives_the_eager_bits(fp8kv, tracker):
+    """Every step replays a captured graph (two layers); each replay's output,
+    with the loop's eager host work in between, equals the eager step's."""
+    eager, graph = _pair(fp8kv, tracker)
+    for s in range(T):
+        eager.step()
+        graph.step()
+        assert torch.equal(eager.out, graph.out), s
+    _same_state(eager, graph)
+    eager.close()
+    graph.close()
+
+
+def test_graph_replay_stale_tag(fp8kv):
+    """A stale remembered tag aborts the request under graph replay too; the
+    retired request's lengths and table are changed in device memory that the
+    graph reads, and the other requests continue with the eager bits."""
+    eager, graph = _pair(fp8kv, True)
+    for lp in (eager, graph):
+        lp.run(6)
+        lp.corrupt_expected(1, 0)
+        lp.step()
+    assert list(graph.abort.cpu().numpy()) == [0, 1, 0]
+    assert graph.live == [True, False, True]
+    for s in range(T - 7):
+        eager.step()
+        graph.step()
+        assert torch.equal(eager.out, graph.out), s
+    assert (graph.out[1] == 0).all()
+    _same_state(eager, graph)
+    eager.close()
+    graph.close()

@@ -61,9 +61,13 @@ class DecodeLoop:
                  num_kv_heads: int = 8, tracker: bool = True, seed: int = 0,
                  cache_dtype: int = fp8kv.E4M3, step_sets: Optional[int] = None,
                  out_dtype: int = fp8kv.OUT_BF16, slack_pages: int = 16, layers: int = 1,
-                 device="cuda"):
+                 graph: bool = False, device="cuda"):
         """step_sets: how many distinct per-step Q/K/V sets to generate (None: one
-        per step, exact inputs; a small number cycles them, enough for timing)."""
+        per step, exact inputs; a small number cycles them, enough for timing).
+        graph: the launches of each step set (every layer's append and attention,
+        and the check) are captured once in a HIP graph and each step replays
+        one graph; host work (page allocation, table upload, read-back of the
+        abort flags) stays outside."""
         assert num_q_heads % num_kv_heads == 0
         self.B, self.P, self.T = batch, prompt_len, gen_len
         self.Hq, self.Hkv = num_q_heads, num_kv_heads
@@ -133,6 +137,8 @@ class DecodeLoop:
         self._fill_prompt()
         self.reset()
         self._launches = [self._prepare(i) for i in range(S)]
+        self.graph = graph
+        self._graphs = [self._capture(i) for i in range(S)] if graph else None
 
     # ------------------------------------------------------------------ setup
     def _take_pages(self, b: int, n: int):
@@ -200,6 +206,18 @@ class DecodeLoop:
                 prepare=True))
         return calls
 
+    def _capture(self, i: int):
+        """Step set i's launches recorded in a HIP graph.  The launches are
+        marshalled inside the capture, so they name the capturing stream; the
+        graph holds their pointers, whose contents (page table, lengths, flags)
+        each replay reads afresh."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for launch in self._prepare(i):
+                launch()
+        torch.cuda.synchronize()
+        return g
+
     # ------------------------------------------------------------------ step
     def step(self) -> float:
         """One decode step for all live requests; returns its wall time in seconds
@@ -216,8 +234,11 @@ class DecodeLoop:
                 self.pool.sync(self.tags)         # the new pages' tags
             else:
                 self.page_table.copy_(self.pt_host, non_blocking=True)
-        for launch in self._launches[s % self.step_sets]:
-            launch()
+        if self._graphs is not None:
+            self._graphs[s % self.step_sets].replay()
+        else:
+            for launch in self._launches[s % self.step_sets]:
+                launch()
         self.abort_host.copy_(self.abort, non_blocking=True)
         self.lens.add_(1)
         torch.cuda.synchronize()
