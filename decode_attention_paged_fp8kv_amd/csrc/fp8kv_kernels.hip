@@ -38,7 +38,9 @@ constexpr int kHeadDim = 128;
 constexpr int kPage = 16;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxGroup = 16;
+// (query, head) columns of one kv-head: one or two 16-column MFMA tiles
+constexpr int kTileCols = 16;
+constexpr int kMaxGroup = 2 * kTileCols;
 // word 3 of a raw buffer resource on gfx9-family parts (32-bit data, no
 // swizzle, no index stride)
 constexpr int kRsrcWord3 = 0x00020000;
@@ -55,6 +57,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 #endif
 #ifndef FP8KV_DEPTH_BF16
 #define FP8KV_DEPTH_BF16 1
+#endif
+// the same with two column tiles (2 waves per SIMD, more registers per wave)
+#ifndef FP8KV_DEPTH_E4M3_2T
+#define FP8KV_DEPTH_E4M3_2T 2
+#endif
+#ifndef FP8KV_DEPTH_BF16_2T
+#define FP8KV_DEPTH_BF16_2T 2
 #endif
 // waves per compute unit the automatic worker count aims for
 #ifndef FP8KV_WAVES_PER_CU
@@ -608,8 +617,12 @@ __device__ __forceinline__ void segment_workgroups(int64_t first, int64_t last, 
   wl = ((last + 1) * NWG - 1) / W;
 }
 
-template <int CACHE, int DEPTH>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+// NT: 16-column tiles of (query, head) pairs per kv-head (1 or 2).  Two tiles
+// double the Q fragments and accumulators, so that form runs 2 waves per SIMD
+// instead of 3; each page's K/V fragments are converted once for both tiles.
+template <int CACHE, int DEPTH, int NT>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 : 2, NT == 1 ? 3 : 2)))
 void decode_kernel(DecodeArgs a) {
   constexpr int TB = Tile<CACHE>::kBytes;
   constexpr int NC = Tile<CACHE>::kChunks;
@@ -621,11 +634,16 @@ void decode_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15;   // (query, head) of the group: the MFMA column
+  const int n = lane & 15;   // MFMA column: (query, head) pair 16*ct + n of tile ct
   const int qd = lane >> 4;  // lane quarter
   const int B = a.batch;
-  // trailing tokens of the context this column's query does not see
-  const int lag = n < a.C ? a.qlen - 1 - n / a.G : 0;
+  // trailing tokens of the context the query of column 16*ct + n does not see
+  int lag[NT];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    const int col = kTileCols * ct + n;
+    lag[ct] = col < a.C ? a.qlen - 1 - col / a.G : 0;
+  }
 
   // ---- prologue: page prefix sums of the live requests ------------------
   {
@@ -740,13 +758,19 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int s = 0; s < DEPTH; ++s) pid_ring[s] = fetch_pid();
 
-  // Q fragment (B operand of the QK^T MFMA) of a piece: lane (n, qd) holds,
-  // for step kk, q[column n][32 qd + 8 kk + i], i < 8; columns past C are 0
-  auto load_q = [&](const Piece& pc, u32x4_t (&dst)[4]) {
-    const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(
-        a.q + column_row(a, pc.b, pc.g, n < a.C ? n : 0) * kHeadDim + 32 * qd);
+  // Q fragments (B operands of the QK^T MFMA) of a piece: lane (n, qd) holds,
+  // for tile ct and step kk, q[column 16 ct + n][32 qd + 8 kk + i], i < 8;
+  // columns past C are 0
+  auto load_q = [&](const Piece& pc, u32x4_t (&dst)[NT][4]) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) dst[kk] = n < a.C ? qrow[kk] : u32x4_t{0u, 0u, 0u, 0u};
+    for (int ct = 0; ct < NT; ++ct) {
+      const int col = kTileCols * ct + n;
+      const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(
+          a.q + column_row(a, pc.b, pc.g, col < a.C ? col : 0) * kHeadDim + 32 * qd);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        dst[ct][kk] = col < a.C ? qrow[kk] : u32x4_t{0u, 0u, 0u, 0u};
+    }
   };
   Piece P = first;  // piece being processed (all waves visit every piece)
   for (;;) {
@@ -759,25 +783,34 @@ void decode_kernel(DecodeArgs a) {
     // few pieces).  Waiting at the first MFMA instead would put the wait
     // inside the page loop, where the compiler cannot count the loads issued
     // after Q and drains the prefetch every step.
-    u32x4_t qcur[4];
+    u32x4_t qcur[NT][4];
     load_q(P, qcur);
     if constexpr (CACHE == FP8KV_E4M3) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) asm volatile("" ::"v"(qcur[kk]));
+      for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) asm volatile("" ::"v"(qcur[ct][kk]));
     }
     Piece Pn = P;
     const bool has_next = next_piece(Pn, s_pre, B, a.Hkv, X1);
 
-    f32x4_t acc[8];
+    f32x4_t acc[NT][8];
+    float m_run[NT];  // running max of column 16 ct + n (log2 units)
+    float l_run[NT];  // this lane's share of the softmax denominator
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;  // running max for head n (log2 units)
-    float l_run = 0.f;        // this lane's share of the softmax denominator
+    for (int ct = 0; ct < NT; ++ct) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[ct][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      m_run[ct] = -INFINITY;
+      l_run[ct] = 0.f;
+    }
 
     if (cnt > 0) {
-      bf16x8_t qf[4];
+      bf16x8_t qf[NT][4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qf[kk] = __builtin_bit_cast(bf16x8_t, qcur[kk]);
+      for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qf[ct][kk] = __builtin_bit_cast(bf16x8_t, qcur[ct][kk]);
       // scores in log2 units: s = (q.k_code) * sm_scale * k_scale * log2(e)
       const float sc = a.sm_scale * (a.k_scale ? uniform_load(a.k_scale, P.g) : 1.0f) * kLog2e;
 
@@ -791,8 +824,10 @@ void decode_kernel(DecodeArgs a) {
           const int left = (i < cnt && okp[s]) ? ctx - page * kPage : 0;
           const int valid = min(left, kPage);
 
-          // ---- S^T = K Q^T : rows = 16 tokens, cols = 16 heads ------------
-          f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+          // ---- S^T = K Q^T : rows = 16 tokens, cols = 16 (query, head) ----
+          f32x4_t st[NT];
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) st[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
             bf16x8_t kfrag;
@@ -802,17 +837,23 @@ void decode_kernel(DecodeArgs a) {
             } else {
               kfrag = __builtin_bit_cast(bf16x8_t, kr[s][kk]);
             }
-            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[kk], st, 0, 0, 0);
-          }
-          // lane (n, qd) now holds scores of head n for tokens 4qd + r
-          float sv[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sv[r] = st[r] * sc;
+            for (int ct = 0; ct < NT; ++ct)
+              st[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[ct][kk], st[ct], 0, 0, 0);
+          }
+          // lane (n, qd) now holds scores of column n for tokens 4qd + r
+          float sv[NT][4];
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sv[ct][r] = st[ct][r] * sc;
           u32x4_t vmask = {~0u, ~0u, ~0u, ~0u};
           if (left - (a.qlen - 1) < kPage) {  // some column stops inside this page
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (4 * qd + r >= left - lag) sv[r] = -INFINITY;
+            for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (4 * qd + r >= left - lag[ct]) sv[ct][r] = -INFINITY;
             // tokens past the end may hold any bytes: clear their V so 0*x stays 0
             const int keep = min(max(valid - 4 * qd, 0), 4);  // tokens 4qd+j, j<keep
             if constexpr (CACHE == FP8KV_E4M3) {
@@ -824,46 +865,57 @@ void decode_kernel(DecodeArgs a) {
               vmask = u32x4_t{m0, m1, m0, m1};
             }
           }
-          float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-          mx = wave_max_rows(mx);
-          const float m_new = fmaxf(m_run, mx);
-          if (__any(m_new > m_run)) {
-            const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+          float p[NT][4];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) acc[t] *= alpha;
-            l_run *= alpha;
-            m_run = m_new;
+          for (int ct = 0; ct < NT; ++ct) {
+            float mx = fmaxf(fmaxf(sv[ct][0], sv[ct][1]), fmaxf(sv[ct][2], sv[ct][3]));
+            mx = wave_max_rows(mx);
+            const float m_new = fmaxf(m_run[ct], mx);
+            if (__any(m_new > m_run[ct])) {
+              const float alpha = (m_run[ct] == -INFINITY) ? 0.f : fast_exp2(m_run[ct] - m_new);
+#pragma unroll
+              for (int t = 0; t < 8; ++t) acc[ct][t] *= alpha;
+              l_run[ct] *= alpha;
+              m_run[ct] = m_new;
+            }
+            const float mref = (m_run[ct] == -INFINITY) ? 0.f : m_run[ct];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[ct][r] = fast_exp2(sv[ct][r] - mref);
+            l_run[ct] += (p[ct][0] + p[ct][1]) + (p[ct][2] + p[ct][3]);
           }
-          const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-          float p[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sv[r] - mref);
-          l_run += (p[0] + p[1]) + (p[2] + p[3]);
 
-          // ---- O^T += V^T P^T : rows = dims 8m + t (tile t), cols = heads --
+          // ---- O^T += V^T P^T : rows = dims 8m + t (tile t), cols = columns
           if constexpr (CACHE == FP8KV_E4M3) {
             // P split into two f16 terms (hi + lo) so the weights keep ~22 bits
-            f16x4_t ph, pl;
+            f16x4_t ph[NT], pl[NT];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              ph[r] = static_cast<_Float16>(p[r]);
-              pl[r] = static_cast<_Float16>(p[r] - static_cast<float>(ph[r]));
-            }
+            for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                ph[ct][r] = static_cast<_Float16>(p[ct][r]);
+                pl[ct][r] = static_cast<_Float16>(p[ct][r] - static_cast<float>(ph[ct][r]));
+              }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
               const unsigned w = vr[s][t >> 2][t & 3] & vmask[t & 3];
               const f16x4_t vfrag = e4m3x4_to_f16(w);
-              acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(vfrag, ph, acc[t], 0, 0, 0);
-              acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(vfrag, pl, acc[t], 0, 0, 0);
+#pragma unroll
+              for (int ct = 0; ct < NT; ++ct) {
+                acc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x16f16(vfrag, ph[ct], acc[ct][t], 0, 0, 0);
+                acc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x16f16(vfrag, pl[ct], acc[ct][t], 0, 0, 0);
+              }
             }
           } else {
-            s16x4_t ph, pl;
+            s16x4_t ph[NT], pl[NT];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const __bf16 h = static_cast<__bf16>(p[r]);
-              ph[r] = __builtin_bit_cast(short, h);
-              pl[r] = __builtin_bit_cast(short, static_cast<__bf16>(p[r] - static_cast<float>(h)));
-            }
+            for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const __bf16 h = static_cast<__bf16>(p[ct][r]);
+                ph[ct][r] = __builtin_bit_cast(short, h);
+                pl[ct][r] =
+                    __builtin_bit_cast(short, static_cast<__bf16>(p[ct][r] - static_cast<float>(h)));
+              }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
               const u32x4_t w = vr[s][t >> 1];
@@ -871,8 +923,11 @@ void decode_kernel(DecodeArgs a) {
               pair.x = ((t & 1) ? w.z : w.x) & vmask.x;
               pair.y = ((t & 1) ? w.w : w.y) & vmask.y;
               const s16x4_t vfrag = __builtin_bit_cast(s16x4_t, pair);
-              acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vfrag, ph, acc[t], 0, 0, 0);
-              acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vfrag, pl, acc[t], 0, 0, 0);
+#pragma unroll
+              for (int ct = 0; ct < NT; ++ct) {
+                acc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vfrag, ph[ct], acc[ct][t], 0, 0, 0);
+                acc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vfrag, pl[ct], acc[ct][t], 0, 0, 0);
+              }
             }
           }
           // refill this slot DEPTH pages ahead; its page id was fetched DEPTH
@@ -883,61 +938,66 @@ void decode_kernel(DecodeArgs a) {
       }
     }
 
-    // ---- merge the 4 waves' states for this piece through LDS -----------
-    const float l_tot = wave_sum_rows(l_run);
+    // ---- merge the 4 waves' states for this piece through LDS, one tile of
+    // columns at a time -------------------------------------------------------
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int ct = 0; ct < NT; ++ct) {
+      const float l_tot = wave_sum_rows(l_run[ct]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s_acc[wave][t * 4 + r][lane] = acc[t][r];
-    if (qd == 0) {
-      s_m[wave][n] = m_run;
-      s_l[wave][n] = l_tot;
-    }
-    lds_barrier();
-    {
-      float M = -INFINITY;
+      for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][n]);
-      float e[kWaves];
-      float L = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = s_m[w][n];
-        e[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-        L += e[w] * s_l[w][n];
+        for (int r = 0; r < 4; ++r) s_acc[wave][t * 4 + r][lane] = acc[ct][t][r];
+      if (qd == 0) {
+        s_m[wave][n] = m_run[ct];
+        s_l[wave][n] = l_tot;
       }
-      // wave `wave` merges accumulator row r = wave: dims 32 qd + 8 wave + t
-      float O[8];
+      lds_barrier();
+      {
+        float M = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        float o = 0.f;
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][n]);
+        float e[kWaves];
+        float L = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) o += e[w] * s_acc[w][t * 4 + wave][lane];
-        O[t] = o;
-      }
-      if (n < a.C) {
-        const int d0 = 32 * qd + 8 * wave;
-        if (P.ps == P.sx && P.pe == P.sx + P.n) {
-          // the whole segment sits in this slice: write the output
-          const float vsc = a.v_scale ? uniform_load(a.v_scale, P.g) : 1.0f;
-          const float inv = L > 0.f ? vsc / L : 0.f;
-          float v[8];
+        for (int w = 0; w < kWaves; ++w) {
+          const float mw = s_m[w][n];
+          e[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+          L += e[w] * s_l[w][n];
+        }
+        // wave `wave` merges accumulator row r = wave: dims 32 qd + 8 wave + t
+        float O[8];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) v[t] = O[t] * inv;
-          store_out8(a, column_row(a, P.b, P.g, n) * kHeadDim + d0, v);
-        } else {
-          const int64_t pidx = (bw + static_cast<int64_t>(P.b) * a.Hkv + P.g) * a.C + n;
-          f32x4_t* po = reinterpret_cast<f32x4_t*>(a.ws_o + pidx * kHeadDim + d0);
-          po[0] = f32x4_t{O[0], O[1], O[2], O[3]};
-          po[1] = f32x4_t{O[4], O[5], O[6], O[7]};
-          if (qd == 0 && wave == 0) {
-            a.ws_ml[pidx * 2] = M;
-            a.ws_ml[pidx * 2 + 1] = L;
+        for (int t = 0; t < 8; ++t) {
+          float o = 0.f;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) o += e[w] * s_acc[w][t * 4 + wave][lane];
+          O[t] = o;
+        }
+        const int col = kTileCols * ct + n;
+        if (col < a.C) {
+          const int d0 = 32 * qd + 8 * wave;
+          if (P.ps == P.sx && P.pe == P.sx + P.n) {
+            // the whole segment sits in this slice: write the output
+            const float vsc = a.v_scale ? uniform_load(a.v_scale, P.g) : 1.0f;
+            const float inv = L > 0.f ? vsc / L : 0.f;
+            float v[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) v[t] = O[t] * inv;
+            store_out8(a, column_row(a, P.b, P.g, col) * kHeadDim + d0, v);
+          } else {
+            const int64_t pidx = (bw + static_cast<int64_t>(P.b) * a.Hkv + P.g) * a.C + col;
+            f32x4_t* po = reinterpret_cast<f32x4_t*>(a.ws_o + pidx * kHeadDim + d0);
+            po[0] = f32x4_t{O[0], O[1], O[2], O[3]};
+            po[1] = f32x4_t{O[4], O[5], O[6], O[7]};
+            if (qd == 0 && wave == 0) {
+              a.ws_ml[pidx * 2] = M;
+              a.ws_ml[pidx * 2 + 1] = L;
+            }
           }
         }
       }
+      lds_barrier();  // LDS is reused by the next tile or piece
     }
-    lds_barrier();  // LDS is reused by the next piece
     if (!has_next) break;
     P = Pn;
   }
@@ -1056,8 +1116,8 @@ __global__ __launch_bounds__(kMergeGroupedThreads) void merge_grouped_kernel(Dec
   __shared__ f32x4_t s_o[kMergeGroupedThreads];
   const int64_t W = static_cast<int64_t>(a.Hkv) * a.ws_pre[a.batch];
   const int64_t NWG = slice_count(W, grid);
-  const int items = a.C * (kHeadDim / 4);            // (column, 4 dims) pairs, at most 512
-  const int groups = kMergeGroupedThreads / items;   // at least 2
+  const int items = a.C * (kHeadDim / 4);            // (column, 4 dims) pairs, at most 1024
+  const int groups = kMergeGroupedThreads / items;   // at least 1
   const int t = threadIdx.x;
   const bool active = t < items * groups;
   const int idx = t % items, grp = t / items;
@@ -1299,7 +1359,7 @@ fp8kv_status decode_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
     return FP8KV_INVALID_ARG;
   if (num_q_heads % desc->num_kv_heads != 0) return FP8KV_UNSUPPORTED;
   const int G = num_q_heads / desc->num_kv_heads;
-  // all (query, head) pairs of a kv-head share one 16-column MFMA tile
+  // the (query, head) pairs of a kv-head fill one or two 16-column MFMA tiles
   if (G * q_len > kMaxGroup || batch > kMaxBatch) return FP8KV_UNSUPPORTED;
   if (out_dtype != FP8KV_OUT_BF16 && out_dtype != FP8KV_OUT_F32) return FP8KV_INVALID_ARG;
   if (batch == 0) return FP8KV_OK;
@@ -1344,15 +1404,27 @@ fp8kv_status decode_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
   // tokens: ~100), which costs more than the extra workgroups gain; the
   // default grid is capped at kDefaultPiecesPerSegment workgroups per segment.
   // An explicit worker count is used as given.
+  // more than 16 (query, head) columns: two column tiles, 2 waves per SIMD
+  // instead of 3, so the default grid holds 2/3 as many workgroups
+  const bool two_tiles = a.C > kTileCols;
   int blocks = workers / kWaves;
+  if (num_workers == 0 && two_tiles) blocks = blocks / 3 * 2;
   if (num_workers == 0 && static_cast<int64_t>(kDefaultPiecesPerSegment) * segs < blocks)
     blocks = kDefaultPiecesPerSegment * segs;
   if (desc->cache_dtype == FP8KV_E4M3) {
-    hipLaunchKernelGGL((decode_kernel<FP8KV_E4M3, FP8KV_DEPTH_E4M3>), dim3(blocks),
-                       dim3(kThreads), 0, stream, a);
+    if (two_tiles)
+      hipLaunchKernelGGL((decode_kernel<FP8KV_E4M3, FP8KV_DEPTH_E4M3_2T, 2>), dim3(blocks),
+                         dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<FP8KV_E4M3, FP8KV_DEPTH_E4M3, 1>), dim3(blocks),
+                         dim3(kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((decode_kernel<FP8KV_BF16, FP8KV_DEPTH_BF16>), dim3(blocks),
-                       dim3(kThreads), 0, stream, a);
+    if (two_tiles)
+      hipLaunchKernelGGL((decode_kernel<FP8KV_BF16, FP8KV_DEPTH_BF16_2T, 2>), dim3(blocks),
+                         dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<FP8KV_BF16, FP8KV_DEPTH_BF16, 1>), dim3(blocks),
+                         dim3(kThreads), 0, stream, a);
   }
   st = launched();
   if (st != FP8KV_OK) return st;

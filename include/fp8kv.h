@@ -27,7 +27,7 @@
  *   - Nothing here is thread-safe for concurrent calls on one pool object.
  *
  * Fixed shapes: page_size 16 tokens, head_dim 128.  Hq % Hkv == 0 and the
- * group size G = Hq / Hkv is at most 16.  Q-head h reads kv-head h / G.
+ * group size G = Hq / Hkv is at most 32.  Q-head h reads kv-head h / G.
  *
  * Cache layout.  One K pool and one V pool per layer, each
  *     [num_pages][num_kv_heads][tile]
@@ -58,7 +58,7 @@ typedef int32_t fp8kv_status;
 enum {
   FP8KV_OK = 0,
   FP8KV_INVALID_ARG = -1,          /* null pointer, negative size, bad id    */
-  FP8KV_UNSUPPORTED = -2,          /* page_size != 16, head_dim != 128, G>16 */
+  FP8KV_UNSUPPORTED = -2,          /* page_size != 16, head_dim != 128, G>32 */
   FP8KV_OUT_OF_PAGES = -3,         /* pool has fewer free pages than asked   */
   FP8KV_WORKSPACE_TOO_SMALL = -4,  /* decode workspace below the query size  */
   FP8KV_HIP_ERROR = -5             /* a HIP call failed: fp8kv_last_hip_error */
@@ -265,9 +265,11 @@ fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc *desc, const void *d_
 /*   appended (fp8kv_append with q_len tokens per request); query i stands   */
 /*   for the new token at position ctx-q_len+i and attends tokens            */
 /*   0..ctx-q_len+i (causal among the new tokens; a query with no token to   */
-/*   see gives +0).  (Hq / Hkv) * q_len <= 16: the (query, head) pairs of a  */
-/*   kv-head share one 16-wide MFMA tile, so checking q_len tokens reads the */
-/*   cache once.  q_len = 1 is fp8kv_decode_attention.                        */
+/*   see gives +0).  (Hq / Hkv) * q_len <= 32: the (query, head) pairs of a  */
+/*   kv-head share one or two 16-wide MFMA tiles, so checking q_len tokens   */
+/*   reads the cache once.  Above 16 pairs the kernel runs 2 waves per SIMD  */
+/*   instead of 3.  q_len = 1 is fp8kv_decode_attention.  Larger products    */
+/*   return FP8KV_UNSUPPORTED and fp8kv_decode_workspace_size_q() 0.         */
 /*   d_workspace: at least fp8kv_decode_workspace_size_q() bytes.             */
 /* ------------------------------------------------------------------------ */
 size_t fp8kv_decode_workspace_size_q(const fp8kv_cache_desc *desc, int32_t batch,

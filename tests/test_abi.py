@@ -78,9 +78,9 @@ def test_argument_validation_before_any_device_call():
     t2 = list(args_tail)
     t2[0] = ctypes.c_int32(7)
     assert f(ctypes.byref(ok), fake, fake, fake, fake, fake, *t2) == -2
-    # G > 16
+    # G > 32
     t3 = list(args_tail)
-    t3[0] = ctypes.c_int32(34)
+    t3[0] = ctypes.c_int32(66)
     assert f(ctypes.byref(ok), fake, fake, fake, fake, fake, *t3) == -2
     # null output
     t4 = list(args_tail)
@@ -127,6 +127,20 @@ def test_workspace_size_grows_with_workers_and_batch():
     assert s1 >= slots * G * 130 * 4 + 65 * 4
     assert fp8kv.decode_num_workers(10) == 12
     assert fp8kv.decode_workspace_size(fp8kv.desc(100, 8), 4, 60, 64) == 0  # Hq % Hkv != 0
+
+
+def test_multi_query_column_limit():
+    # (Hq / Hkv) * q_len (query, head) pairs per kv-head: at most two 16-column tiles
+    d = fp8kv.desc(100, 8)
+    ws = fp8kv.decode_workspace_size_q
+    one = ws(d, 4, 64, 1, 64)
+    assert one == fp8kv.decode_workspace_size(d, 4, 64, 64)
+    assert ws(d, 4, 64, 2, 64) > one                 # 16 columns
+    assert ws(d, 4, 64, 4, 64) > ws(d, 4, 64, 3, 64)  # 32 > 24 columns
+    assert ws(d, 4, 64, 5, 64) == 0                  # 40 columns
+    assert ws(fp8kv.desc(100, 2), 4, 64, 1, 64) > 0   # G = 32
+    assert ws(fp8kv.desc(100, 2), 4, 66, 1, 64) == 0  # G = 33
+    assert ws(d, 4, 64, 0, 64) == 0                  # no query
 
 
 def test_prepared_launch_checks_once_and_keeps_its_tensors():

@@ -3,10 +3,12 @@ verification) -- fp8kv_append of the q_len new tokens, then
 fp8kv_decode_attention_q -- against the oracle's multi-query attention.
 
 Query i of a request sees the cache up to its own new token.  Covered: the
-(query, head) layouts G*q_len = 16, 12 and 5 columns, histories whose new
-tokens cross page boundaries, several work partitions, an aborted request,
-q_len = 1 against the single-query entry point (bitwise), each row against a
-one-token decode over its own prefix, and the G*q_len > 16 rejection.
+(query, head) layouts G*q_len = 16, 12 and 5 columns (one 16-column MFMA
+tile) and 24 and 32 columns and G = 32 (two tiles), both cache types,
+histories whose new tokens cross page boundaries, several work partitions, an
+aborted request, q_len = 1 against the single-query entry point (bitwise),
+each row against a one-token decode over its own prefix, and the
+G*q_len > 32 rejection.
 """
 import math
 
@@ -24,7 +26,7 @@ pytestmark = pytest.mark.gpu
 SEED = 31
 
 
-def _setup(fp8kv, hist, T, Hq, Hkv, seed=SEED):
+def _setup(fp8kv, hist, T, Hq, Hkv, seed=SEED, cache_dtype=0):
     """History of hist[b] tokens in the cache, the T new tokens appended by one
     fp8kv_append call; returns everything both sides need."""
     dev = "cuda"
@@ -42,10 +44,10 @@ def _setup(fp8kv, hist, T, Hq, Hkv, seed=SEED):
     scale = {w: scales_from_amax(np.max([np.abs(bf16_bits_to_f32(t)).max(axis=(0, 2))
                                          for t in toks[w]], axis=0)) for w in "kv"}
     q = np.stack([token_bits(seed, "q", b, 0, T, Hq) for b in range(B)])   # [B][T][Hq][128]
-    d = fp8kv.desc(N, Hkv)
+    d = fp8kv.desc(N, Hkv, cache_dtype)
     K, V = fp8kv.new_cache(d, dev)
     st = dict(fp8kv=fp8kv, d=d, K=K, V=V, pt=pt, ctx=ctx, q=q, toks=toks, scale=scale, B=B, T=T,
-              Hq=Hq, Hkv=Hkv, N=N,
+              Hq=Hq, Hkv=Hkv, N=N, cd=cache_dtype,
               ks=torch.from_numpy(scale["k"]).to(dev), vs=torch.from_numpy(scale["v"]).to(dev),
               pt_d=torch.from_numpy(pt).to(dev), ctx_d=torch.from_numpy(ctx).to(dev),
               q_d=torch.from_numpy(q.view(np.int16)).to(dev))
@@ -68,7 +70,7 @@ def _setup(fp8kv, hist, T, Hq, Hkv, seed=SEED):
 
 
 def _oracle(st, abort=None):
-    Ko, Vo = oracle.new_cache(st["N"], st["Hkv"])
+    Ko, Vo = oracle.new_cache(st["N"], st["Hkv"], st["cd"])
     for b in range(st["B"]):
         c = int(st["ctx"][b])
         if abort is not None and abort[b]:
@@ -76,9 +78,9 @@ def _oracle(st, abort=None):
         if c > 0:
             oracle.append(Ko, Vo, st["scale"]["k"], st["scale"]["v"], st["toks"]["k"][b][:c],
                           st["toks"]["v"][b][:c], np.full(c, b, np.int32),
-                          np.arange(c, dtype=np.int32), st["pt"])
+                          np.arange(c, dtype=np.int32), st["pt"], cache_dtype=st["cd"])
     ref, _ = oracle.attention_multi(Ko, Vo, st["scale"]["k"], st["scale"]["v"], st["q"], st["pt"],
-                                    st["ctx"], SM_SCALE, abort=abort)
+                                    st["ctx"], SM_SCALE, abort=abort, cache_dtype=st["cd"])
     return Ko, Vo, ref
 
 
@@ -92,7 +94,8 @@ def _run(st, out_dtype, num_workers=0, abort=None):
     return (out.view(torch.int16) if out.dtype == torch.bfloat16 else out).cpu().numpy()
 
 
-@pytest.mark.parametrize("Hq,Hkv,T", [(64, 8, 2), (8, 2, 3), (4, 4, 5)])
+@pytest.mark.parametrize("Hq,Hkv,T", [(64, 8, 2), (8, 2, 3), (4, 4, 5),
+                                      (64, 8, 3), (64, 8, 4), (64, 2, 1), (32, 2, 2), (16, 4, 5)])
 @pytest.mark.parametrize("hist", [[1, 14, 15, 30, 47, 100], [0, 13, 16, 31]])
 def test_multi_query_matches_oracle(Hq, Hkv, T, hist):
     import decode_attention_paged_fp8kv_amd as fp8kv
@@ -142,24 +145,35 @@ def test_aborted_request_gives_zero_rows():
     check_outputs(o[[0, 2]], None, ref[[0, 2]])
 
 
+@pytest.mark.parametrize("Hq,Hkv,T", [(64, 8, 4), (64, 8, 2)])
+def test_bf16_cache(Hq, Hkv, T):
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    st = _setup(fp8kv, [5, 16, 33, 70], T, Hq, Hkv, cache_dtype=fp8kv.BF16)
+    _, _, ref = _oracle(st)
+    for nw in (0, 16):
+        err = check_outputs(_run(st, fp8kv.OUT_F32, nw), _run(st, fp8kv.OUT_BF16, nw).view(np.uint16),
+                            ref)
+        print(f"bf16 cache Hq={Hq} Hkv={Hkv} T={T} workers={nw}: max abs err {err:.3e}")
+
+
 def test_too_many_columns_is_rejected():
     import decode_attention_paged_fp8kv_amd as fp8kv
-    st = _setup(fp8kv, [3], 3, 64, 8)              # G = 8, q_len = 3: 24 columns
-    assert fp8kv.decode_workspace_size_q(st["d"], 1, 64, 3) == 0
+    st = _setup(fp8kv, [3], 5, 64, 8)              # G = 8, q_len = 5: 40 columns
+    assert fp8kv.decode_workspace_size_q(st["d"], 1, 64, 5) == 0
     with pytest.raises(fp8kv.Fp8kvError) as e:
         _run(st, fp8kv.OUT_F32)
     assert e.value.status == -2
 
 
-def test_ragged_64_two_queries_full_size():
-    """The 64-request ragged workload with q_len 2 (G*q_len = 16 columns), in the
-    launch configuration the speculative-verification study times: sampled
-    (request, kv-head) pairs against the oracle, and the newest query's rows
-    against the one-token decode over the same cache."""
+@pytest.mark.parametrize("T", [2, 4])
+def test_ragged_64_full_size(T):
+    """The 64-request ragged workload with q_len 2 and 4 (G*q_len = 16 and 32
+    columns), in the launch configuration the speculative-verification study
+    times: sampled (request, kv-head) pairs against the oracle, and the newest
+    query's rows against the one-token decode over the same cache."""
     import decode_attention_paged_fp8kv_amd as fp8kv
     import workloads
     from workloads import device
-    T = 2
     w = workloads.make(3)
     st = device.build(w)
     sp = device.build_spec(st, T)

@@ -145,7 +145,7 @@ def build_spec(s: DeviceStep, q_len: int) -> SpecStep:
     need = fp8kv.decode_workspace_size_q(s.desc, w.B, w.Hq, q_len, s.num_workers)
     if need == 0:
         raise ValueError(f"{w.Hq // w.Hkv} q-heads per kv-head x q_len {q_len} exceeds the "
-                         "decode kernel's 16 columns")
+                         "decode kernel's 32 columns")
     ws = torch.zeros(need, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     return SpecStep(base=s, q_len=q_len, q=w.q_bits_multi(q_len, "torch", dev), k_new=kn,
