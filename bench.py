@@ -319,6 +319,31 @@ def spec_study(args):
         "step_time_ratio_vs_one_token": round(t_spec / t_one, 4)}), flush=True)
 
 
+def device_info():
+    """What the numbers were measured on."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2**30, 1), "hip": torch.version.hip}
+
+
+def device_copy(n_bytes: int = 2 << 30):
+    """A plain device-to-device copy of 2 GiB (torch's copy kernel): read plus
+    written bytes per second, the streaming rate a simple kernel reaches on this
+    part, beside the 8 TB/s denominator."""
+    import torch
+    x = torch.ones(n_bytes, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    t = statistics.median(event_times([lambda: y.copy_(x)], 10)[0]) * 1e-3
+    del x, y
+    torch.cuda.empty_cache()
+    return {"bytes_moved": 2 * n_bytes, "us": round(t * 1e6, 1),
+            "gbps": round(2 * n_bytes / t / 1e9, 1)}
+
+
 def cpu_baseline(w, target_s: float = 15.0):
     """The oracle as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -517,6 +542,7 @@ def main():
         "tag_check_alone_us": round(statistics.median(tv) * 1e3, 2),
         "state_copies": R,
         "launch": "hip graph replay" if args.graph else "eager",
+        "device": device_info(),
     }
     if not args.no_extras and cfg == 3:
         log("bench: tag-check overhead (interleaved on/off)")
@@ -556,6 +582,7 @@ def main():
             del c2, st2
             torch.cuda.empty_cache()
         res["uniform_32x8192"] = var
+        res["device_copy"] = device_copy()
     if not args.no_cpu_baseline and cfg == 3:
         log("bench: CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(w)

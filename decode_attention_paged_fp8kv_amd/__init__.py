@@ -7,8 +7,9 @@ is missing the import fails -- there is no fallback.
 
 Names mirror the C ABI in ``include/fp8kv.h``:
   Pool, verify_tags, append, verify_append, decode_attention,
-  decode_workspace_size, decode_num_workers, cache_offset, cache_bytes,
-  debug_convert_e4m3.
+  decode_attention_q, decode_workspace_size, decode_workspace_size_q,
+  decode_num_workers, cache_offset, cache_bytes, debug_convert_e4m3;
+  step() chains the step's calls in the order the pages give.
 """
 from __future__ import annotations
 
@@ -371,6 +372,36 @@ def decode_attention_q(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, page
     return _run(_decode_q, args, "decode_attention_q", out,
                 (d, k_cache, v_cache, k_scale, v_scale, q, page_table, ctx_lens, abort, out,
                  workspace), prepare)
+
+
+def step(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, k_new, v_new, new_pos,
+         page_table, ctx_lens, expected_tags=None, pool_tags=None, abort=None, out=None,
+         out_dtype: int = OUT_BF16, sm_scale: Optional[float] = None, num_workers: int = 0,
+         workspace=None, stream=None):
+    """One decode step of one layer in the pages' order: the tag check of every
+    page the step reads, the append of each request's new token (skipped for
+    aborted requests), then attention (+0 rows for them).  With expected_tags
+    and pool_tags the check and the append are one launch (verify_append);
+    without them this is the no-op tracker: append and attention, no check.
+    q [B][Hq][128], k_new / v_new [B][Hkv][128] BF16 bits, new_pos [B] = L_b,
+    ctx_lens [B] = L_b + 1.  Returns (out, abort); abort is None without the
+    tracker.  Page allocation and the tag upload (Pool.alloc / Pool.sync)
+    come before, on the host."""
+    if (expected_tags is None) != (pool_tags is None):
+        raise ValueError("expected_tags and pool_tags go together (both or neither)")
+    if expected_tags is not None:
+        abort = verify_append(d, k_cache, v_cache, k_scale, v_scale, k_new, v_new, new_pos,
+                              page_table, expected_tags, ctx_lens, pool_tags, abort=abort,
+                              stream=stream)
+    else:
+        seq = torch.arange(ctx_lens.shape[0], dtype=torch.int32, device=ctx_lens.device)
+        append(d, k_cache, v_cache, k_scale, v_scale, k_new, v_new, seq, new_pos, page_table,
+               stream=stream)
+        abort = None
+    out = decode_attention(d, k_cache, v_cache, k_scale, v_scale, q, page_table, ctx_lens,
+                           abort=abort, out=out, out_dtype=out_dtype, sm_scale=sm_scale,
+                           num_workers=num_workers, workspace=workspace, stream=stream)
+    return out, abort
 
 
 def debug_convert_e4m3(codes: torch.Tensor, which: int, stream=None) -> torch.Tensor:

@@ -171,6 +171,26 @@ def test_fused_equals_separate_check_and_append(lib, dev, cache_dtype):
     assert (oa == ob).all()
 
 
+@pytest.mark.parametrize("tracker", [True, False])
+def test_step_helper_equals_its_calls(lib, dev, tracker):
+    """fp8kv.step runs check + append (one launch) and attention, or without the
+    tags the no-op tracker's append and attention: the same bits as the calls."""
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    w = workloads.make(5, batch=24)
+    a = dev.build(w, num_workers=64)
+    b = dev.build(w, num_workers=64)
+    tags = dict(expected_tags=a.expected_tags, pool_tags=a.pool_tags) if tracker else {}
+    out, ab = fp8kv.step(a.desc, a.K, a.V, a.k_scale, a.v_scale, a.q, a.k_new, a.v_new,
+                         a.token_pos, a.page_table, a.ctx_lens, num_workers=64, **tags)
+    ref = b.step(check_tags=tracker)
+    assert torch.equal(out, ref)
+    assert torch.equal(a.K, b.K) and torch.equal(a.V, b.V)
+    if tracker:
+        assert (_host(ab) == w.expected_abort).all() and torch.equal(ab, b.abort)
+    else:
+        assert ab is None
+
+
 def test_empty_context_and_abort_rows_are_zero(lib, dev):
     w = workloads.custom("edge", [40, 100, 7, 300], Hq=8, Hkv=2, seed=3)
     st = dev.build(w, num_workers=8)
