@@ -525,7 +525,7 @@ def main():
                    "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": 128, "page_tokens": 16, "kv_cache": args.cache, "tag_check": True,
                    "attended_tokens": int(w.ctx_lens.sum()),
-                   "decode_waves": st.num_workers, "parallelism": "none (1 GPU)"},
+                   "decode_waves": fp8kv.decode_num_workers(st.num_workers), "parallelism": "none (1 GPU)"},
         "step_us_p50": round(p50 * 1e3, 2), "step_us_p95": round(p95 * 1e3, 2),
         "hbm_gbps": round(gbps, 1), "pct_of_8tbps": round(100 * gbps / PEAK_GBPS, 2),
         "step_alg_bytes": step_bytes,

@@ -203,7 +203,9 @@ def build(w: Workload, cache_dtype: int = fp8kv.E4M3, device="cuda", num_workers
     q = w.q_bits("torch", device).contiguous()
     k_new = w.new_kv_bits("k", "torch", device).contiguous()
     v_new = w.new_kv_bits("v", "torch", device).contiguous()
-    nw = fp8kv.decode_num_workers(num_workers)
+    # 0: the library's default grid (all workgroups resident, at most 24 per
+    # (request, kv-head), 2/3 as many for two column tiles)
+    nw = num_workers
     need = fp8kv.decode_workspace_size(d, w.B, w.Hq, nw)
     ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
     torch.cuda.synchronize()
