@@ -142,7 +142,8 @@ def test_tiny_step_parity(lib, dev, cache_dtype):
 EDGE_LENS = [0, 1, 14, 15, 16, 17, 30, 31, 32, 47, 63, 64, 65, 127, 255, 256, 300, 1023, 2100]
 
 
-@pytest.mark.parametrize("G,Hkv", [(1, 4), (2, 2), (4, 2), (8, 1), (16, 1), (8, 3)])
+@pytest.mark.parametrize("G,Hkv", [(1, 4), (2, 2), (4, 2), (8, 1), (16, 1), (8, 3), (32, 1),
+                                   (24, 2)])
 @pytest.mark.parametrize("workers", [0, 4, 12, 64, 1024])
 def test_lengths_groups_workers(lib, dev, G, Hkv, workers):
     """Few workers: slices cross many (request, kv-head) boundaries.  Many
@@ -189,6 +190,45 @@ def test_step_helper_equals_its_calls(lib, dev, tracker):
         assert (_host(ab) == w.expected_abort).all() and torch.equal(ab, b.abort)
     else:
         assert ab is None
+
+
+def test_largest_batch(lib, dev):
+    """4096 requests (the largest batch) with short contexts, 1% of them holding
+    one stale entry: every abort flag, every cache byte and every output row
+    against the oracle; one request more is rejected."""
+    rng = np.random.default_rng(4096)
+    L = rng.integers(0, 41, 4096)
+    w = workloads.custom("max_batch", L, Hq=8, Hkv=2, seed=4096, pool_slack=3)
+    for b in rng.choice(4096, 41, replace=False):
+        i = int(rng.integers(0, w.n_pages[b]))
+        w.pool_tags[w.page_table[b, i]] += np.uint32(1)      # the page was handed out again
+        w.stale[b, i] = True
+    for b in range(4096):                                    # sharers of a bumped page see it too
+        n = w.n_pages[b]
+        w.stale[b, :n] = w.expected_tags[b, :n] != w.pool_tags[w.page_table[b, :n]]
+    st = dev.build(w)
+    out16 = st.step(check_tags=True)
+    out32 = st.decode(out_dtype=lib.OUT_F32)
+    ab = _host(st.abort)
+    exp_ab = oracle.verify(w.page_table, w.expected_tags, w.ctx_lens, w.pool_tags)
+    assert (exp_ab == w.expected_abort).all() and 30 <= exp_ab.sum() <= 41
+    assert (ab == exp_ab).all()
+    Ko, Vo = oracle_state(w, st.k_scale_host, st.v_scale_host, abort=exp_ab)
+    pages = np.arange(w.num_pages)
+    assert (unswizzle(_host(st.K), w.Hkv, 0, pages, False) == Ko).all()
+    assert (unswizzle(_host(st.V), w.Hkv, 0, pages, True) == Vo).all()
+    ref, _ = oracle.attention(Ko, Vo, st.k_scale_host, st.v_scale_host, w.q_bits(), w.page_table,
+                              w.ctx_lens, SM_SCALE, abort=exp_ab)
+    o32 = _host(out32)
+    assert (o32[exp_ab == 1] == 0).all()
+    err = check_outputs(o32, _host(out16.view(torch.int16)), ref)
+    print(f"4096 requests, {int(exp_ab.sum())} aborted: max abs err {err:.3e}")
+    big = torch.zeros(4097, dtype=torch.int32, device="cuda")
+    with pytest.raises(lib.Fp8kvError) as e:
+        lib.decode_attention(st.desc, st.K, st.V, st.k_scale, st.v_scale,
+                             torch.zeros((4097, 8, 128), dtype=torch.int16, device="cuda"),
+                             torch.zeros((4097, 4), dtype=torch.int32, device="cuda"), big)
+    assert e.value.status == -2
 
 
 def test_empty_context_and_abort_rows_are_zero(lib, dev):
