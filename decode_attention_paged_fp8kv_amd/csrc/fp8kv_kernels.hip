@@ -1016,7 +1016,8 @@ void decode_kernel(DecodeArgs a) {
 // release/acquire per piece, which on this part writes back and invalidates
 // the L2 and costs far more than this launch.
 constexpr int kMergeUnroll = 8;
-constexpr int kMergeFlatThreads = 256;
+// flat form: a thread per (column, 4 dims) pair, 256 to 1024 threads (C*32)
+constexpr int kMergeFlatMaxThreads = 1024;
 constexpr int kMergeGroupedThreads = 1024;
 // segments average at least this many pieces: the grouped form
 constexpr int kMergeGroupedMinPieces = 4;
@@ -1092,13 +1093,14 @@ __device__ __forceinline__ bool segment_span(const DecodeArgs& a, int seg, int64
   return wf != wl;
 }
 
-__global__ __launch_bounds__(kMergeFlatThreads) void merge_flat_kernel(DecodeArgs a, int64_t grid) {
+__global__ __launch_bounds__(kMergeFlatMaxThreads) void merge_flat_kernel(DecodeArgs a,
+                                                                          int64_t grid) {
   const int64_t W = static_cast<int64_t>(a.Hkv) * a.ws_pre[a.batch];
   const int64_t NWG = slice_count(W, grid);
   for (int seg = blockIdx.x; seg < a.batch * a.Hkv; seg += gridDim.x) {
     int64_t wf, wl;
     if (!segment_span(a, seg, W, NWG, wf, wl)) continue;
-    for (int idx = threadIdx.x; idx < a.C * (kHeadDim / 4); idx += kMergeFlatThreads) {
+    for (int idx = threadIdx.x; idx < a.C * (kHeadDim / 4); idx += blockDim.x) {
       const int n = idx / (kHeadDim / 4);
       const int d = 4 * (idx % (kHeadDim / 4));
       float M = -INFINITY, L = 0.f;
@@ -1428,12 +1430,16 @@ fp8kv_status decode_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
   }
   st = launched();
   if (st != FP8KV_OK) return st;
+  // at least 256 threads, one per (column, 4 dims) pair up to 1024
+  const int pairs = a.C * (kHeadDim / 4);
+  const int flat_threads =
+      pairs < 256 ? 256 : (pairs > kMergeFlatMaxThreads ? kMergeFlatMaxThreads : pairs);
   const dim3 mgrid(segs < 1024 ? segs : 1024);
   if (blocks >= static_cast<int64_t>(kMergeGroupedMinPieces) * segs)
     hipLaunchKernelGGL(merge_grouped_kernel, mgrid, dim3(kMergeGroupedThreads), 0, stream, a,
                        static_cast<int64_t>(blocks));
   else
-    hipLaunchKernelGGL(merge_flat_kernel, mgrid, dim3(kMergeFlatThreads), 0, stream, a,
+    hipLaunchKernelGGL(merge_flat_kernel, mgrid, dim3(flat_threads), 0, stream, a,
                        static_cast<int64_t>(blocks));
   return launched();
 }
