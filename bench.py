@@ -319,6 +319,60 @@ def spec_study(args):
         "step_time_ratio_vs_one_token": round(t_spec / t_one, 4)}), flush=True)
 
 
+def shared_study(args):
+    """Cache reuse: 64 requests continuing one 16,384-token prompt (U[16, 2048]
+    own tokens each), the prompt's pages mapped by every request (shared) vs a
+    private copy per request.  Same values, lengths and work partition, so the
+    outputs are bit-identical; what changes is how many distinct bytes the
+    step reads.  Step = fused check + append, then attention."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from workloads import device
+
+    res = {}
+    for shared in (True, False):
+        w = workloads.shared_prefix(shared=shared)
+        log(f"bench: {w.name}")
+        st = device.build(w)
+        st.step(check_tags=True)
+        torch.cuda.synchronize()
+        live = st.abort.cpu().numpy() == 0
+        step_bytes, attn_bytes = alg_bytes(w, 0, True, active=live)
+        # distinct K/V bytes: the shared prompt once, every request's own tokens
+        own = (w.ctx_lens - w.prefix_len).astype(np.int64)
+        kv_tok = int(own[live].sum()) + (w.prefix_len if shared else w.prefix_len * int(live.sum()))
+        unique_kv = 2 * w.Hkv * 128 * kv_tok
+        for _ in range(args.warmup):
+            st.step(check_tags=True)
+        t = time_steps(lambda: st.step(check_tags=True), args.steps)
+        td = statistics.median(event_times([lambda: st.decode(True)], max(20, args.steps // 2))[0]) * 1e-3
+        res["shared" if shared else "private"] = {
+            "workload": w.name, "pool_pages": w.num_pages, "ms_per_step": round(t * 1e3, 4),
+            "tokens_s": round(int(live.sum()) / t, 1), "decode_us": round(td * 1e6, 2),
+            "alg_bytes_per_decode": attn_bytes,
+            "alg_gbps": round(attn_bytes / td / 1e9, 1),
+            "distinct_kv_bytes": unique_kv,
+            "distinct_kv_gbps": round(unique_kv / td / 1e9, 1)}
+        res["out_" + ("shared" if shared else "private")] = st.decode(True, out_dtype=1).clone()
+        del st
+        torch.cuda.empty_cache()
+    same = bool(torch.equal(res.pop("out_shared"), res.pop("out_private")))
+    sh, pr = res["shared"], res["private"]
+    print(json.dumps({
+        "metric": "shared-prompt decode step (64 requests, one 16,384-token prompt mapped by all "
+                  "+ U[16, 2048] own tokens): tokens/s, shared pages vs private copies",
+        "value": sh["tokens_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "data": "synthetic",
+        "dtype": "e4m3 cache; bf16/f16 MFMA, f32 accumulate",
+        "config": {"workload": sh["workload"], "requests": 64, "prompt_tokens": 16384,
+                   "q_heads": 64, "kv_heads": 8, "head_dim": 128, "page_tokens": 16,
+                   "kv_cache": "e4m3", "tag_check": True},
+        "shared": sh, "private": pr, "step_speedup": round(pr["ms_per_step"] / sh["ms_per_step"], 3),
+        "outputs_bit_identical": same}), flush=True)
+
+
 def device_info():
     """What the numbers were measured on."""
     import torch
@@ -423,6 +477,8 @@ def main():
     ap.add_argument("--accuracy", action="store_true",
                     help="measure the FP8 cache's output error against the BF16 cache instead")
     ap.add_argument("--accuracy-configs", type=int, nargs="+", default=[2, 3, 4])
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="cache reuse study: a prompt's pages shared by 64 requests vs copies")
     ap.add_argument("--qlen", type=int, default=1,
                     help="q_len > 1: speculative-verification study (q_len new tokens per "
                          "request checked in one step)")
@@ -459,6 +515,9 @@ def main():
         return
     if args.qlen > 1:
         spec_study(args)
+        return
+    if args.shared_prefix:
+        shared_study(args)
         return
     if args.calibrate_copy:
         n = 1 << 30

@@ -109,3 +109,43 @@ def test_shared_prefix_decode_and_isolation():
                            tags_d)
     assert ab.cpu().numpy().tolist() == [1, 0]
     pool.close()
+
+
+def test_shared_prompt_workload_full_size():
+    """64 requests continuing one 16,384-token prompt whose pages all of them map:
+    abort flags clear, sampled (request, kv-head) pairs against the oracle (the
+    prompt regenerated once per pair), and outputs bit-identical to the same
+    requests holding private copies of the prompt (same values, lengths and
+    work partition)."""
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    import workloads
+    from workloads import device
+    outs = {}
+    for shared in (True, False):
+        w = workloads.shared_prefix(shared=shared)
+        st = device.build(w)
+        st.step(check_tags=True)
+        outs[shared] = st.decode(True, out_dtype=fp8kv.OUT_F32)
+        torch.cuda.synchronize()
+        assert (st.abort.cpu().numpy() == 0).all()
+        if shared:
+            assert len(np.unique(w.page_table[:, :1024])) == 1024
+            ws, sts = w, st
+        else:
+            del st
+    assert torch.equal(outs[True], outs[False])
+    w, st = ws, sts
+    o32 = outs[True].cpu().numpy()
+    q = w.q_bits()
+    G = w.G
+    for b, g in [(0, 0), (37, 5), (63, 7)]:
+        n = int(w.ctx_lens[b])
+        K, V = oracle.new_cache(w.num_pages, 1)
+        sk, sv = st.k_scale_host[g:g + 1], st.v_scale_host[g:g + 1]
+        oracle.append(K, V, sk, sv, w.kv_tokens_head("k", b, 0, n, g)[:, None, :],
+                      w.kv_tokens_head("v", b, 0, n, g)[:, None, :], np.zeros(n, np.int32),
+                      np.arange(n, dtype=np.int32), w.page_table[b:b + 1])
+        ref, _ = oracle.attention(K, V, sk, sv, q[b:b + 1, g * G:(g + 1) * G], w.page_table[b:b + 1],
+                                  w.ctx_lens[b:b + 1], SM_SCALE)
+        err = check_outputs(o32[b, g * G:(g + 1) * G], None, ref[0])
+        print(f"shared prompt b={b} g={g} ctx={n}: max abs err {err:.3e}")

@@ -96,3 +96,25 @@ def test_multi_query_stream():
     assert (q[:, 2] == w.q_bits()).all()
     assert (q[:, :2] == w.q_bits_multi(3)[:, :2]).all()
     assert not (q[:, 0] == q[:, 2]).all()
+
+
+def test_shared_prompt_workload():
+    """A common prompt: one stream for tokens below prefix_len in every request
+    (both backends, whole-token and per-head generators), own streams after it;
+    shared pages are one set of ids with one tag, the private twin has distinct
+    pages and the same lengths."""
+    w = workloads.shared_prefix(B=5, prefix_len=48, suffix_max=40, Hq=8, Hkv=2)
+    p = workloads.shared_prefix(B=5, prefix_len=48, suffix_max=40, Hq=8, Hkv=2, shared=False)
+    assert (w.ctx_before == p.ctx_before).all() and (w.ctx_before >= 48 + 16).all()
+    assert (w.page_table[:, :3] == w.page_table[0, :3]).all()
+    assert (w.expected_tags[:, :3] == w.expected_tags[0, :3]).all()
+    used = w.page_table[w.page_table >= 0]
+    assert len(np.unique(used)) == w.num_pages == 3 + int((w.n_pages - 3).sum())
+    pu = p.page_table[p.page_table >= 0]
+    assert len(np.unique(pu)) == pu.size == p.num_pages
+    assert (w.kv_tokens("v", 0, 0, 48) == w.kv_tokens("v", 4, 0, 48)).all()
+    assert not (w.kv_tokens("v", 0, 48, 60) == w.kv_tokens("v", 4, 48, 60)).all()
+    full = w.kv_tokens("k", 3, 0, int(w.ctx_lens[3]))
+    assert (full == p.kv_tokens("k", 3, 0, int(w.ctx_lens[3]))).all()
+    assert (full.view(np.int16) == w.kv_tokens("k", 3, 0, int(w.ctx_lens[3]), "torch", "cpu").numpy()).all()
+    assert (w.kv_tokens_head("k", 3, 40, 60, 1) == full[40:60, 1]).all()

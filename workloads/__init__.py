@@ -41,6 +41,7 @@ _C2 = 0x846CA68B
 
 # tensor ids that key the streams
 _T_Q, _T_K, _T_V = 1, 2, 3
+_PREFIX_ROW = 1 << 24   # stream row of a common prompt (requests are rows 0..B-1)
 
 
 def _build_normal_table() -> np.ndarray:
@@ -188,6 +189,10 @@ class Workload:
     saturate_new: bool = False    # overwrite 4 values of the appended token with +-25
     D: int = D_HEAD
     S: int = PAGE
+    # tokens [0, prefix_len) of every request are one common stream (a shared
+    # prompt); prefix_shared: their pages are the same physical pages for all
+    prefix_len: int = 0
+    prefix_shared: bool = False
 
     @property
     def G(self) -> int:
@@ -218,6 +223,20 @@ class Workload:
     def _kv_key(self, which: str, b: int) -> int:
         return stream_key(self.seed, _T_K if which == "k" else _T_V, b)
 
+    def _prefix_key(self, which: str) -> int:
+        return stream_key(self.seed, _T_K if which == "k" else _T_V, _PREFIX_ROW)
+
+    def _split(self, t0: int, t1: int):
+        """[t0, t1) as (key row, start, end) runs: the common prefix stream, then
+        the request's own stream (its counters keep their token positions)."""
+        p = self.prefix_len
+        runs = []
+        if t0 < min(t1, p):
+            runs.append((True, t0, min(t1, p)))
+        if max(t0, p) < t1:
+            runs.append((False, max(t0, p), t1))
+        return runs
+
     def kv_tokens(self, which: str, b: int, t0: int, t1: int,
                   backend: str = "numpy", device=None, with_saturation=True):
         """BF16 bits of K or V for request b, tokens [t0, t1), shape [t][Hkv][D].
@@ -226,8 +245,16 @@ class Workload:
         for saturation, 4 values of that token in kv-head 0 are replaced by
         +-25 after scale calibration (they are excluded from amax)."""
         per_tok = self.Hkv * self.D
-        bits = draw_bits(self._kv_key(which, b), t0 * per_tok, (t1 - t0) * per_tok,
-                         backend, device, self.outlier_per_65536)
+        parts = [draw_bits(self._prefix_key(which) if pre else self._kv_key(which, b),
+                           a * per_tok, (c - a) * per_tok, backend, device, self.outlier_per_65536)
+                 for pre, a, c in self._split(t0, t1)]
+        if len(parts) == 1:
+            bits = parts[0]
+        elif backend == "numpy":
+            bits = np.concatenate(parts)
+        else:
+            import torch
+            bits = torch.cat(parts)
         if backend == "numpy":
             bits = bits.reshape(t1 - t0, self.Hkv, self.D)
         else:
@@ -246,11 +273,14 @@ class Workload:
                        with_saturation=True) -> np.ndarray:
         """The same bits as kv_tokens(...)[:, g, :] (numpy), generated for one
         kv-head only: shape [t][D]."""
-        t = np.arange(t0, t1, dtype=np.uint64)[:, None]
         d = np.arange(self.D, dtype=np.uint64)[None, :]
-        ctr = (t * np.uint64(self.Hkv) + np.uint64(g)) * np.uint64(self.D) + d
-        bits = draw_bits_at(self._kv_key(which, b), ctr.ravel(), self.outlier_per_65536)
-        bits = bits.reshape(t1 - t0, self.D)
+        parts = []
+        for pre, a, c in self._split(t0, t1):
+            t = np.arange(a, c, dtype=np.uint64)[:, None]
+            ctr = (t * np.uint64(self.Hkv) + np.uint64(g)) * np.uint64(self.D) + d
+            key = self._prefix_key(which) if pre else self._kv_key(which, b)
+            parts.append(draw_bits_at(key, ctr.ravel(), self.outlier_per_65536))
+        bits = (np.concatenate(parts) if parts else np.zeros(0, np.uint16)).reshape(t1 - t0, self.D)
         L = int(self.ctx_before[b])
         if with_saturation and self.saturate_new and g == 0 and t0 <= L < t1:
             for dd, sgn in zip((5, 40, 77, 120), (0, 0x8000, 0, 0x8000)):
@@ -391,6 +421,41 @@ def make(config: int, seed: Optional[int] = None, *, stale_mode: str = "entries"
     return Workload(name=name, seed=seed, B=B, Hq=Hq, Hkv=Hkv, ctx_before=L.astype(np.int32),
                     num_pages=pool, page_table=pt, expected_tags=etag, pool_tags=tags,
                     stale=stale, outlier_per_65536=outl, saturate_new=sat)
+
+
+def shared_prefix(B: int = 64, prefix_len: int = 16384, suffix_max: int = 2048, Hq: int = 64,
+                  Hkv: int = 8, seed: int = 6, shared: bool = True) -> Workload:
+    """B requests continuing one common prompt of prefix_len tokens (a multiple of
+    16), each with its own U[16, suffix_max] tokens after it.  shared: the
+    prefix's pages are one set of physical pages mapped by every request (one
+    holder each, the same tags); otherwise every request holds its own copy of
+    the same values (the baseline without cache reuse).  Suffix lengths and the
+    values do not depend on `shared`."""
+    assert prefix_len % PAGE == 0
+    rng = np.random.Generator(np.random.PCG64(seed))
+    L = (prefix_len + rng.integers(16, suffix_max, size=B, endpoint=True)).astype(np.int32)
+    n_pages = (L + 1 + PAGE - 1) // PAGE
+    P0 = prefix_len // PAGE
+    own = n_pages - P0 if shared else n_pages
+    pool = int(own.sum()) + (P0 if shared else 0)
+    perm = rng.permutation(pool).astype(np.int32)
+    pt = np.full((B, int(n_pages.max())), -1, np.int32)
+    off = 0
+    if shared:
+        pt[:, :P0] = perm[:P0]
+        off = P0
+    for b in range(B):
+        k = int(own[b])
+        pt[b, int(n_pages[b]) - k: int(n_pages[b])] = perm[off: off + k]
+        off += k
+    tags = rng.integers(0, 2**32, size=pool, dtype=np.uint64).astype(np.uint32)
+    etag = np.zeros(pt.shape, np.uint32)
+    used = pt >= 0
+    etag[used] = tags[pt[used]]
+    name = f"{'shared' if shared else 'private'}_prefix_{B}x{prefix_len}"
+    return Workload(name=name, seed=seed, B=B, Hq=Hq, Hkv=Hkv, ctx_before=L, num_pages=pool,
+                    page_table=pt, expected_tags=etag, pool_tags=tags,
+                    stale=np.zeros(pt.shape, bool), prefix_len=prefix_len, prefix_shared=shared)
 
 
 def custom(name: str, ctx_before, Hq: int, Hkv: int, seed: int = 7,
