@@ -323,8 +323,10 @@ def shared_study(args):
     """Cache reuse: 64 requests continuing one 16,384-token prompt (U[16, 2048]
     own tokens each), the prompt's pages mapped by every request (shared) vs a
     private copy per request.  Same values, lengths and work partition, so the
-    outputs are bit-identical; what changes is how many distinct bytes the
-    step reads.  Step = fused check + append, then attention."""
+    plain call's outputs are bit-identical; what changes is how many distinct
+    bytes the step reads.  With shared pages the shared-prompt call also reads
+    each of the prompt's pages once for the whole batch.  Step = fused check +
+    append, then attention."""
     import numpy as np
     import torch
 
@@ -356,20 +358,52 @@ def shared_study(args):
             "distinct_kv_bytes": unique_kv,
             "distinct_kv_gbps": round(unique_kv / td / 1e9, 1)}
         res["out_" + ("shared" if shared else "private")] = st.decode(True, out_dtype=1).clone()
+        if shared:
+            # the shared-prompt call: the prompt's pages once for the whole batch
+            import decode_attention_paged_fp8kv_amd as fp8kv
+            P0 = w.prefix_len // 16
+            pp = st.page_table[0, :P0].contiguous()
+            ws = torch.zeros(fp8kv.decode_workspace_size_shared(st.desc, w.B, w.Hq, w.prefix_len),
+                             dtype=torch.uint8, device="cuda")
+            call = fp8kv.decode_attention_shared(st.desc, st.K, st.V, st.k_scale, st.v_scale,
+                                                 st.q, pp, w.prefix_len, st.page_table,
+                                                 st.ctx_lens, abort=st.abort, workspace=ws,
+                                                 prepare=True)
+
+            def cstep():
+                st.verify_append()
+                call()
+            for _ in range(args.warmup):
+                cstep()
+            tc = time_steps(cstep, args.steps)
+            tdc = statistics.median(event_times([call], max(20, args.steps // 2))[0]) * 1e-3
+            res["shared_call"] = {
+                "ms_per_step": round(tc * 1e3, 4), "tokens_s": round(int(live.sum()) / tc, 1),
+                "decode_us": round(tdc * 1e6, 2), "alg_gbps": round(attn_bytes / tdc / 1e9, 1),
+                "distinct_kv_gbps": round(unique_kv / tdc / 1e9, 1)}
+            out_c = fp8kv.decode_attention_shared(st.desc, st.K, st.V, st.k_scale, st.v_scale,
+                                                  st.q, pp, w.prefix_len, st.page_table,
+                                                  st.ctx_lens, abort=st.abort, out_dtype=1,
+                                                  workspace=ws)
+            res["shared_call"]["max_abs_diff_vs_plain_call"] = float(
+                (out_c - res["out_shared"]).abs().max())
         del st
         torch.cuda.empty_cache()
     same = bool(torch.equal(res.pop("out_shared"), res.pop("out_private")))
-    sh, pr = res["shared"], res["private"]
+    sh, pr, sc = res["shared"], res["private"], res["shared_call"]
     print(json.dumps({
         "metric": "shared-prompt decode step (64 requests, one 16,384-token prompt mapped by all "
                   "+ U[16, 2048] own tokens): tokens/s, shared pages vs private copies",
-        "value": sh["tokens_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "value": sc["tokens_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "higher_is_better": True, "data": "synthetic",
         "dtype": "e4m3 cache; bf16/f16 MFMA, f32 accumulate",
         "config": {"workload": sh["workload"], "requests": 64, "prompt_tokens": 16384,
                    "q_heads": 64, "kv_heads": 8, "head_dim": 128, "page_tokens": 16,
                    "kv_cache": "e4m3", "tag_check": True},
-        "shared": sh, "private": pr, "step_speedup": round(pr["ms_per_step"] / sh["ms_per_step"], 3),
+        "value_is": "shared pages, shared-prompt call (fp8kv_decode_attention_shared)",
+        "shared_call": sc, "shared": sh, "private": pr,
+        "step_speedup_shared_pages": round(pr["ms_per_step"] / sh["ms_per_step"], 3),
+        "step_speedup_shared_call": round(pr["ms_per_step"] / sc["ms_per_step"], 3),
         "outputs_bit_identical": same}), flush=True)
 
 

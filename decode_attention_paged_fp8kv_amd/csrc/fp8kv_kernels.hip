@@ -439,9 +439,16 @@ struct DecodeArgs {
   float* ws_o;     // [slots][C][128] unnormalised weighted V
   float* ws_ml;    // [slots][C][2]   (max in log2 units, sum)
   int32_t* ws_pre; // [B+1] page prefix sums of live requests
+  // log2-sum-exp of each written output row ([B][qlen][Hq], -inf for +0 rows),
+  // or null: what a caller needs to merge these rows with attention over
+  // other tokens
+  float* lse;
   int64_t page_stride;
-  // qlen: new tokens (queries) per request; C = G * qlen MFMA columns used
-  int32_t batch, max_pages, num_pages, Hq, Hkv, G, qlen, C, out_f32;
+  // qlen: new tokens (queries) per request; C = G * qlen MFMA columns used.
+  // The page table is read from column 0 with row stride pt_stride, max_pages
+  // columns at most; its first page holds token tok0 of the request (ctx_lens
+  // count from token 0), so tok0 > 0 views a table past some leading pages.
+  int32_t batch, max_pages, pt_stride, tok0, num_pages, Hq, Hkv, G, qlen, C, out_f32;
   float sm_scale;
 };
 
@@ -480,7 +487,7 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ int live_pages(const DecodeArgs& a, int b) {
   // the flag is loaded next to the length (without an abort array, from a
   // byte of the length itself, and ignored), not after it
-  const int ctx = a.ctx_lens[b];
+  const int ctx = a.ctx_lens[b] - a.tok0;
   const uint8_t flag =
       *(a.abort ? a.abort + b : reinterpret_cast<const uint8_t*>(a.ctx_lens + b));
   const int n = ctx > 0 ? (ctx + kPage - 1) / kPage : 0;
@@ -699,6 +706,9 @@ void decode_kernel(DecodeArgs a) {
         else
           static_cast<uint16_t*>(a.out)[base + i] = 0;
       }
+      if (a.lse)
+        for (int i = threadIdx.x; i < a.qlen * a.Hq; i += kThreads)
+          a.lse[static_cast<int64_t>(b) * a.qlen * a.Hq + i] = -INFINITY;
     }
   }
 
@@ -725,7 +735,7 @@ void decode_kernel(DecodeArgs a) {
     // a vector load: it retires right after the page loads issued before it,
     // which are waited for first anyway (page ids through the scalar cache
     // measured slower: 12 waves per CU contend for it)
-    if (J.real()) pid = a.page_table[static_cast<int64_t>(J.p.b) * a.max_pages + J.page(wave)];
+    if (J.real()) pid = a.page_table[static_cast<int64_t>(J.p.b) * a.pt_stride + J.page(wave)];
     J.advance(s_pre, B, a.Hkv, X1, wave);
     return pid;
   };
@@ -777,7 +787,7 @@ void decode_kernel(DecodeArgs a) {
     const int cnt = wave_count(P, wave);
     const int iters = (cnt + DEPTH - 1) / DEPTH * DEPTH;
     const int pg0 = static_cast<int>(P.ps - P.sx) + wave;  // my first page in the piece
-    const int ctx = uniform_load(a.ctx_lens, P.b);
+    const int ctx = uniform_load(a.ctx_lens, P.b) - a.tok0;
     // Q is waited for here, once per piece: vector loads retire in order, so
     // this also waits for the pages already in flight (a slice holds only a
     // few pieces).  Waiting at the first MFMA instead would put the wait
@@ -984,6 +994,8 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) v[t] = O[t] * inv;
             store_out8(a, column_row(a, P.b, P.g, col) * kHeadDim + d0, v);
+            if (a.lse && qd == 0 && wave == 0)
+              a.lse[column_row(a, P.b, P.g, col)] = L > 0.f ? M + __log2f(L) : -INFINITY;
           } else {
             const int64_t pidx = (bw + static_cast<int64_t>(P.b) * a.Hkv + P.g) * a.C + col;
             f32x4_t* po = reinterpret_cast<f32x4_t*>(a.ws_o + pidx * kHeadDim + d0);
@@ -1062,9 +1074,10 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int64_t seg, i
 }
 
 __device__ __forceinline__ void merge_store(const DecodeArgs& a, int b, int g, int n, int d,
-                                            float L, f32x4_t O) {
+                                            float M, float L, f32x4_t O) {
   const float vsc = a.v_scale ? a.v_scale[g] : 1.0f;
   const float inv = L > 0.f ? vsc / L : 0.f;
+  if (a.lse && d == 0) a.lse[column_row(a, b, g, n)] = L > 0.f ? M + __log2f(L) : -INFINITY;
   const int64_t io = column_row(a, b, g, n) * kHeadDim + d;
   if (a.out_f32) {
     *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + io) = O * inv;
@@ -1106,7 +1119,7 @@ __global__ __launch_bounds__(kMergeFlatMaxThreads) void merge_flat_kernel(Decode
       float M = -INFINITY, L = 0.f;
       f32x4_t O = {0.f, 0.f, 0.f, 0.f};
       merge_pieces(a, seg, n, d, wf, wl + 1, M, L, O);
-      merge_store(a, seg / a.Hkv, seg % a.Hkv, n, d, L, O);
+      merge_store(a, seg / a.Hkv, seg % a.Hkv, n, d, M, L, O);
     }
   }
 }
@@ -1141,9 +1154,251 @@ __global__ __launch_bounds__(kMergeGroupedThreads) void merge_grouped_kernel(Dec
     if (active && grp == 0) {
       for (int k = 1; k < groups; ++k)
         merge_state(M, L, O, s_m[k * items + idx], s_l[k * items + idx], s_o[k * items + idx]);
-      merge_store(a, seg / a.Hkv, seg % a.Hkv, n, d, L, O);
+      merge_store(a, seg / a.Hkv, seg % a.Hkv, n, d, M, L, O);
     }
     __syncthreads();  // LDS is reused for the next segment
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 6. a prompt shared by every request of the batch (cache reuse)
+// ---------------------------------------------------------------------------
+// When all requests continue one prompt whose pages they all map, each of
+// those pages is read once per kv-head for the whole batch: the MFMA columns
+// are the (request, q-head) pairs of the kv-head (B*G of them, 16 per wave),
+// so the prompt part is a dense product instead of B separate reads.  A
+// workgroup takes 4 column tiles (one per wave) and a range of the prompt's
+// pages; its waves read the same pages at the same time, which the caches
+// serve once.  Each (column, page range) leaves (max, sum, weighted V) for
+// the combine pass.  The requests' own tokens go through decode_kernel over
+// the rest of their tables, with its log-sum-exp output.
+struct PrefixArgs {
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const uint16_t* q;           // [B][Hq][128]
+  const int32_t* prefix_pages; // [P0]
+  float* ws_o;                 // [S][B*Hq][128]
+  float* ws_ml;                // [S][B*Hq][2]
+  int64_t page_stride;
+  int32_t batch, Hq, Hkv, G, P0, S, tiles, blocks, num_pages;
+  float sm_scale;
+};
+
+template <int CACHE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void prefix_kernel(PrefixArgs a) {
+  constexpr int TB = Tile<CACHE>::kBytes;
+  constexpr int NC = Tile<CACHE>::kChunks;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, qd = lane >> 4;
+  // workgroup -> (kv-head g, page range s, column block): the blocks reading
+  // the same pages are Hkv*S apart, so with Hkv*S a multiple of 8 they land on
+  // one XCD (workgroups go round robin over the 8) and share its L2
+  const int gs = blockIdx.x % (a.Hkv * a.S);
+  const int blk = blockIdx.x / (a.Hkv * a.S);
+  const int g = gs / a.S, s = gs % a.S;
+  const int tile = blk * kWaves + wave;
+  if (tile >= a.tiles) return;  // no barrier in this kernel
+  const int cols = a.batch * a.G;
+  const int col = tile * kTileCols + n;
+  const int b = col / a.G;
+  const int64_t row = static_cast<int64_t>(b) * a.Hq + g * a.G + (col - b * a.G);
+  bf16x8_t qf[4];
+  {
+    const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(a.q + (col < cols ? row : 0) * kHeadDim +
+                                                           32 * qd);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8_t, col < cols ? qrow[kk] : u32x4_t{0u, 0u, 0u, 0u});
+  }
+  const int p0 = static_cast<int>(static_cast<int64_t>(s) * a.P0 / a.S);
+  const int p1 = static_cast<int>(static_cast<int64_t>(s + 1) * a.P0 / a.S);
+  const float sc = a.sm_scale * (a.k_scale ? uniform_load(a.k_scale, g) : 1.0f) * kLog2e;
+
+  // pages in flight (4 or 6 measured no faster: this kernel is bound by its
+  // per-page arithmetic, not by load latency)
+  constexpr int R = 2;
+  u32x4_t kr[R][NC], vr[R][NC];
+  bool okp[R];
+  auto issue = [&](int slot, int p) {
+    const int pid = p < p1 ? uniform_load(a.prefix_pages, p) : -1;
+    const bool ok = static_cast<unsigned>(pid) < static_cast<unsigned>(a.num_pages);
+    const int64_t off = ok ? static_cast<int64_t>(pid) * a.page_stride + static_cast<int64_t>(g) * TB : 0;
+    const auto krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_cache + off),
+                                                       (short)0, ok ? TB : 0, kRsrcWord3);
+    const auto vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_cache + off),
+                                                       (short)0, ok ? TB : 0, kRsrcWord3);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      kr[slot][c] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, c * 1024 + lane * 16, 0, 0));
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      vr[slot][c] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, c * 1024 + lane * 16, 0, 0));
+    okp[slot] = ok;
+  };
+#pragma unroll
+  for (int r = 0; r < R; ++r) issue(r, p0 + r);
+
+  f32x4_t acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int p = p0; p < p1; p += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (p + r < p1) {
+        f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          bf16x8_t kfrag;
+          if constexpr (CACHE == FP8KV_E4M3) {
+            const u32x4_t w = kr[r][kk >> 1];
+            kfrag = (kk & 1) ? e4m3x8_to_bf16(w.z, w.w) : e4m3x8_to_bf16(w.x, w.y);
+          } else {
+            kfrag = __builtin_bit_cast(bf16x8_t, kr[r][kk]);
+          }
+          st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[kk], st, 0, 0, 0);
+        }
+        // the prompt's pages are full; a page id outside the pool adds nothing
+        float sv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[i] = okp[r] ? st[i] * sc : -INFINITY;
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mx = wave_max_rows(mx);
+        const float m_new = fmaxf(m_run, mx);
+        if (__any(m_new > m_run)) {
+          const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+          l_run *= alpha;
+          m_run = m_new;
+        }
+        const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(sv[i] - mref);
+        l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        if constexpr (CACHE == FP8KV_E4M3) {
+          f16x4_t ph, pl;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ph[i] = static_cast<_Float16>(pr[i]);
+            pl[i] = static_cast<_Float16>(pr[i] - static_cast<float>(ph[i]));
+          }
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const f16x4_t vfrag = e4m3x4_to_f16(vr[r][t >> 2][t & 3]);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(vfrag, ph, acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(vfrag, pl, acc[t], 0, 0, 0);
+          }
+        } else {
+          s16x4_t ph, pl;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const __bf16 h = static_cast<__bf16>(pr[i]);
+            ph[i] = __builtin_bit_cast(short, h);
+            pl[i] = __builtin_bit_cast(short, static_cast<__bf16>(pr[i] - static_cast<float>(h)));
+          }
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const u32x4_t w = vr[r][t >> 1];
+            u32x2_t pair;
+            pair.x = (t & 1) ? w.z : w.x;
+            pair.y = (t & 1) ? w.w : w.y;
+            const s16x4_t vfrag = __builtin_bit_cast(s16x4_t, pair);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vfrag, ph, acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vfrag, pl, acc[t], 0, 0, 0);
+          }
+        }
+      }
+      issue(r, p + r + R);
+    }
+  }
+  const float l_tot = wave_sum_rows(l_run);
+  if (col < cols) {
+    // acc[t][i] of lane (n, qd) holds dim 32 qd + 8 i + t
+    const int64_t pidx = static_cast<int64_t>(s) * a.batch * a.Hq + row;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4_t* po = reinterpret_cast<f32x4_t*>(a.ws_o + pidx * kHeadDim + 32 * qd + 8 * i);
+      po[0] = f32x4_t{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+      po[1] = f32x4_t{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+    }
+    if (qd == 0) {
+      a.ws_ml[pidx * 2] = m_run;
+      a.ws_ml[pidx * 2 + 1] = l_tot;
+    }
+  }
+}
+
+// Output rows of the shared-prompt call: the prompt's S partial states and
+// the own-token rows (normalised, with their log-sum-exp) in one log-sum-exp.
+// A thread per (row, 4 dims).  Rows of aborted requests, of contexts that do
+// not extend past the prompt and of contexts the table cannot hold are +0.
+struct CombineArgs {
+  const float* ws_o;
+  const float* ws_ml;
+  const float* suf_out;   // [B][Hq][128] f32
+  const float* suf_lse;   // [B][Hq]
+  const int32_t* ctx_lens;
+  const uint8_t* abort;
+  const float* v_scale;
+  void* out;
+  int32_t batch, Hq, G, S, prefix_len, max_tokens, out_f32;
+};
+
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t rows = static_cast<int64_t>(a.batch) * a.Hq;
+  if (idx >= rows * (kHeadDim / 4)) return;
+  const int64_t row = idx / (kHeadDim / 4);
+  const int d = 4 * static_cast<int>(idx % (kHeadDim / 4));
+  const int b = static_cast<int>(row / a.Hq);
+  const int h = static_cast<int>(row % a.Hq);
+  const int ctx = a.ctx_lens[b];
+  const bool aborted = a.abort != nullptr && a.abort[b] != 0;
+  f32x4_t res = {0.f, 0.f, 0.f, 0.f};
+  if (!aborted && ctx > a.prefix_len && ctx <= a.max_tokens) {
+    const float vsc = a.v_scale ? a.v_scale[h / a.G] : 1.0f;
+    float M = -INFINITY, L = 0.f;
+    f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < a.S; s0 += kMergeUnroll) {
+      // issue the loads of several ranges before using any of them
+      float m[kMergeUnroll], l[kMergeUnroll];
+      f32x4_t o[kMergeUnroll];
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u) {
+        const bool has = s0 + u < a.S;
+        const int64_t pidx = (s0 + u) * rows + row;
+        m[u] = has ? a.ws_ml[pidx * 2] : -INFINITY;
+        l[u] = has ? a.ws_ml[pidx * 2 + 1] : 0.f;
+        o[u] = has ? *reinterpret_cast<const f32x4_t*>(a.ws_o + pidx * kHeadDim + d)
+                   : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u) merge_state(M, L, O, m[u], l[u], o[u]);
+    }
+    O *= vsc;  // the prompt's partial sums are in cache units
+    // the own-token rows are normalised: as a state, (lse, 1, row)
+    merge_state(M, L, O, a.suf_lse[row], 1.0f,
+                *reinterpret_cast<const f32x4_t*>(a.suf_out + row * kHeadDim + d));
+    if (L > 0.f) res = O * (1.0f / L);
+  }
+  const int64_t io = row * kHeadDim + d;
+  if (a.out_f32) {
+    *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + io) = res;
+  } else {
+    u32x2_t w;
+    w.x = __builtin_bit_cast(unsigned short, static_cast<__bf16>(res[0])) |
+          (static_cast<unsigned>(__builtin_bit_cast(unsigned short, static_cast<__bf16>(res[1]))) << 16);
+    w.y = __builtin_bit_cast(unsigned short, static_cast<__bf16>(res[2])) |
+          (static_cast<unsigned>(__builtin_bit_cast(unsigned short, static_cast<__bf16>(res[3]))) << 16);
+    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + io) = w;
   }
 }
 
@@ -1347,14 +1602,16 @@ size_t decode_workspace(const fp8kv_cache_desc* desc, int32_t batch, int32_t num
   return workspace_layout(batch, num_q_heads, desc->num_kv_heads, q_len, w).total;
 }
 
-fp8kv_status decode_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
-                         const void* d_v_cache, const float* d_k_scale, const float* d_v_scale,
-                         const uint16_t* d_q, int32_t num_q_heads, int32_t q_len,
-                         const int32_t* d_page_table, int32_t max_pages_per_seq,
-                         const int32_t* d_ctx_lens, int32_t batch, float sm_scale,
-                         const uint8_t* d_abort, void* d_out, int32_t out_dtype,
-                         int32_t num_workers, void* d_workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
+// Checks one decode call's arguments and fills its kernel arguments (the
+// whole table from token 0, no log-sum-exp output).
+fp8kv_status decode_setup(const fp8kv_cache_desc* desc, const void* d_k_cache,
+                          const void* d_v_cache, const float* d_k_scale, const float* d_v_scale,
+                          const uint16_t* d_q, int32_t num_q_heads, int32_t q_len,
+                          const int32_t* d_page_table, int32_t max_pages_per_seq,
+                          const int32_t* d_ctx_lens, int32_t batch, float sm_scale,
+                          const uint8_t* d_abort, void* d_out, int32_t out_dtype,
+                          int32_t num_workers, void* d_workspace, size_t workspace_bytes,
+                          DecodeArgs& a, int32_t& workers) {
   fp8kv_status st = check_desc(desc);
   if (st != FP8KV_OK) return st;
   if (batch < 0 || max_pages_per_seq < 0 || num_q_heads <= 0 || num_workers < 0 || q_len <= 0)
@@ -1369,12 +1626,11 @@ fp8kv_status decode_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
       (max_pages_per_seq > 0 && !d_page_table))
     return FP8KV_INVALID_ARG;
   if (desc->cache_dtype == FP8KV_E4M3 && (!d_k_scale || !d_v_scale)) return FP8KV_INVALID_ARG;
-  const int32_t workers = fp8kv_decode_num_workers(num_workers);
+  workers = fp8kv_decode_num_workers(num_workers);
   if (workers <= 0) return FP8KV_HIP_ERROR;
   const WorkspaceLayout L =
       workspace_layout(batch, num_q_heads, desc->num_kv_heads, q_len, workers);
   if (!d_workspace || workspace_bytes < L.total) return FP8KV_WORKSPACE_TOO_SMALL;
-  DecodeArgs a;
   a.k_cache = static_cast<const uint8_t*>(d_k_cache);
   a.v_cache = static_cast<const uint8_t*>(d_v_cache);
   // a BF16 cache holds the values themselves: no scales
@@ -1389,9 +1645,12 @@ fp8kv_status decode_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
   a.ws_o = reinterpret_cast<float*>(ws + L.o);
   a.ws_ml = reinterpret_cast<float*>(ws + L.ml);
   a.ws_pre = reinterpret_cast<int32_t*>(ws + L.pre);
+  a.lse = nullptr;
   a.page_stride = static_cast<int64_t>(desc->num_kv_heads) * tile_bytes(desc);
   a.batch = batch;
   a.max_pages = max_pages_per_seq;
+  a.pt_stride = max_pages_per_seq;
+  a.tok0 = 0;
   a.num_pages = desc->num_pages;
   a.Hq = num_q_heads;
   a.Hkv = desc->num_kv_heads;
@@ -1400,20 +1659,26 @@ fp8kv_status decode_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
   a.C = G * q_len;
   a.out_f32 = out_dtype == FP8KV_OUT_F32 ? 1 : 0;
   a.sm_scale = sm_scale;
-  const int segs = batch * desc->num_kv_heads;
-  // With the device's default grid, long segments shared by many workgroups
-  // leave the merge a long chain of pieces per segment (one request of 8k
-  // tokens: ~100), which costs more than the extra workgroups gain; the
-  // default grid is capped at kDefaultPiecesPerSegment workgroups per segment.
-  // An explicit worker count is used as given.
-  // more than 16 (query, head) columns: two column tiles, 2 waves per SIMD
-  // instead of 3, so the default grid holds 2/3 as many workgroups
+  return FP8KV_OK;
+}
+
+// The decode kernel and its merge pass.
+fp8kv_status decode_launch(const DecodeArgs& a, int32_t cache_dtype, int32_t workers,
+                           int32_t num_workers, hipStream_t stream) {
+  const int segs = a.batch * a.Hkv;
+  // More than 16 (query, head) columns: two column tiles, 2 waves per SIMD
+  // instead of 3, so the default grid holds 2/3 as many workgroups.  With the
+  // default grid, long segments shared by many workgroups leave the merge a
+  // long chain of pieces per segment (one request of 8k tokens: ~100), which
+  // costs more than the extra workgroups gain: the default grid is capped at
+  // kDefaultPiecesPerSegment workgroups per segment.  An explicit worker
+  // count is used as given.
   const bool two_tiles = a.C > kTileCols;
   int blocks = workers / kWaves;
   if (num_workers == 0 && two_tiles) blocks = blocks / 3 * 2;
   if (num_workers == 0 && static_cast<int64_t>(kDefaultPiecesPerSegment) * segs < blocks)
     blocks = kDefaultPiecesPerSegment * segs;
-  if (desc->cache_dtype == FP8KV_E4M3) {
+  if (cache_dtype == FP8KV_E4M3) {
     if (two_tiles)
       hipLaunchKernelGGL((decode_kernel<FP8KV_E4M3, FP8KV_DEPTH_E4M3_2T, 2>), dim3(blocks),
                          dim3(kThreads), 0, stream, a);
@@ -1428,7 +1693,7 @@ fp8kv_status decode_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
       hipLaunchKernelGGL((decode_kernel<FP8KV_BF16, FP8KV_DEPTH_BF16, 1>), dim3(blocks),
                          dim3(kThreads), 0, stream, a);
   }
-  st = launched();
+  fp8kv_status st = launched();
   if (st != FP8KV_OK) return st;
   // at least 256 threads, one per (column, 4 dims) pair up to 1024
   const int pairs = a.C * (kHeadDim / 4);
@@ -1444,6 +1709,142 @@ fp8kv_status decode_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
   return launched();
 }
 
+fp8kv_status decode_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
+                         const void* d_v_cache, const float* d_k_scale, const float* d_v_scale,
+                         const uint16_t* d_q, int32_t num_q_heads, int32_t q_len,
+                         const int32_t* d_page_table, int32_t max_pages_per_seq,
+                         const int32_t* d_ctx_lens, int32_t batch, float sm_scale,
+                         const uint8_t* d_abort, void* d_out, int32_t out_dtype,
+                         int32_t num_workers, void* d_workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  DecodeArgs a;
+  int32_t workers = 0;
+  const fp8kv_status st = decode_setup(desc, d_k_cache, d_v_cache, d_k_scale, d_v_scale, d_q,
+                                       num_q_heads, q_len, d_page_table, max_pages_per_seq,
+                                       d_ctx_lens, batch, sm_scale, d_abort, d_out, out_dtype,
+                                       num_workers, d_workspace, workspace_bytes, a, workers);
+  if (st != FP8KV_OK || batch == 0) return st;
+  return decode_launch(a, desc->cache_dtype, workers, num_workers, stream);
+}
+
+// ---- the shared-prompt call ------------------------------------------------
+// page ranges of the prompt: enough workgroups to fill the device, at least
+// kPrefixMinPages pages each
+constexpr int kPrefixMinPages = 8;
+
+struct SharedLayout {
+  size_t decode, o, ml, suf_out, suf_lse, total;
+  int32_t S, tiles, blocks;
+};
+
+SharedLayout shared_layout(int32_t batch, int32_t Hq, int32_t Hkv, int32_t P0, int32_t workers) {
+  SharedLayout L;
+  const int32_t G = Hq / Hkv;
+  L.tiles = static_cast<int32_t>((static_cast<int64_t>(batch) * G + kTileCols - 1) / kTileCols);
+  L.blocks = (L.tiles + kWaves - 1) / kWaves;
+  const int64_t base = static_cast<int64_t>(Hkv) * L.blocks;
+  const int64_t want = (workers / kWaves + base - 1) / base;
+  const int64_t most = P0 / kPrefixMinPages > 1 ? P0 / kPrefixMinPages : 1;
+  L.S = static_cast<int32_t>(want < 1 ? 1 : (want < most ? want : most));
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t rows = static_cast<size_t>(batch) * Hq;
+  L.decode = up(workspace_layout(batch, Hq, Hkv, 1, workers).total);
+  L.o = L.decode;
+  L.ml = L.o + up(static_cast<size_t>(L.S) * rows * kHeadDim * sizeof(float));
+  L.suf_out = L.ml + up(static_cast<size_t>(L.S) * rows * 2 * sizeof(float));
+  L.suf_lse = L.suf_out + up(rows * kHeadDim * sizeof(float));
+  L.total = L.suf_lse + up(rows * sizeof(float));
+  return L;
+}
+
+fp8kv_status shared_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
+                         const void* d_v_cache, const float* d_k_scale, const float* d_v_scale,
+                         const uint16_t* d_q, int32_t num_q_heads,
+                         const int32_t* d_prefix_pages, int32_t prefix_len,
+                         const int32_t* d_page_table, int32_t max_pages_per_seq,
+                         const int32_t* d_ctx_lens, int32_t batch, float sm_scale,
+                         const uint8_t* d_abort, void* d_out, int32_t out_dtype,
+                         int32_t num_workers, void* d_workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (prefix_len < 0 || prefix_len % kPage != 0) return FP8KV_INVALID_ARG;
+  const int32_t P0 = prefix_len / kPage;
+  if (P0 == 0)
+    return decode_impl(desc, d_k_cache, d_v_cache, d_k_scale, d_v_scale, d_q, num_q_heads, 1,
+                       d_page_table, max_pages_per_seq, d_ctx_lens, batch, sm_scale, d_abort,
+                       d_out, out_dtype, num_workers, d_workspace, workspace_bytes, stream);
+  if (max_pages_per_seq < P0 || !d_prefix_pages) return FP8KV_INVALID_ARG;
+  // the own tokens: the table past the prompt's pages, f32 rows with their
+  // log-sum-exp, in the workspace (checked with the whole workspace below)
+  DecodeArgs a;
+  int32_t workers = 0;
+  fp8kv_status st = decode_setup(desc, d_k_cache, d_v_cache, d_k_scale, d_v_scale, d_q,
+                                 num_q_heads, 1, d_page_table, max_pages_per_seq, d_ctx_lens,
+                                 batch, sm_scale, d_abort, d_out, out_dtype, num_workers,
+                                 d_workspace, workspace_bytes, a, workers);
+  if (st != FP8KV_OK || batch == 0) return st;
+  const SharedLayout L = shared_layout(batch, num_q_heads, desc->num_kv_heads, P0, workers);
+  if (workspace_bytes < L.total) return FP8KV_WORKSPACE_TOO_SMALL;
+  char* ws = static_cast<char*>(d_workspace);
+
+  PrefixArgs pa;
+  pa.k_cache = a.k_cache;
+  pa.v_cache = a.v_cache;
+  pa.k_scale = a.k_scale;
+  pa.v_scale = a.v_scale;
+  pa.q = d_q;
+  pa.prefix_pages = d_prefix_pages;
+  pa.ws_o = reinterpret_cast<float*>(ws + L.o);
+  pa.ws_ml = reinterpret_cast<float*>(ws + L.ml);
+  pa.page_stride = a.page_stride;
+  pa.batch = batch;
+  pa.Hq = num_q_heads;
+  pa.Hkv = a.Hkv;
+  pa.G = a.G;
+  pa.P0 = P0;
+  pa.S = L.S;
+  pa.tiles = L.tiles;
+  pa.blocks = L.blocks;
+  pa.num_pages = desc->num_pages;
+  pa.sm_scale = sm_scale;
+  const int64_t pgrid = static_cast<int64_t>(a.Hkv) * L.S * L.blocks;
+  if (pgrid > 0x7FFFFFFF) return FP8KV_UNSUPPORTED;
+  if (desc->cache_dtype == FP8KV_E4M3)
+    hipLaunchKernelGGL(prefix_kernel<FP8KV_E4M3>, dim3(pgrid), dim3(kThreads), 0, stream, pa);
+  else
+    hipLaunchKernelGGL(prefix_kernel<FP8KV_BF16>, dim3(pgrid), dim3(kThreads), 0, stream, pa);
+  st = launched();
+  if (st != FP8KV_OK) return st;
+
+  a.page_table = d_page_table + P0;
+  a.max_pages = max_pages_per_seq - P0;
+  a.tok0 = prefix_len;
+  a.out = ws + L.suf_out;
+  a.out_f32 = 1;
+  a.lse = reinterpret_cast<float*>(ws + L.suf_lse);
+  st = decode_launch(a, desc->cache_dtype, workers, num_workers, stream);
+  if (st != FP8KV_OK) return st;
+
+  CombineArgs ca;
+  ca.ws_o = pa.ws_o;
+  ca.ws_ml = pa.ws_ml;
+  ca.suf_out = reinterpret_cast<const float*>(ws + L.suf_out);
+  ca.suf_lse = a.lse;
+  ca.ctx_lens = d_ctx_lens;
+  ca.abort = d_abort;
+  ca.v_scale = a.v_scale;
+  ca.out = d_out;
+  ca.batch = batch;
+  ca.Hq = num_q_heads;
+  ca.G = a.G;
+  ca.S = L.S;
+  ca.prefix_len = prefix_len;
+  ca.max_tokens = max_pages_per_seq * kPage;
+  ca.out_f32 = out_dtype == FP8KV_OUT_F32 ? 1 : 0;
+  const int64_t threads = static_cast<int64_t>(batch) * num_q_heads * (kHeadDim / 4);
+  hipLaunchKernelGGL(combine_kernel, dim3((threads + 255) / 256), dim3(256), 0, stream, ca);
+  return launched();
+}
+
 }  // namespace
 
 extern "C" {
@@ -1456,6 +1857,29 @@ size_t fp8kv_decode_workspace_size(const fp8kv_cache_desc* desc, int32_t batch,
 size_t fp8kv_decode_workspace_size_q(const fp8kv_cache_desc* desc, int32_t batch,
                                      int32_t num_q_heads, int32_t q_len, int32_t num_workers) {
   return decode_workspace(desc, batch, num_q_heads, q_len, num_workers);
+}
+
+size_t fp8kv_decode_workspace_size_shared(const fp8kv_cache_desc* desc, int32_t batch,
+                                          int32_t num_q_heads, int32_t prefix_len,
+                                          int32_t num_workers) {
+  const size_t plain = decode_workspace(desc, batch, num_q_heads, 1, num_workers);
+  if (plain == 0 || prefix_len < 0 || prefix_len % kPage != 0) return 0;
+  if (prefix_len == 0) return plain;
+  const int32_t w = fp8kv_decode_num_workers(num_workers);
+  return shared_layout(batch, num_q_heads, desc->num_kv_heads, prefix_len / kPage, w).total;
+}
+
+fp8kv_status fp8kv_decode_attention_shared(
+    const fp8kv_cache_desc* desc, const void* d_k_cache, const void* d_v_cache,
+    const float* d_k_scale, const float* d_v_scale, const uint16_t* d_q, int32_t num_q_heads,
+    const int32_t* d_prefix_pages, int32_t prefix_len, const int32_t* d_page_table,
+    int32_t max_pages_per_seq, const int32_t* d_ctx_lens, int32_t batch, float sm_scale,
+    const uint8_t* d_abort, void* d_out, int32_t out_dtype, int32_t num_workers,
+    void* d_workspace, size_t workspace_bytes, hipStream_t stream) {
+  return shared_impl(desc, d_k_cache, d_v_cache, d_k_scale, d_v_scale, d_q, num_q_heads,
+                     d_prefix_pages, prefix_len, d_page_table, max_pages_per_seq, d_ctx_lens,
+                     batch, sm_scale, d_abort, d_out, out_dtype, num_workers, d_workspace,
+                     workspace_bytes, stream);
 }
 
 fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc* desc, const void* d_k_cache,

@@ -149,3 +149,99 @@ def test_shared_prompt_workload_full_size():
                                   w.ctx_lens[b:b + 1], SM_SCALE)
         err = check_outputs(o32[b, g * G:(g + 1) * G], None, ref[0])
         print(f"shared prompt b={b} g={g} ctx={n}: max abs err {err:.3e}")
+
+
+# ---------------------------------------------------------------------------
+# the shared-prompt call: the prompt's pages read once for the whole batch
+# ---------------------------------------------------------------------------
+def _shared_state(Hq, Hkv, cache_dtype=0, B=5, prefix=48, suffix=40, seed=6):
+    import workloads
+    from workloads import device
+    w = workloads.shared_prefix(B=B, prefix_len=prefix, suffix_max=suffix, Hq=Hq, Hkv=Hkv,
+                                seed=seed)
+    st = device.build(w, cache_dtype=cache_dtype)
+    st.step(check_tags=True)
+    torch.cuda.synchronize()
+    return w, st
+
+
+def _shared_call(fp8kv, w, st, out_dtype, workers=0, ctx=None, abort=None, prefix=None):
+    P0 = w.prefix_len // 16
+    prefix = w.prefix_len if prefix is None else prefix
+    out = fp8kv.decode_attention_shared(
+        st.desc, st.K, st.V, st.k_scale, st.v_scale, st.q, st.page_table[0, :max(P0, 1)].contiguous(),
+        prefix, st.page_table, st.ctx_lens if ctx is None else ctx, abort=abort,
+        out_dtype=out_dtype, num_workers=workers)
+    torch.cuda.synchronize()
+    return (out.view(torch.int16) if out.dtype == torch.bfloat16 else out).cpu().numpy()
+
+
+@pytest.mark.parametrize("Hq,Hkv,cd", [(8, 2, 0), (64, 8, 0), (4, 4, 0), (64, 2, 0), (8, 2, 1),
+                                       (64, 8, 1)])
+def test_shared_call_matches_oracle(Hq, Hkv, cd):
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    from _helpers import oracle_state
+    w, st = _shared_state(Hq, Hkv, cd)
+    Ko, Vo = oracle_state(w, st.k_scale_host, st.v_scale_host, cd)
+    ref, _ = oracle.attention(Ko, Vo, st.k_scale_host, st.v_scale_host, w.q_bits(), w.page_table,
+                              w.ctx_lens, SM_SCALE, cache_dtype=cd)
+    plain = st.decode(True, out_dtype=fp8kv.OUT_F32).cpu().numpy()
+    for nw in (0, 8, 64):
+        o32 = _shared_call(fp8kv, w, st, fp8kv.OUT_F32, nw)
+        o16 = _shared_call(fp8kv, w, st, fp8kv.OUT_BF16, nw).view(np.uint16)
+        err = check_outputs(o32, o16, ref)
+        assert np.abs(o32 - plain).max() <= 1e-5
+        print(f"shared call Hq={Hq} Hkv={Hkv} cache={cd} workers={nw}: max abs err {err:.3e}")
+
+
+def test_shared_call_edges():
+    """No prompt is the plain call (bitwise); aborted requests and contexts that
+    stop inside the prompt give +0 rows, the others stay exact; bad prompt
+    lengths are rejected before anything runs."""
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    from _helpers import oracle_state
+    w, st = _shared_state(8, 2)
+    plain = st.decode(True, out_dtype=fp8kv.OUT_F32).cpu().numpy()
+    assert np.array_equal(_shared_call(fp8kv, w, st, fp8kv.OUT_F32, prefix=0), plain)
+    ab = torch.tensor([0, 1, 0, 0, 0], dtype=torch.uint8, device="cuda")
+    ctx = w.ctx_lens.copy()
+    ctx[3] = w.prefix_len            # ends exactly at the end of the prompt
+    ctx[4] = 20                      # ends inside the prompt
+    o = _shared_call(fp8kv, w, st, fp8kv.OUT_F32, ctx=torch.from_numpy(ctx).cuda(), abort=ab)
+    assert (o[[1, 3, 4]] == 0).all()
+    Ko, Vo = oracle_state(w, st.k_scale_host, st.v_scale_host)
+    ref, _ = oracle.attention(Ko, Vo, st.k_scale_host, st.v_scale_host, w.q_bits(), w.page_table,
+                              w.ctx_lens, SM_SCALE)
+    check_outputs(o[[0, 2]], None, ref[[0, 2]])
+    assert fp8kv.decode_workspace_size_shared(st.desc, w.B, w.Hq, 8) == 0
+    for bad in (8, -16, 16 * (w.max_pages + 1)):
+        with pytest.raises(fp8kv.Fp8kvError) as e:
+            _shared_call(fp8kv, w, st, fp8kv.OUT_F32, prefix=bad)
+        assert e.value.status == -1
+
+
+def test_shared_call_full_size():
+    """The 64-request, 16,384-token-prompt workload: sampled pairs against the
+    oracle and every row against the plain call."""
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    import workloads
+    from workloads import device
+    w = workloads.shared_prefix()
+    st = device.build(w)
+    st.step(check_tags=True)
+    plain = st.decode(True, out_dtype=fp8kv.OUT_F32).cpu().numpy()
+    o32 = _shared_call(fp8kv, w, st, fp8kv.OUT_F32)
+    assert np.abs(o32 - plain).max() <= 1e-5
+    q = w.q_bits()
+    G = w.G
+    for b, g in [(5, 1), (63, 6)]:
+        n = int(w.ctx_lens[b])
+        K, V = oracle.new_cache(w.num_pages, 1)
+        sk, sv = st.k_scale_host[g:g + 1], st.v_scale_host[g:g + 1]
+        oracle.append(K, V, sk, sv, w.kv_tokens_head("k", b, 0, n, g)[:, None, :],
+                      w.kv_tokens_head("v", b, 0, n, g)[:, None, :], np.zeros(n, np.int32),
+                      np.arange(n, dtype=np.int32), w.page_table[b:b + 1])
+        ref, _ = oracle.attention(K, V, sk, sv, q[b:b + 1, g * G:(g + 1) * G], w.page_table[b:b + 1],
+                                  w.ctx_lens[b:b + 1], SM_SCALE)
+        err = check_outputs(o32[b, g * G:(g + 1) * G], None, ref[0])
+        print(f"shared call full size b={b} g={g}: max abs err {err:.3e}")
