@@ -72,6 +72,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
@@ -1218,8 +1219,8 @@ void prefix_kernel(PrefixArgs a) {
   const int p1 = static_cast<int>(static_cast<int64_t>(s + 1) * a.P0 / a.S);
   const float sc = a.sm_scale * (a.k_scale ? uniform_load(a.k_scale, g) : 1.0f) * kLog2e;
 
-  // pages in flight (4 or 6 measured no faster: this kernel is bound by its
-  // per-page arithmetic, not by load latency)
+  // pages in flight: the two of one step (a deeper ring measured no faster:
+  // this kernel is bound by its per-page arithmetic, not by load latency)
   constexpr int R = 2;
   u32x4_t kr[R][NC], vr[R][NC];
   bool okp[R];
@@ -1248,76 +1249,80 @@ void prefix_kernel(PrefixArgs a) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  for (int p = p0; p < p1; p += R) {
+  // the two pages of the ring are one 32-token step: PV runs on the 16x16x32
+  // MFMA, whose k index 8 qd + j holds token 4 qd + (j % 4) of page j / 4 --
+  // the lane's own V and P values of the two pages side by side
+  for (int p = p0; p < p1; p += 2) {
+    float sv[2][4];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (p + r < p1) {
-        f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 2; ++r) {
+      f32x4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          bf16x8_t kfrag;
-          if constexpr (CACHE == FP8KV_E4M3) {
-            const u32x4_t w = kr[r][kk >> 1];
-            kfrag = (kk & 1) ? e4m3x8_to_bf16(w.z, w.w) : e4m3x8_to_bf16(w.x, w.y);
-          } else {
-            kfrag = __builtin_bit_cast(bf16x8_t, kr[r][kk]);
-          }
-          st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[kk], st, 0, 0, 0);
-        }
-        // the prompt's pages are full; a page id outside the pool adds nothing
-        float sv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sv[i] = okp[r] ? st[i] * sc : -INFINITY;
-        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-        mx = wave_max_rows(mx);
-        const float m_new = fmaxf(m_run, mx);
-        if (__any(m_new > m_run)) {
-          const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
-#pragma unroll
-          for (int t = 0; t < 8; ++t) acc[t] *= alpha;
-          l_run *= alpha;
-          m_run = m_new;
-        }
-        const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-        float pr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(sv[i] - mref);
-        l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8_t kfrag;
         if constexpr (CACHE == FP8KV_E4M3) {
-          f16x4_t ph, pl;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            ph[i] = static_cast<_Float16>(pr[i]);
-            pl[i] = static_cast<_Float16>(pr[i] - static_cast<float>(ph[i]));
-          }
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const f16x4_t vfrag = e4m3x4_to_f16(vr[r][t >> 2][t & 3]);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(vfrag, ph, acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(vfrag, pl, acc[t], 0, 0, 0);
-          }
+          const u32x4_t w = kr[r][kk >> 1];
+          kfrag = (kk & 1) ? e4m3x8_to_bf16(w.z, w.w) : e4m3x8_to_bf16(w.x, w.y);
         } else {
-          s16x4_t ph, pl;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const __bf16 h = static_cast<__bf16>(pr[i]);
-            ph[i] = __builtin_bit_cast(short, h);
-            pl[i] = __builtin_bit_cast(short, static_cast<__bf16>(pr[i] - static_cast<float>(h)));
-          }
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const u32x4_t w = vr[r][t >> 1];
-            u32x2_t pair;
-            pair.x = (t & 1) ? w.z : w.x;
-            pair.y = (t & 1) ? w.w : w.y;
-            const s16x4_t vfrag = __builtin_bit_cast(s16x4_t, pair);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vfrag, ph, acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vfrag, pl, acc[t], 0, 0, 0);
-          }
+          kfrag = __builtin_bit_cast(bf16x8_t, kr[r][kk]);
         }
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[kk], st, 0, 0, 0);
       }
-      issue(r, p + r + R);
+      // the prompt's pages are full; a page past the range or with an id
+      // outside the pool adds nothing
+      const bool use = okp[r] && p + r < p1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[r][i] = use ? st[i] * sc : -INFINITY;
     }
+    float mx = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                     fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+    mx = wave_max_rows(mx);
+    const float m_new = fmaxf(m_run, mx);
+    if (__any(m_new > m_run)) {
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+    float pr[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pr[j] = fast_exp2(sv[j / 4][j % 4] - mref);
+    l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+    if constexpr (CACHE == FP8KV_E4M3) {
+      f16x8_t ph, pl;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        ph[j] = static_cast<_Float16>(pr[j]);
+        pl[j] = static_cast<_Float16>(pr[j] - static_cast<float>(ph[j]));
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const f16x4_t va = e4m3x4_to_f16(vr[0][t >> 2][t & 3]);
+        const f16x4_t vb = e4m3x4_to_f16(vr[1][t >> 2][t & 3]);
+        const f16x8_t vfrag = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vfrag, ph, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vfrag, pl, acc[t], 0, 0, 0);
+      }
+    } else {
+      bf16x8_t ph, pl;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        ph[j] = static_cast<__bf16>(pr[j]);
+        pl[j] = static_cast<__bf16>(pr[j] - static_cast<float>(ph[j]));
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const u32x4_t wa = vr[0][t >> 1], wb = vr[1][t >> 1];
+        const u32x4_t w = (t & 1) ? u32x4_t{wa.z, wa.w, wb.z, wb.w} : u32x4_t{wa.x, wa.y, wb.x, wb.y};
+        const bf16x8_t vfrag = __builtin_bit_cast(bf16x8_t, w);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfrag, ph, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfrag, pl, acc[t], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) issue(r, p + r + 2);
   }
   const float l_tot = wave_sum_rows(l_run);
   if (col < cols) {
