@@ -642,6 +642,11 @@ void decode_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // the ring's two pages as one step with PV on the 16x16x32 MFMA: half the PV
+  // instructions, which the two-tile form (2 waves per SIMD, twice the MFMA
+  // work per page) gains from; the one-tile form refills its first slot a
+  // page later that way and measured slower
+  constexpr bool kPairPV = DEPTH == 2 && NT == 2;
   const int n = lane & 15;   // MFMA column: (query, head) pair 16*ct + n of tile ct
   const int qd = lane >> 4;  // lane quarter
   const int B = a.batch;
@@ -826,6 +831,127 @@ void decode_kernel(DecodeArgs a) {
       const float sc = a.sm_scale * (a.k_scale ? uniform_load(a.k_scale, P.g) : 1.0f) * kLog2e;
 
       for (int i0 = 0; i0 < iters; i0 += DEPTH) {
+        if constexpr (kPairPV) {
+          // the ring's two pages as one 32-token step: joint softmax update, PV
+          // on the 16x16x32 MFMA whose k index 8 qd + j holds token
+          // 4 qd + (j % 4) of page j / 4 (the lane's own V and P of both pages)
+          float sv[2][NT][4];
+          u32x4_t vmask[2];
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const int i = i0 + s;
+            const int page = pg0 + kWaves * i;
+            const int left = (i < cnt && okp[s]) ? ctx - page * kPage : 0;
+            const int valid = min(left, kPage);
+            f32x4_t st[NT];
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) st[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+              bf16x8_t kfrag;
+              if constexpr (CACHE == FP8KV_E4M3) {
+                const u32x4_t w = kr[s][kk >> 1];
+                kfrag = (kk & 1) ? e4m3x8_to_bf16(w.z, w.w) : e4m3x8_to_bf16(w.x, w.y);
+              } else {
+                kfrag = __builtin_bit_cast(bf16x8_t, kr[s][kk]);
+              }
+#pragma unroll
+              for (int ct = 0; ct < NT; ++ct)
+                st[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[ct][kk], st[ct], 0, 0, 0);
+            }
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) sv[s][ct][r] = st[ct][r] * sc;
+            vmask[s] = u32x4_t{~0u, ~0u, ~0u, ~0u};
+            if (left - (a.qlen - 1) < kPage) {
+#pragma unroll
+              for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (4 * qd + r >= left - lag[ct]) sv[s][ct][r] = -INFINITY;
+              const int keep = min(max(valid - 4 * qd, 0), 4);
+              if constexpr (CACHE == FP8KV_E4M3) {
+                const unsigned m = keep >= 4 ? ~0u : ((1u << (8 * keep)) - 1u);
+                vmask[s] = u32x4_t{m, m, m, m};
+              } else {
+                const unsigned m0 = keep >= 2 ? ~0u : (keep == 1 ? 0xFFFFu : 0u);
+                const unsigned m1 = keep >= 4 ? ~0u : (keep == 3 ? 0xFFFFu : 0u);
+                vmask[s] = u32x4_t{m0, m1, m0, m1};
+              }
+            }
+          }
+          float p[NT][8];
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) {
+            float mx = fmaxf(fmaxf(fmaxf(sv[0][ct][0], sv[0][ct][1]), fmaxf(sv[0][ct][2], sv[0][ct][3])),
+                             fmaxf(fmaxf(sv[1][ct][0], sv[1][ct][1]), fmaxf(sv[1][ct][2], sv[1][ct][3])));
+            mx = wave_max_rows(mx);
+            const float m_new = fmaxf(m_run[ct], mx);
+            if (__any(m_new > m_run[ct])) {
+              const float alpha = (m_run[ct] == -INFINITY) ? 0.f : fast_exp2(m_run[ct] - m_new);
+#pragma unroll
+              for (int t = 0; t < 8; ++t) acc[ct][t] *= alpha;
+              l_run[ct] *= alpha;
+              m_run[ct] = m_new;
+            }
+            const float mref = (m_run[ct] == -INFINITY) ? 0.f : m_run[ct];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p[ct][j] = fast_exp2(sv[j / 4][ct][j % 4] - mref);
+            l_run[ct] += ((p[ct][0] + p[ct][1]) + (p[ct][2] + p[ct][3])) +
+                         ((p[ct][4] + p[ct][5]) + (p[ct][6] + p[ct][7]));
+          }
+          if constexpr (CACHE == FP8KV_E4M3) {
+            f16x8_t ph[NT], pl[NT];
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                ph[ct][j] = static_cast<_Float16>(p[ct][j]);
+                pl[ct][j] = static_cast<_Float16>(p[ct][j] - static_cast<float>(ph[ct][j]));
+              }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              const f16x4_t va = e4m3x4_to_f16(vr[0][t >> 2][t & 3] & vmask[0][t & 3]);
+              const f16x4_t vb = e4m3x4_to_f16(vr[1][t >> 2][t & 3] & vmask[1][t & 3]);
+              const f16x8_t vfrag = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+#pragma unroll
+              for (int ct = 0; ct < NT; ++ct) {
+                acc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vfrag, ph[ct], acc[ct][t], 0, 0, 0);
+                acc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vfrag, pl[ct], acc[ct][t], 0, 0, 0);
+              }
+            }
+          } else {
+            bf16x8_t ph[NT], pl[NT];
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                ph[ct][j] = static_cast<__bf16>(p[ct][j]);
+                pl[ct][j] = static_cast<__bf16>(p[ct][j] - static_cast<float>(ph[ct][j]));
+              }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              const u32x4_t wa = vr[0][t >> 1], wb = vr[1][t >> 1];
+              const u32x4_t w = (t & 1) ? u32x4_t{wa.z & vmask[0].x, wa.w & vmask[0].y,
+                                                  wb.z & vmask[1].x, wb.w & vmask[1].y}
+                                        : u32x4_t{wa.x & vmask[0].x, wa.y & vmask[0].y,
+                                                  wb.x & vmask[1].x, wb.y & vmask[1].y};
+              const bf16x8_t vfrag = __builtin_bit_cast(bf16x8_t, w);
+#pragma unroll
+              for (int ct = 0; ct < NT; ++ct) {
+                acc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfrag, ph[ct], acc[ct][t], 0, 0, 0);
+                acc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfrag, pl[ct], acc[ct][t], 0, 0, 0);
+              }
+            }
+          }
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            issue(s, __builtin_amdgcn_readfirstlane(pid_ring[s]));
+            pid_ring[s] = fetch_pid();
+          }
+          continue;
+        }
 #pragma unroll
         for (int s = 0; s < DEPTH; ++s) {
           const int i = i0 + s;
