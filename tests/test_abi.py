@@ -155,3 +155,18 @@ def test_prepared_launch_checks_once_and_keeps_its_tensors():
         raise AssertionError("a host tensor was accepted")
     # a prepared launch holds the tensors its pointers refer to
     assert "_keep" in fp8kv.Launch.__slots__
+
+
+def test_shared_prompt_workspace():
+    # the shared-prompt call's workspace: the plain decode's plus the prompt's partial
+    # states and the own-token rows; prompt lengths must be multiples of 16
+    d = fp8kv.desc(4096, 8)
+    ws = fp8kv.decode_workspace_size_shared
+    plain = fp8kv.decode_workspace_size(d, 64, 64, 3072)
+    assert ws(d, 64, 64, 0, 3072) == plain
+    a, b = ws(d, 64, 64, 1024, 3072), ws(d, 64, 64, 16384, 3072)
+    assert plain < a <= b
+    assert a >= plain + 64 * 64 * (128 + 2) * 4 + 64 * 64 * (128 + 1) * 4
+    for bad in (8, -16, 17):
+        assert ws(d, 64, 64, bad, 3072) == 0
+    assert ws(d, 64, 66, 1024, 3072) == 0          # Hq % Hkv != 0
