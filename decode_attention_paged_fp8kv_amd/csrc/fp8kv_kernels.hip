@@ -9,16 +9,24 @@
 // Kernels:
 //   verify_tags_kernel      one workgroup per request: any stale/out-of-range
 //                           page among the pages the step reads -> abort[b]=1
-//   append_kernel<C>        quantize-on-append of new tokens into their pages
-//   decode_split_kernel<C>  per (request, kv-head, split): paged K/V tiles are
+//   verify_append_kernel<C> the same check and the request's new token
+//                           appended in one launch (append skipped on abort)
+//   append_kernel<C>        quantize-on-append of any number of tokens
+//   decode_kernel<C, D, NT> persistent workgroups, each an equal slice of the
+//                           (request, kv-head, page) list: paged K/V tiles are
 //                           loaded straight into matrix-core fragment registers
 //                           (16-byte buffer loads, tile layout = fragment
 //                           order), converted e4m3 -> bf16/f16 in hardware,
 //                           QK^T and PV on MFMA, online softmax in registers,
 //                           4 waves merged through LDS; writes the output, or a
-//                           (max, sum, weighted V) partial when the request is
-//                           split
-//   combine_kernel          log-sum-exp merge of the partials in split order
+//                           (max, sum, weighted V) partial for a split segment
+//   merge_flat_kernel,      log-sum-exp merge of the partials in workgroup
+//   merge_grouped_kernel    order (few pieces per segment / many)
+//   prefix_kernel<C>        a prompt shared by the batch: its pages read once
+//                           per kv-head with the (request, q-head) pairs as
+//                           MFMA columns
+//   combine_kernel          the prompt's partials and the own-token rows joined
+//                           by log-sum-exp
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,7 +55,8 @@ constexpr int kRsrcWord3 = 0x00020000;
 // Cache policy of the K/V tile loads: nt (streaming).  Each tile is read
 // once per step, so keeping it out of the normal replacement order costs no
 // reuse; measured on gfx950, random 2 KB reads with nt run ~13% faster than
-// with the default policy.
+// with the default policy.  (Pages shared by many requests are re-read; the
+// shared-prompt call reads those with the default policy, once per batch.)
 constexpr int kKvLoadPolicy = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 
