@@ -361,14 +361,13 @@ def shared_study(args):
         if shared:
             # the shared-prompt call: the prompt's pages once for the whole batch
             import decode_attention_paged_fp8kv_amd as fp8kv
-            P0 = w.prefix_len // 16
-            pp = st.page_table[0, :P0].contiguous()
-            ws = torch.zeros(fp8kv.decode_workspace_size_shared(st.desc, w.B, w.Hq, w.prefix_len),
+            groups = ([0, w.B], [w.prefix_len])
+            ws = torch.zeros(fp8kv.decode_workspace_size_shared(st.desc, w.B, w.Hq, w.max_pages,
+                                                                *groups),
                              dtype=torch.uint8, device="cuda")
             call = fp8kv.decode_attention_shared(st.desc, st.K, st.V, st.k_scale, st.v_scale,
-                                                 st.q, pp, w.prefix_len, st.page_table,
-                                                 st.ctx_lens, abort=st.abort, workspace=ws,
-                                                 prepare=True)
+                                                 st.q, st.page_table, st.ctx_lens, *groups,
+                                                 abort=st.abort, workspace=ws, prepare=True)
 
             def cstep():
                 st.verify_append()
@@ -382,9 +381,8 @@ def shared_study(args):
                 "decode_us": round(tdc * 1e6, 2), "alg_gbps": round(attn_bytes / tdc / 1e9, 1),
                 "distinct_kv_gbps": round(unique_kv / tdc / 1e9, 1)}
             out_c = fp8kv.decode_attention_shared(st.desc, st.K, st.V, st.k_scale, st.v_scale,
-                                                  st.q, pp, w.prefix_len, st.page_table,
-                                                  st.ctx_lens, abort=st.abort, out_dtype=1,
-                                                  workspace=ws)
+                                                  st.q, st.page_table, st.ctx_lens, *groups,
+                                                  abort=st.abort, out_dtype=1, workspace=ws)
             res["shared_call"]["max_abs_diff_vs_plain_call"] = float(
                 (out_c - res["out_shared"]).abs().max())
         del st

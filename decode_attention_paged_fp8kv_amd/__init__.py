@@ -85,10 +85,11 @@ _decode_q = _sig("fp8kv_decode_attention_q", _i32,
                  [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _i32, _i32, _p, _i32, _p, _i32,
                   ctypes.c_float, _p, _p, _i32, _i32, _p, ctypes.c_size_t, _p])
 _ws_size_shared = _sig("fp8kv_decode_workspace_size_shared", ctypes.c_size_t,
-                       [ctypes.POINTER(CacheDesc), _i32, _i32, _i32, _i32])
+                       [ctypes.POINTER(CacheDesc), _i32, _i32, _i32, _i32, _p, _p, _i32])
 _decode_shared = _sig("fp8kv_decode_attention_shared", _i32,
-                      [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _i32,
-                       _p, _i32, ctypes.c_float, _p, _p, _i32, _i32, _p, ctypes.c_size_t, _p])
+                      [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _i32, _i32, _p, _p, _p,
+                       _i32, _p, _i32, ctypes.c_float, _p, _p, _i32, _i32, _p, ctypes.c_size_t,
+                       _p])
 _verify_append = _sig("fp8kv_verify_append", _i32,
                       [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _p,
                        _i32, _p, _p, _p])
@@ -380,27 +381,41 @@ def decode_attention_q(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, page
                  workspace), prepare)
 
 
-def decode_workspace_size_shared(d: CacheDesc, batch: int, num_q_heads: int, prefix_len: int,
-                                 num_workers: int = 0) -> int:
-    return int(_ws_size_shared(ctypes.byref(d), batch, num_q_heads, prefix_len, num_workers))
+def _groups(group_start, prefix_len):
+    """Host int32 arrays of a prompt-group description (kept alive by the caller)."""
+    import numpy as np
+    gs = np.ascontiguousarray(np.asarray(group_start, dtype=np.int32))
+    pl = np.ascontiguousarray(np.asarray(prefix_len, dtype=np.int32))
+    if gs.ndim != 1 or pl.ndim != 1 or gs.size != pl.size + 1:
+        raise ValueError("group_start needs one entry more than prefix_len")
+    return gs, pl
 
 
-def decode_attention_shared(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, prefix_pages,
-                            prefix_len: int, page_table, ctx_lens, abort=None, out=None,
+def decode_workspace_size_shared(d: CacheDesc, batch: int, num_q_heads: int, max_pages: int,
+                                 group_start, prefix_len, num_workers: int = 0) -> int:
+    gs, pl = _groups(group_start, prefix_len)
+    return int(_ws_size_shared(ctypes.byref(d), batch, num_q_heads, max_pages, pl.size,
+                               gs.ctypes.data, pl.ctypes.data, num_workers))
+
+
+def decode_attention_shared(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, page_table,
+                            ctx_lens, group_start, prefix_len, abort=None, out=None,
                             out_dtype: int = OUT_BF16, sm_scale: Optional[float] = None,
                             num_workers: int = 0, workspace=None, stream=None,
                             prepare: bool = False):
-    """decode_attention for a batch whose requests all continue one prompt of
-    prefix_len tokens (a multiple of 16) held in prefix_pages, the first
-    prefix_len/16 entries of every request's table: the prompt's pages are read
-    once per kv-head for the whole batch.  Returns out [B][Hq][128]."""
+    """decode_attention for a batch whose requests [group_start[k],
+    group_start[k+1]) continue prompt k of prefix_len[k] tokens (a multiple of
+    16), on the pages their tables list first: each prompt's pages are read
+    once per kv-head for its whole group.  Returns out [B][Hq][128]."""
     B, Hq, D = q.shape
+    gs, pl = _groups(group_start, prefix_len)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((B, Hq, D), device=q.device,
                           dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32)
-    need = decode_workspace_size_shared(d, B, Hq, prefix_len, num_workers)
+    P = page_table.shape[1]
+    need = decode_workspace_size_shared(d, B, Hq, P, gs, pl, num_workers)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     fp8 = d.cache_dtype == E4M3
@@ -408,16 +423,15 @@ def decode_attention_shared(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q,
             _dev(v_cache, _U8 + _BITS16, "v_cache"),
             _dev(k_scale, _F32, "k_scale", allow_none=not fp8),
             _dev(v_scale, _F32, "v_scale", allow_none=not fp8),
-            _dev(q, _BITS16, "q"), Hq, _dev(prefix_pages, _I32, "prefix_pages", allow_none=True),
-            int(prefix_len), _dev(page_table, _I32, "page_table"), page_table.shape[1],
-            _dev(ctx_lens, _I32, "ctx_lens"), B, float(sm_scale),
-            _dev(abort, _U8, "abort", allow_none=True),
+            _dev(q, _BITS16, "q"), Hq, pl.size, gs.ctypes.data, pl.ctypes.data,
+            _dev(page_table, _I32, "page_table"), P, _dev(ctx_lens, _I32, "ctx_lens"), B,
+            float(sm_scale), _dev(abort, _U8, "abort", allow_none=True),
             _dev(out, (torch.bfloat16, torch.int16, torch.float32), "out"), out_dtype,
             num_workers, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
             _stream(stream))
     return _run(_decode_shared, args, "decode_attention_shared", out,
-                (d, k_cache, v_cache, k_scale, v_scale, q, prefix_pages, page_table, ctx_lens,
-                 abort, out, workspace), prepare)
+                (d, k_cache, v_cache, k_scale, v_scale, q, page_table, ctx_lens, abort, out,
+                 workspace, gs, pl), prepare)
 
 
 def step(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, k_new, v_new, new_pos,

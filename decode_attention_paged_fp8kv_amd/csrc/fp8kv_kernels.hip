@@ -22,9 +22,10 @@
 //                           (max, sum, weighted V) partial for a split segment
 //   merge_flat_kernel,      log-sum-exp merge of the partials in workgroup
 //   merge_grouped_kernel    order (few pieces per segment / many)
-//   prefix_kernel<C>        a prompt shared by the batch: its pages read once
-//                           per kv-head with the (request, q-head) pairs as
-//                           MFMA columns
+//   prefix_kernel<C>        prompts shared by groups of requests: each one's
+//                           pages read once per kv-head with the group's
+//                           (request, q-head) pairs as MFMA columns
+//   view_kernel             each request's table and context past its prompt
 //   combine_kernel          the prompt's partials and the own-token rows joined
 //                           by log-sum-exp
 #include <hip/hip_runtime.h>
@@ -1297,30 +1298,72 @@ __global__ __launch_bounds__(kMergeGroupedThreads) void merge_grouped_kernel(Dec
 }
 
 // ---------------------------------------------------------------------------
-// 6. a prompt shared by every request of the batch (cache reuse)
+// 6. prompts shared by groups of requests (cache reuse)
 // ---------------------------------------------------------------------------
-// When all requests continue one prompt whose pages they all map, each of
-// those pages is read once per kv-head for the whole batch: the MFMA columns
-// are the (request, q-head) pairs of the kv-head (B*G of them, 16 per wave),
-// so the prompt part is a dense product instead of B separate reads.  A
+// When a group of requests continues one prompt whose pages they all map,
+// each of those pages is read once per kv-head for the whole group: the MFMA
+// columns are the group's (request, q-head) pairs of the kv-head (16 per
+// wave), so the prompt part is a dense product instead of separate reads.  A
 // workgroup takes 4 column tiles (one per wave) and a range of the prompt's
 // pages; its waves read the same pages at the same time, which the caches
 // serve once.  Each (column, page range) leaves (max, sum, weighted V) for
 // the combine pass.  The requests' own tokens go through decode_kernel over
 // the rest of their tables, with its log-sum-exp output.
+// Requests [req_start[k], req_end[k]) continue prompt k of prefix_len[k]
+// tokens, on the pages their tables list first (read from the table of the
+// group's first request).  Group k's workgroups are [wg_start[k],
+// wg_start[k+1]): S[k] page ranges x Hkv x blocks[k] column blocks; its
+// partial states start at row part_base[k] of the workspace.
+constexpr int kMaxPromptGroups = 32;
+struct PromptGroups {
+  int32_t n;
+  int32_t req_start[kMaxPromptGroups];
+  int32_t req_end[kMaxPromptGroups];
+  int32_t prefix_len[kMaxPromptGroups];
+  int32_t S[kMaxPromptGroups];
+  int32_t tiles[kMaxPromptGroups];
+  int32_t blocks[kMaxPromptGroups];
+  int32_t wg_start[kMaxPromptGroups + 1];
+  int64_t part_base[kMaxPromptGroups + 1];
+};
+
+// the group of request b, or -1
+__device__ __forceinline__ int prompt_group(const PromptGroups& pg, int b) {
+  for (int k = 0; k < pg.n; ++k)
+    if (b >= pg.req_start[k] && b < pg.req_end[k]) return k;
+  return -1;
+}
+
 struct PrefixArgs {
   const uint8_t* k_cache;
   const uint8_t* v_cache;
   const float* k_scale;
   const float* v_scale;
   const uint16_t* q;           // [B][Hq][128]
-  const int32_t* prefix_pages; // [P0]
-  float* ws_o;                 // [S][B*Hq][128]
-  float* ws_ml;                // [S][B*Hq][2]
+  const int32_t* page_table;   // [B][max_pages]
+  const int32_t* ctx_lens;     // [B]
+  int32_t* view_pt;            // [B][max_pages]: each table past its prompt
+  int32_t* view_ctx;           // [B]: each context past its prompt
+  float* ws_o;                 // [rows][128], rows as in PromptGroups
+  float* ws_ml;                // [rows][2]
   int64_t page_stride;
-  int32_t batch, Hq, Hkv, G, P0, S, tiles, blocks, num_pages;
+  int32_t batch, Hq, Hkv, G, max_pages, num_pages;
   float sm_scale;
+  PromptGroups pg;
 };
+
+// The own-token view of every request: its table past its prompt's pages and
+// its context past the prompt (the plain decode then runs on it).  A
+// workgroup per request.
+__global__ __launch_bounds__(256) void view_kernel(PrefixArgs a) {
+  const int b = blockIdx.x;
+  const int k = prompt_group(a.pg, b);
+  const int p0 = k < 0 ? 0 : a.pg.prefix_len[k] / kPage;
+  const int64_t row = static_cast<int64_t>(b) * a.max_pages;
+  for (int j = threadIdx.x; j < a.max_pages; j += 256)
+    a.view_pt[row + j] = j + p0 < a.max_pages ? a.page_table[row + j + p0] : -1;
+  if (threadIdx.x == 0) a.view_ctx[b] = a.ctx_lens[b] - p0 * kPage;
+}
 
 template <int CACHE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
@@ -1330,18 +1373,27 @@ void prefix_kernel(PrefixArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, qd = lane >> 4;
-  // workgroup -> (kv-head g, page range s, column block): the blocks reading
-  // the same pages are Hkv*S apart, so with Hkv*S a multiple of 8 they land on
-  // one XCD (workgroups go round robin over the 8) and share its L2
-  const int gs = blockIdx.x % (a.Hkv * a.S);
-  const int blk = blockIdx.x / (a.Hkv * a.S);
-  const int g = gs / a.S, s = gs % a.S;
+  // workgroup -> (prompt group k, kv-head g, page range s, column block): the
+  // blocks reading the same pages are Hkv*S apart, so with Hkv*S a multiple of
+  // 8 they land on one XCD (workgroups go round robin over the 8) and share
+  // its L2
+  int k = 0;
+  while (k + 1 < a.pg.n && static_cast<int>(blockIdx.x) >= a.pg.wg_start[k + 1]) ++k;
+  const int S = a.pg.S[k];
+  const int P0 = a.pg.prefix_len[k] / kPage;
+  const int wg = static_cast<int>(blockIdx.x) - a.pg.wg_start[k];
+  const int gs = wg % (a.Hkv * S);
+  const int blk = wg / (a.Hkv * S);
+  const int g = gs / S, s = gs % S;
   const int tile = blk * kWaves + wave;
-  if (tile >= a.tiles) return;  // no barrier in this kernel
-  const int cols = a.batch * a.G;
+  if (tile >= a.pg.tiles[k]) return;  // no barrier in this kernel
+  const int b0 = a.pg.req_start[k];
+  const int nreq = a.pg.req_end[k] - b0;
+  const int cols = nreq * a.G;
   const int col = tile * kTileCols + n;
-  const int b = col / a.G;
-  const int64_t row = static_cast<int64_t>(b) * a.Hq + g * a.G + (col - b * a.G);
+  const int bl = col / a.G;  // request within the group
+  const int64_t row = static_cast<int64_t>(b0 + bl) * a.Hq + g * a.G + (col - bl * a.G);
+  const int32_t* prefix_pages = a.page_table + static_cast<int64_t>(b0) * a.max_pages;
   bf16x8_t qf[4];
   {
     const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(a.q + (col < cols ? row : 0) * kHeadDim +
@@ -1350,8 +1402,8 @@ void prefix_kernel(PrefixArgs a) {
     for (int kk = 0; kk < 4; ++kk)
       qf[kk] = __builtin_bit_cast(bf16x8_t, col < cols ? qrow[kk] : u32x4_t{0u, 0u, 0u, 0u});
   }
-  const int p0 = static_cast<int>(static_cast<int64_t>(s) * a.P0 / a.S);
-  const int p1 = static_cast<int>(static_cast<int64_t>(s + 1) * a.P0 / a.S);
+  const int p0 = static_cast<int>(static_cast<int64_t>(s) * P0 / S);
+  const int p1 = static_cast<int>(static_cast<int64_t>(s + 1) * P0 / S);
   const float sc = a.sm_scale * (a.k_scale ? uniform_load(a.k_scale, g) : 1.0f) * kLog2e;
 
   // pages in flight: the two of one step (a deeper ring measured no faster:
@@ -1360,7 +1412,7 @@ void prefix_kernel(PrefixArgs a) {
   u32x4_t kr[R][NC], vr[R][NC];
   bool okp[R];
   auto issue = [&](int slot, int p) {
-    const int pid = p < p1 ? uniform_load(a.prefix_pages, p) : -1;
+    const int pid = p < p1 ? uniform_load(prefix_pages, p) : -1;
     const bool ok = static_cast<unsigned>(pid) < static_cast<unsigned>(a.num_pages);
     const int64_t off = ok ? static_cast<int64_t>(pid) * a.page_stride + static_cast<int64_t>(g) * TB : 0;
     const auto krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_cache + off),
@@ -1462,7 +1514,8 @@ void prefix_kernel(PrefixArgs a) {
   const float l_tot = wave_sum_rows(l_run);
   if (col < cols) {
     // acc[t][i] of lane (n, qd) holds dim 32 qd + 8 i + t
-    const int64_t pidx = static_cast<int64_t>(s) * a.batch * a.Hq + row;
+    const int64_t pidx = a.pg.part_base[k] + (static_cast<int64_t>(s) * nreq + bl) * a.Hq +
+                         (row - static_cast<int64_t>(b0 + bl) * a.Hq);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f32x4_t* po = reinterpret_cast<f32x4_t*>(a.ws_o + pidx * kHeadDim + 32 * qd + 8 * i);
@@ -1489,7 +1542,8 @@ struct CombineArgs {
   const uint8_t* abort;
   const float* v_scale;
   void* out;
-  int32_t batch, Hq, G, S, prefix_len, max_tokens, out_f32;
+  int32_t batch, Hq, G, max_tokens, out_f32;
+  PromptGroups pg;
 };
 
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
@@ -1500,21 +1554,26 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int d = 4 * static_cast<int>(idx % (kHeadDim / 4));
   const int b = static_cast<int>(row / a.Hq);
   const int h = static_cast<int>(row % a.Hq);
+  const int k = prompt_group(a.pg, b);
+  const int S = k < 0 ? 0 : a.pg.S[k];
+  const int prefix_len = k < 0 ? 0 : a.pg.prefix_len[k];
+  const int64_t nreq = k < 0 ? 0 : a.pg.req_end[k] - a.pg.req_start[k];
+  const int64_t base = k < 0 ? 0 : a.pg.part_base[k] + (b - a.pg.req_start[k]) * a.Hq + h;
   const int ctx = a.ctx_lens[b];
   const bool aborted = a.abort != nullptr && a.abort[b] != 0;
   f32x4_t res = {0.f, 0.f, 0.f, 0.f};
-  if (!aborted && ctx > a.prefix_len && ctx <= a.max_tokens) {
+  if (!aborted && ctx > prefix_len && ctx <= a.max_tokens) {
     const float vsc = a.v_scale ? a.v_scale[h / a.G] : 1.0f;
     float M = -INFINITY, L = 0.f;
     f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < a.S; s0 += kMergeUnroll) {
+    for (int s0 = 0; s0 < S; s0 += kMergeUnroll) {
       // issue the loads of several ranges before using any of them
       float m[kMergeUnroll], l[kMergeUnroll];
       f32x4_t o[kMergeUnroll];
 #pragma unroll
       for (int u = 0; u < kMergeUnroll; ++u) {
-        const bool has = s0 + u < a.S;
-        const int64_t pidx = (s0 + u) * rows + row;
+        const bool has = s0 + u < S;
+        const int64_t pidx = base + (s0 + u) * nreq * a.Hq;
         m[u] = has ? a.ws_ml[pidx * 2] : -INFINITY;
         l[u] = has ? a.ws_ml[pidx * 2 + 1] : 0.f;
         o[u] = has ? *reinterpret_cast<const f32x4_t*>(a.ws_o + pidx * kHeadDim + d)
@@ -1868,62 +1927,95 @@ fp8kv_status decode_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
 }
 
 // ---- the shared-prompt call ------------------------------------------------
-// page ranges of the prompt: enough workgroups to fill the device, at least
+// page ranges of a prompt: enough workgroups to fill the device, at least
 // kPrefixMinPages pages each
 constexpr int kPrefixMinPages = 8;
 
 struct SharedLayout {
-  size_t decode, o, ml, suf_out, suf_lse, total;
-  int32_t S, tiles, blocks;
+  size_t o, ml, suf_out, suf_lse, view_pt, view_ctx, total;
+  PromptGroups pg;
+  int64_t grid;
 };
 
-SharedLayout shared_layout(int32_t batch, int32_t Hq, int32_t Hkv, int32_t P0, int32_t workers) {
-  SharedLayout L;
+// Checks the group description (host arrays) and lays out the workspace.
+// Groups with an empty prompt are dropped (their requests attend as usual).
+fp8kv_status shared_layout(int32_t batch, int32_t Hq, int32_t Hkv, int32_t max_pages,
+                           int32_t num_groups, const int32_t* h_group_start,
+                           const int32_t* h_prefix_len, int32_t workers, SharedLayout& L) {
+  if (num_groups < 0 || num_groups > kMaxPromptGroups || (num_groups > 0 && (!h_group_start ||
+                                                                           !h_prefix_len)))
+    return FP8KV_INVALID_ARG;
+  if (num_groups > 0 && (h_group_start[0] < 0 || h_group_start[num_groups] > batch))
+    return FP8KV_INVALID_ARG;
   const int32_t G = Hq / Hkv;
-  L.tiles = static_cast<int32_t>((static_cast<int64_t>(batch) * G + kTileCols - 1) / kTileCols);
-  L.blocks = (L.tiles + kWaves - 1) / kWaves;
-  const int64_t base = static_cast<int64_t>(Hkv) * L.blocks;
-  const int64_t want = (workers / kWaves + base - 1) / base;
-  const int64_t most = P0 / kPrefixMinPages > 1 ? P0 / kPrefixMinPages : 1;
-  L.S = static_cast<int32_t>(want < 1 ? 1 : (want < most ? want : most));
+  PromptGroups& pg = L.pg;
+  pg.n = 0;
+  pg.wg_start[0] = 0;
+  pg.part_base[0] = 0;
+  int64_t wgs = 0, part = 0;
+  for (int k = 0; k < num_groups; ++k) {
+    const int32_t r0 = h_group_start[k], r1 = h_group_start[k + 1], len = h_prefix_len[k];
+    if (r1 < r0 || len < 0 || len % kPage != 0 || len / kPage > max_pages)
+      return FP8KV_INVALID_ARG;
+    if (len == 0 || r1 == r0) continue;
+    const int m = pg.n++;
+    pg.req_start[m] = r0;
+    pg.req_end[m] = r1;
+    pg.prefix_len[m] = len;
+    const int32_t P0 = len / kPage;
+    pg.tiles[m] = static_cast<int32_t>((static_cast<int64_t>(r1 - r0) * G + kTileCols - 1) / kTileCols);
+    pg.blocks[m] = (pg.tiles[m] + kWaves - 1) / kWaves;
+    const int64_t base = static_cast<int64_t>(Hkv) * pg.blocks[m];
+    const int64_t want = (workers / kWaves + base - 1) / base;
+    const int64_t most = P0 / kPrefixMinPages > 1 ? P0 / kPrefixMinPages : 1;
+    pg.S[m] = static_cast<int32_t>(want < 1 ? 1 : (want < most ? want : most));
+    pg.wg_start[m] = static_cast<int32_t>(wgs);
+    pg.part_base[m] = part;
+    wgs += base * pg.S[m];
+    part += static_cast<int64_t>(pg.S[m]) * (r1 - r0) * Hq;
+    if (wgs > 0x7FFFFFFF) return FP8KV_UNSUPPORTED;
+  }
+  pg.wg_start[pg.n] = static_cast<int32_t>(wgs);
+  pg.part_base[pg.n] = part;
+  L.grid = wgs;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t rows = static_cast<size_t>(batch) * Hq;
-  L.decode = up(workspace_layout(batch, Hq, Hkv, 1, workers).total);
-  L.o = L.decode;
-  L.ml = L.o + up(static_cast<size_t>(L.S) * rows * kHeadDim * sizeof(float));
-  L.suf_out = L.ml + up(static_cast<size_t>(L.S) * rows * 2 * sizeof(float));
+  L.o = up(workspace_layout(batch, Hq, Hkv, 1, workers).total);
+  L.ml = L.o + up(static_cast<size_t>(part) * kHeadDim * sizeof(float));
+  L.suf_out = L.ml + up(static_cast<size_t>(part) * 2 * sizeof(float));
   L.suf_lse = L.suf_out + up(rows * kHeadDim * sizeof(float));
-  L.total = L.suf_lse + up(rows * sizeof(float));
-  return L;
+  L.view_pt = L.suf_lse + up(rows * sizeof(float));
+  L.view_ctx = L.view_pt + up(static_cast<size_t>(batch) * max_pages * sizeof(int32_t));
+  L.total = L.view_ctx + up(static_cast<size_t>(batch) * sizeof(int32_t));
+  return FP8KV_OK;
 }
 
 fp8kv_status shared_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
                          const void* d_v_cache, const float* d_k_scale, const float* d_v_scale,
-                         const uint16_t* d_q, int32_t num_q_heads,
-                         const int32_t* d_prefix_pages, int32_t prefix_len,
+                         const uint16_t* d_q, int32_t num_q_heads, int32_t num_groups,
+                         const int32_t* h_group_start, const int32_t* h_prefix_len,
                          const int32_t* d_page_table, int32_t max_pages_per_seq,
                          const int32_t* d_ctx_lens, int32_t batch, float sm_scale,
                          const uint8_t* d_abort, void* d_out, int32_t out_dtype,
                          int32_t num_workers, void* d_workspace, size_t workspace_bytes,
                          hipStream_t stream) {
-  if (prefix_len < 0 || prefix_len % kPage != 0) return FP8KV_INVALID_ARG;
-  const int32_t P0 = prefix_len / kPage;
-  if (P0 == 0)
-    return decode_impl(desc, d_k_cache, d_v_cache, d_k_scale, d_v_scale, d_q, num_q_heads, 1,
-                       d_page_table, max_pages_per_seq, d_ctx_lens, batch, sm_scale, d_abort,
-                       d_out, out_dtype, num_workers, d_workspace, workspace_bytes, stream);
-  if (max_pages_per_seq < P0 || !d_prefix_pages) return FP8KV_INVALID_ARG;
-  // the own tokens: the table past the prompt's pages, f32 rows with their
-  // log-sum-exp, in the workspace (checked with the whole workspace below)
+  // the plain call's checks first (the workspace size once the groups are known)
   DecodeArgs a;
   int32_t workers = 0;
   fp8kv_status st = decode_setup(desc, d_k_cache, d_v_cache, d_k_scale, d_v_scale, d_q,
                                  num_q_heads, 1, d_page_table, max_pages_per_seq, d_ctx_lens,
                                  batch, sm_scale, d_abort, d_out, out_dtype, num_workers,
-                                 d_workspace, workspace_bytes, a, workers);
+                                 d_workspace, d_workspace ? SIZE_MAX : 0, a, workers);
+  if (st != FP8KV_OK) return st;
+  SharedLayout L;
+  st = shared_layout(batch, num_q_heads, desc->num_kv_heads, max_pages_per_seq, num_groups,
+                     h_group_start, h_prefix_len, workers, L);
   if (st != FP8KV_OK || batch == 0) return st;
-  const SharedLayout L = shared_layout(batch, num_q_heads, desc->num_kv_heads, P0, workers);
-  if (workspace_bytes < L.total) return FP8KV_WORKSPACE_TOO_SMALL;
+  const size_t need = L.pg.n == 0
+                          ? workspace_layout(batch, num_q_heads, desc->num_kv_heads, 1, workers).total
+                          : L.total;
+  if (workspace_bytes < need) return FP8KV_WORKSPACE_TOO_SMALL;
+  if (L.pg.n == 0) return decode_launch(a, desc->cache_dtype, workers, num_workers, stream);
   char* ws = static_cast<char*>(d_workspace);
 
   PrefixArgs pa;
@@ -1932,7 +2024,10 @@ fp8kv_status shared_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
   pa.k_scale = a.k_scale;
   pa.v_scale = a.v_scale;
   pa.q = d_q;
-  pa.prefix_pages = d_prefix_pages;
+  pa.page_table = d_page_table;
+  pa.ctx_lens = d_ctx_lens;
+  pa.view_pt = reinterpret_cast<int32_t*>(ws + L.view_pt);
+  pa.view_ctx = reinterpret_cast<int32_t*>(ws + L.view_ctx);
   pa.ws_o = reinterpret_cast<float*>(ws + L.o);
   pa.ws_ml = reinterpret_cast<float*>(ws + L.ml);
   pa.page_stride = a.page_stride;
@@ -1940,24 +2035,24 @@ fp8kv_status shared_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
   pa.Hq = num_q_heads;
   pa.Hkv = a.Hkv;
   pa.G = a.G;
-  pa.P0 = P0;
-  pa.S = L.S;
-  pa.tiles = L.tiles;
-  pa.blocks = L.blocks;
+  pa.max_pages = max_pages_per_seq;
   pa.num_pages = desc->num_pages;
   pa.sm_scale = sm_scale;
-  const int64_t pgrid = static_cast<int64_t>(a.Hkv) * L.S * L.blocks;
-  if (pgrid > 0x7FFFFFFF) return FP8KV_UNSUPPORTED;
+  pa.pg = L.pg;
   if (desc->cache_dtype == FP8KV_E4M3)
-    hipLaunchKernelGGL(prefix_kernel<FP8KV_E4M3>, dim3(pgrid), dim3(kThreads), 0, stream, pa);
+    hipLaunchKernelGGL(prefix_kernel<FP8KV_E4M3>, dim3(L.grid), dim3(kThreads), 0, stream, pa);
   else
-    hipLaunchKernelGGL(prefix_kernel<FP8KV_BF16>, dim3(pgrid), dim3(kThreads), 0, stream, pa);
+    hipLaunchKernelGGL(prefix_kernel<FP8KV_BF16>, dim3(L.grid), dim3(kThreads), 0, stream, pa);
+  st = launched();
+  if (st != FP8KV_OK) return st;
+  hipLaunchKernelGGL(view_kernel, dim3(batch), dim3(256), 0, stream, pa);
   st = launched();
   if (st != FP8KV_OK) return st;
 
-  a.page_table = d_page_table + P0;
-  a.max_pages = max_pages_per_seq - P0;
-  a.tok0 = prefix_len;
+  // the own tokens: the plain decode over the views, f32 rows with their
+  // log-sum-exp, into the workspace
+  a.page_table = pa.view_pt;
+  a.ctx_lens = pa.view_ctx;
   a.out = ws + L.suf_out;
   a.out_f32 = 1;
   a.lse = reinterpret_cast<float*>(ws + L.suf_lse);
@@ -1976,10 +2071,9 @@ fp8kv_status shared_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
   ca.batch = batch;
   ca.Hq = num_q_heads;
   ca.G = a.G;
-  ca.S = L.S;
-  ca.prefix_len = prefix_len;
   ca.max_tokens = max_pages_per_seq * kPage;
   ca.out_f32 = out_dtype == FP8KV_OUT_F32 ? 1 : 0;
+  ca.pg = L.pg;
   const int64_t threads = static_cast<int64_t>(batch) * num_q_heads * (kHeadDim / 4);
   hipLaunchKernelGGL(combine_kernel, dim3((threads + 255) / 256), dim3(256), 0, stream, ca);
   return launched();
@@ -2000,26 +2094,30 @@ size_t fp8kv_decode_workspace_size_q(const fp8kv_cache_desc* desc, int32_t batch
 }
 
 size_t fp8kv_decode_workspace_size_shared(const fp8kv_cache_desc* desc, int32_t batch,
-                                          int32_t num_q_heads, int32_t prefix_len,
-                                          int32_t num_workers) {
+                                          int32_t num_q_heads, int32_t max_pages_per_seq,
+                                          int32_t num_groups, const int32_t* h_group_start,
+                                          const int32_t* h_prefix_len, int32_t num_workers) {
   const size_t plain = decode_workspace(desc, batch, num_q_heads, 1, num_workers);
-  if (plain == 0 || prefix_len < 0 || prefix_len % kPage != 0) return 0;
-  if (prefix_len == 0) return plain;
-  const int32_t w = fp8kv_decode_num_workers(num_workers);
-  return shared_layout(batch, num_q_heads, desc->num_kv_heads, prefix_len / kPage, w).total;
+  if (plain == 0 || max_pages_per_seq < 0) return 0;
+  SharedLayout L;
+  if (shared_layout(batch, num_q_heads, desc->num_kv_heads, max_pages_per_seq, num_groups,
+                    h_group_start, h_prefix_len, fp8kv_decode_num_workers(num_workers),
+                    L) != FP8KV_OK)
+    return 0;
+  return L.pg.n == 0 ? plain : L.total;
 }
 
 fp8kv_status fp8kv_decode_attention_shared(
     const fp8kv_cache_desc* desc, const void* d_k_cache, const void* d_v_cache,
     const float* d_k_scale, const float* d_v_scale, const uint16_t* d_q, int32_t num_q_heads,
-    const int32_t* d_prefix_pages, int32_t prefix_len, const int32_t* d_page_table,
-    int32_t max_pages_per_seq, const int32_t* d_ctx_lens, int32_t batch, float sm_scale,
-    const uint8_t* d_abort, void* d_out, int32_t out_dtype, int32_t num_workers,
-    void* d_workspace, size_t workspace_bytes, hipStream_t stream) {
+    int32_t num_groups, const int32_t* h_group_start, const int32_t* h_prefix_len,
+    const int32_t* d_page_table, int32_t max_pages_per_seq, const int32_t* d_ctx_lens,
+    int32_t batch, float sm_scale, const uint8_t* d_abort, void* d_out, int32_t out_dtype,
+    int32_t num_workers, void* d_workspace, size_t workspace_bytes, hipStream_t stream) {
   return shared_impl(desc, d_k_cache, d_v_cache, d_k_scale, d_v_scale, d_q, num_q_heads,
-                     d_prefix_pages, prefix_len, d_page_table, max_pages_per_seq, d_ctx_lens,
-                     batch, sm_scale, d_abort, d_out, out_dtype, num_workers, d_workspace,
-                     workspace_bytes, stream);
+                     num_groups, h_group_start, h_prefix_len, d_page_table, max_pages_per_seq,
+                     d_ctx_lens, batch, sm_scale, d_abort, d_out, out_dtype, num_workers,
+                     d_workspace, workspace_bytes, stream);
 }
 
 fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc* desc, const void* d_k_cache,

@@ -286,37 +286,42 @@ fp8kv_status fp8kv_decode_attention_q(const fp8kv_cache_desc *desc, const void *
                                       size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
-/* A prompt shared by every request of the batch: prefix caching, where      */
-/* requests continuing the same prompt map the same cache pages (page "Kimi  */
-/* and GLM Reasoning Slimming: Hands-On Test", section "It Follows the Same  */
-/* Path as Cloudflare's Earlier Infire Optimizations").  Same result as      */
+/* Prompts shared by groups of requests: prefix caching, where requests      */
+/* continuing the same prompt map the same cache pages (page "Kimi and GLM   */
+/* Reasoning Slimming: Hands-On Test", section "It Follows the Same Path as  */
+/* Cloudflare's Earlier Infire Optimizations").  Same result as              */
 /* fp8kv_decode_attention (one new token per request), computed so that     */
-/* each of the prompt's pages is read once per kv-head for the whole batch:  */
-/* the (request, q-head) pairs form the MFMA columns over those pages, the   */
-/* requests' own tokens are attended as usual, and the two parts are joined  */
-/* by their log-sum-exp.                                                     */
-/*   d_prefix_pages: int32 [prefix_len/16], the prompt's page ids; every    */
-/*   request's table holds these ids in its first prefix_len/16 entries (the */
-/*   caller's contract; the tag check reads each request's own table).      */
-/*   prefix_len: a multiple of 16, at most 16*max_pages_per_seq; 0 is        */
-/*   fp8kv_decode_attention.  Rows of requests whose context does not extend */
-/*   past the prompt (ctx <= prefix_len), of aborted requests and of         */
-/*   contexts the table cannot hold are +0.                                  */
-/*   d_workspace: at least fp8kv_decode_workspace_size_shared() bytes (0    */
-/*   for invalid arguments).  Errors as fp8kv_decode_attention, and           */
-/*   FP8KV_INVALID_ARG for a bad prefix_len or a null d_prefix_pages.        */
+/* each of a prompt's pages is read once per kv-head for its whole group:    */
+/* the group's (request, q-head) pairs form the MFMA columns over those      */
+/* pages, each request's own tokens are attended as usual, and the two parts */
+/* are joined by their log-sum-exp.                                          */
+/*   num_groups <= 32; h_group_start: host int32 [num_groups+1], group k =   */
+/*   requests [h_group_start[k], h_group_start[k+1]) (non-decreasing, within  */
+/*   the batch; requests outside every group have no shared prompt);         */
+/*   h_prefix_len: host int32 [num_groups], tokens of group k's prompt, a     */
+/*   multiple of 16, at most 16*max_pages_per_seq (0: no shared prompt).      */
+/*   Every request of group k lists the prompt's prefix_len/16 pages first in */
+/*   its table; they are read from the table of the group's first request    */
+/*   (the caller's contract; the tag check reads each request's own table).  */
+/*   Rows of requests whose context does not extend past their prompt (ctx <= */
+/*   prefix_len), of aborted requests and of contexts the table cannot hold   */
+/*   are +0.  The host arrays are read during the call only.                 */
+/*   d_workspace: at least fp8kv_decode_workspace_size_shared() bytes (same  */
+/*   groups; 0 for invalid arguments).  Errors as fp8kv_decode_attention,     */
+/*   and FP8KV_INVALID_ARG for a bad group description.                      */
 /* ------------------------------------------------------------------------ */
 size_t fp8kv_decode_workspace_size_shared(const fp8kv_cache_desc *desc, int32_t batch,
-                                          int32_t num_q_heads, int32_t prefix_len,
-                                          int32_t num_workers);
+                                          int32_t num_q_heads, int32_t max_pages_per_seq,
+                                          int32_t num_groups, const int32_t *h_group_start,
+                                          const int32_t *h_prefix_len, int32_t num_workers);
 
 fp8kv_status fp8kv_decode_attention_shared(
     const fp8kv_cache_desc *desc, const void *d_k_cache, const void *d_v_cache,
     const float *d_k_scale, const float *d_v_scale, const uint16_t *d_q, int32_t num_q_heads,
-    const int32_t *d_prefix_pages, int32_t prefix_len, const int32_t *d_page_table,
-    int32_t max_pages_per_seq, const int32_t *d_ctx_lens, int32_t batch, float sm_scale,
-    const uint8_t *d_abort, void *d_out, int32_t out_dtype, int32_t num_workers,
-    void *d_workspace, size_t workspace_bytes, hipStream_t stream);
+    int32_t num_groups, const int32_t *h_group_start, const int32_t *h_prefix_len,
+    const int32_t *d_page_table, int32_t max_pages_per_seq, const int32_t *d_ctx_lens,
+    int32_t batch, float sm_scale, const uint8_t *d_abort, void *d_out, int32_t out_dtype,
+    int32_t num_workers, void *d_workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Self-test of the on-read conversion: d_out[i] = the value the attention   */

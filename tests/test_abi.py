@@ -158,15 +158,19 @@ def test_prepared_launch_checks_once_and_keeps_its_tensors():
 
 
 def test_shared_prompt_workspace():
-    # the shared-prompt call's workspace: the plain decode's plus the prompt's partial
-    # states and the own-token rows; prompt lengths must be multiples of 16
+    # the shared-prompt call's workspace: the plain decode's plus the prompts'
+    # partial states, the own-token rows and views; groups are checked
     d = fp8kv.desc(4096, 8)
     ws = fp8kv.decode_workspace_size_shared
     plain = fp8kv.decode_workspace_size(d, 64, 64, 3072)
-    assert ws(d, 64, 64, 0, 3072) == plain
-    a, b = ws(d, 64, 64, 1024, 3072), ws(d, 64, 64, 16384, 3072)
+    assert ws(d, 64, 64, 1100, [0, 64], [0], 3072) == plain
+    assert ws(d, 64, 64, 1100, [0], [], 3072) == plain
+    a, b = ws(d, 64, 64, 1100, [0, 64], [1024], 3072), ws(d, 64, 64, 1100, [0, 64], [16384], 3072)
     assert plain < a <= b
-    assert a >= plain + 64 * 64 * (128 + 2) * 4 + 64 * 64 * (128 + 1) * 4
-    for bad in (8, -16, 17):
-        assert ws(d, 64, 64, bad, 3072) == 0
-    assert ws(d, 64, 66, 1024, 3072) == 0          # Hq % Hkv != 0
+    assert a >= plain + 64 * 64 * (128 + 2) * 4 + 64 * 64 * (128 + 1) * 4 + 64 * 1100 * 4
+    two = ws(d, 64, 64, 1100, [0, 30, 64], [1024, 2048], 3072)
+    assert two > plain
+    for gs, pl in (([0, 64], [8]), ([0, 64], [-16]), ([0, 64], [16 * 1101]), ([0, 70], [16]),
+                   ([10, 5], [16]), ([-1, 5], [16]), ([0] * 34, [16] * 33)):
+        assert ws(d, 64, 64, 1100, gs, pl, 3072) == 0, (gs, pl)
+    assert ws(d, 64, 66, 1100, [0, 64], [1024], 3072) == 0          # Hq % Hkv != 0

@@ -165,13 +165,16 @@ def _shared_state(Hq, Hkv, cache_dtype=0, B=5, prefix=48, suffix=40, seed=6):
     return w, st
 
 
-def _shared_call(fp8kv, w, st, out_dtype, workers=0, ctx=None, abort=None, prefix=None):
-    P0 = w.prefix_len // 16
+def _shared_call(fp8kv, w, st, out_dtype, workers=0, ctx=None, abort=None, prefix=None,
+                 groups=None):
+    """The shared-prompt call: by default one group (the whole batch) on the
+    workload's prompt; `groups` = (group_start, prefix_len) overrides it."""
     prefix = w.prefix_len if prefix is None else prefix
+    gs, pl = groups if groups is not None else ([0, w.B], [prefix])
     out = fp8kv.decode_attention_shared(
-        st.desc, st.K, st.V, st.k_scale, st.v_scale, st.q, st.page_table[0, :max(P0, 1)].contiguous(),
-        prefix, st.page_table, st.ctx_lens if ctx is None else ctx, abort=abort,
-        out_dtype=out_dtype, num_workers=workers)
+        st.desc, st.K, st.V, st.k_scale, st.v_scale, st.q, st.page_table,
+        st.ctx_lens if ctx is None else ctx, gs, pl, abort=abort, out_dtype=out_dtype,
+        num_workers=workers)
     torch.cuda.synchronize()
     return (out.view(torch.int16) if out.dtype == torch.bfloat16 else out).cpu().numpy()
 
@@ -213,7 +216,7 @@ def test_shared_call_edges():
     ref, _ = oracle.attention(Ko, Vo, st.k_scale_host, st.v_scale_host, w.q_bits(), w.page_table,
                               w.ctx_lens, SM_SCALE)
     check_outputs(o[[0, 2]], None, ref[[0, 2]])
-    assert fp8kv.decode_workspace_size_shared(st.desc, w.B, w.Hq, 8) == 0
+    assert fp8kv.decode_workspace_size_shared(st.desc, w.B, w.Hq, w.max_pages, [0, w.B], [8]) == 0
     for bad in (8, -16, 16 * (w.max_pages + 1)):
         with pytest.raises(fp8kv.Fp8kvError) as e:
             _shared_call(fp8kv, w, st, fp8kv.OUT_F32, prefix=bad)
@@ -245,3 +248,40 @@ def test_shared_call_full_size():
                                   w.ctx_lens[b:b + 1], SM_SCALE)
         err = check_outputs(o32[b, g * G:(g + 1) * G], None, ref[0])
         print(f"shared call full size b={b} g={g}: max abs err {err:.3e}")
+
+
+@pytest.mark.parametrize("cd", [0, 1])
+def test_shared_call_prompt_groups(cd):
+    """Three prompts continued by groups of 5, 2 and 9 requests, then 4 requests
+    without one, in a single call: every row against the oracle and the plain
+    call; an empty group description is the plain call (bitwise); groups may
+    skip requests and list prompts of 0 tokens; bad descriptions are rejected."""
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    import workloads
+    from workloads import device
+    from _helpers import oracle_state
+    w = workloads.shared_prompts([(5, 64), (2, 32), (9, 160)], plain=4, suffix_max=70, Hq=16, Hkv=4)
+    st = device.build(w, cache_dtype=cd)
+    st.step(check_tags=True)
+    torch.cuda.synchronize()
+    assert (st.abort.cpu().numpy() == 0).all()
+    Ko, Vo = oracle_state(w, st.k_scale_host, st.v_scale_host, cd)
+    ref, _ = oracle.attention(Ko, Vo, st.k_scale_host, st.v_scale_host, w.q_bits(), w.page_table,
+                              w.ctx_lens, SM_SCALE, cache_dtype=cd)
+    plain = st.decode(True, out_dtype=fp8kv.OUT_F32).cpu().numpy()
+    groups = ([0, 5, 7, 16], [64, 32, 160])
+    for nw in (0, 12):
+        o32 = _shared_call(fp8kv, w, st, fp8kv.OUT_F32, nw, groups=groups)
+        o16 = _shared_call(fp8kv, w, st, fp8kv.OUT_BF16, nw, groups=groups).view(np.uint16)
+        err = check_outputs(o32, o16, ref)
+        assert np.abs(o32 - plain).max() <= 1e-5
+        print(f"3 prompt groups cache={cd} workers={nw}: max abs err {err:.3e}")
+    assert np.array_equal(_shared_call(fp8kv, w, st, fp8kv.OUT_F32, groups=([0], [])), plain)
+    # the middle group attended as usual (prompt of 0 tokens), the last one in part
+    o = _shared_call(fp8kv, w, st, fp8kv.OUT_F32, groups=([0, 5, 7, 12], [64, 0, 160]))
+    assert np.abs(o - plain).max() <= 1e-5
+    check_outputs(o, None, ref)
+    for gs, pl in (([0, 5, 3], [64, 32]), ([0, 5, 30], [64, 32]), ([0, 5], [24])):
+        with pytest.raises(fp8kv.Fp8kvError) as e:
+            _shared_call(fp8kv, w, st, fp8kv.OUT_F32, groups=(gs, pl))
+        assert e.value.status == -1

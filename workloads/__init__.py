@@ -190,9 +190,30 @@ class Workload:
     D: int = D_HEAD
     S: int = PAGE
     # tokens [0, prefix_len) of every request are one common stream (a shared
-    # prompt); prefix_shared: their pages are the same physical pages for all
+    # prompt); prefix_shared: their pages are the same physical pages for all.
+    # With prompt_of (one prompt id per request, -1 for none) and prompt_lens,
+    # each request continues its own prompt instead.
     prefix_len: int = 0
     prefix_shared: bool = False
+    prompt_of: Optional[np.ndarray] = None
+    prompt_lens: tuple = ()
+
+    def prompt(self, b: int):
+        """(prompt id, prompt tokens) of request b; (-1, 0) without one."""
+        if self.prompt_of is None:
+            return (0, self.prefix_len) if self.prefix_len > 0 else (-1, 0)
+        k = int(self.prompt_of[b])
+        return (k, int(self.prompt_lens[k])) if k >= 0 else (-1, 0)
+
+    def first_of_prompt(self, b: int) -> bool:
+        """Whether b is the first request of its prompt (the one whose appends
+        write the shared pages)."""
+        k, _ = self.prompt(b)
+        if k < 0:
+            return True
+        if self.prompt_of is None:
+            return b == 0
+        return int(np.flatnonzero(self.prompt_of == k)[0]) == b
 
     @property
     def G(self) -> int:
@@ -223,13 +244,13 @@ class Workload:
     def _kv_key(self, which: str, b: int) -> int:
         return stream_key(self.seed, _T_K if which == "k" else _T_V, b)
 
-    def _prefix_key(self, which: str) -> int:
-        return stream_key(self.seed, _T_K if which == "k" else _T_V, _PREFIX_ROW)
+    def _prefix_key(self, which: str, k: int = 0) -> int:
+        return stream_key(self.seed, _T_K if which == "k" else _T_V, _PREFIX_ROW + k)
 
-    def _split(self, t0: int, t1: int):
-        """[t0, t1) as (key row, start, end) runs: the common prefix stream, then
-        the request's own stream (its counters keep their token positions)."""
-        p = self.prefix_len
+    def _split(self, b: int, t0: int, t1: int):
+        """[t0, t1) as (prompt stream?, start, end) runs: the request's prompt
+        stream, then its own stream (counters keep their token positions)."""
+        _, p = self.prompt(b)
         runs = []
         if t0 < min(t1, p):
             runs.append((True, t0, min(t1, p)))
@@ -245,9 +266,10 @@ class Workload:
         for saturation, 4 values of that token in kv-head 0 are replaced by
         +-25 after scale calibration (they are excluded from amax)."""
         per_tok = self.Hkv * self.D
-        parts = [draw_bits(self._prefix_key(which) if pre else self._kv_key(which, b),
+        k, _ = self.prompt(b)
+        parts = [draw_bits(self._prefix_key(which, k) if pre else self._kv_key(which, b),
                            a * per_tok, (c - a) * per_tok, backend, device, self.outlier_per_65536)
-                 for pre, a, c in self._split(t0, t1)]
+                 for pre, a, c in self._split(b, t0, t1)]
         if len(parts) == 1:
             bits = parts[0]
         elif backend == "numpy":
@@ -275,10 +297,11 @@ class Workload:
         kv-head only: shape [t][D]."""
         d = np.arange(self.D, dtype=np.uint64)[None, :]
         parts = []
-        for pre, a, c in self._split(t0, t1):
+        kp, _ = self.prompt(b)
+        for pre, a, c in self._split(b, t0, t1):
             t = np.arange(a, c, dtype=np.uint64)[:, None]
             ctr = (t * np.uint64(self.Hkv) + np.uint64(g)) * np.uint64(self.D) + d
-            key = self._prefix_key(which) if pre else self._kv_key(which, b)
+            key = self._prefix_key(which, kp) if pre else self._kv_key(which, b)
             parts.append(draw_bits_at(key, ctr.ravel(), self.outlier_per_65536))
         bits = (np.concatenate(parts) if parts else np.zeros(0, np.uint16)).reshape(t1 - t0, self.D)
         L = int(self.ctx_before[b])
@@ -456,6 +479,51 @@ def shared_prefix(B: int = 64, prefix_len: int = 16384, suffix_max: int = 2048, 
     return Workload(name=name, seed=seed, B=B, Hq=Hq, Hkv=Hkv, ctx_before=L, num_pages=pool,
                     page_table=pt, expected_tags=etag, pool_tags=tags,
                     stale=np.zeros(pt.shape, bool), prefix_len=prefix_len, prefix_shared=shared)
+
+
+def shared_prompts(groups, plain: int = 0, suffix_max: int = 256, Hq: int = 8, Hkv: int = 2,
+                   seed: int = 9) -> Workload:
+    """Several prompts, each continued by a group of requests that map its pages
+    (groups: list of (requests, prompt tokens), prompt tokens a multiple of
+    16), then `plain` requests without a shared prompt.  Everyone has
+    U[16, suffix_max] own tokens (plain requests: that many in total)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    prompt_of, L = [], []
+    for k, (n, plen) in enumerate(groups):
+        assert plen % PAGE == 0
+        prompt_of += [k] * n
+        L += list(plen + rng.integers(16, suffix_max, size=n, endpoint=True))
+    prompt_of += [-1] * plain
+    L += list(rng.integers(16, suffix_max, size=plain, endpoint=True))
+    L = np.array(L, np.int32)
+    prompt_of = np.array(prompt_of, np.int32)
+    B = len(L)
+    n_pages = (L + 1 + PAGE - 1) // PAGE
+    P0 = np.array([groups[k][1] // PAGE if k >= 0 else 0 for k in prompt_of], np.int64)
+    pool = int((n_pages - P0).sum()) + sum(p // PAGE for _, p in groups)
+    perm = rng.permutation(pool).astype(np.int32)
+    pt = np.full((B, int(n_pages.max())), -1, np.int32)
+    off = 0
+    shared = {}
+    for k, (_, plen) in enumerate(groups):
+        shared[k] = perm[off: off + plen // PAGE]
+        off += plen // PAGE
+    for b in range(B):
+        k = int(prompt_of[b])
+        p0 = int(P0[b])
+        if k >= 0:
+            pt[b, :p0] = shared[k]
+        own = int(n_pages[b]) - p0
+        pt[b, p0: p0 + own] = perm[off: off + own]
+        off += own
+    tags = rng.integers(0, 2**32, size=pool, dtype=np.uint64).astype(np.uint32)
+    etag = np.zeros(pt.shape, np.uint32)
+    used = pt >= 0
+    etag[used] = tags[pt[used]]
+    return Workload(name=f"shared_prompts_{len(groups)}", seed=seed, B=B, Hq=Hq, Hkv=Hkv,
+                    ctx_before=L, num_pages=pool, page_table=pt, expected_tags=etag,
+                    pool_tags=tags, stale=np.zeros(pt.shape, bool), prefix_shared=True,
+                    prompt_of=prompt_of, prompt_lens=tuple(p for _, p in groups))
 
 
 def custom(name: str, ctx_before, Hq: int, Hkv: int, seed: int = 7,

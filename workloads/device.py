@@ -162,7 +162,7 @@ def kv_amax(w: Workload, which: str, device) -> np.ndarray:
     am = torch.zeros(w.Hkv, dtype=torch.float32, device=device)
     for b in range(w.B):
         n = int(w.ctx_before[b]) + 1
-        first = w.prefix_len if b > 0 else 0      # a common prompt counts once
+        first = 0 if w.first_of_prompt(b) else w.prompt(b)[1]   # a prompt counts once
         x = _bf16(w.kv_tokens(which, b, first, n, "torch", device, with_saturation=False))
         am = torch.maximum(am, x.float().abs().amax(dim=(0, 2)))
     return am.cpu().numpy()
@@ -192,7 +192,7 @@ def build(w: Workload, cache_dtype: int = fp8kv.E4M3, device="cuda", num_workers
         for b in range(w.B):
             L = int(w.ctx_before[b])
             # pages of a shared prompt are written once, through the first request
-            first = w.prefix_len if (w.prefix_shared and b > 0) else 0
+            first = 0 if (not w.prefix_shared or w.first_of_prompt(b)) else w.prompt(b)[1]
             for t0 in range(first, L, fill_chunk_tokens):
                 t1 = min(L, t0 + fill_chunk_tokens)
                 ks_rows.append(w.kv_tokens("k", b, t0, t1, "torch", device).contiguous())
