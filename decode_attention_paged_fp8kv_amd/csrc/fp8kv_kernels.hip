@@ -455,11 +455,8 @@ struct DecodeArgs {
   // other tokens
   float* lse;
   int64_t page_stride;
-  // qlen: new tokens (queries) per request; C = G * qlen MFMA columns used.
-  // The page table is read from column 0 with row stride pt_stride, max_pages
-  // columns at most; its first page holds token tok0 of the request (ctx_lens
-  // count from token 0), so tok0 > 0 views a table past some leading pages.
-  int32_t batch, max_pages, pt_stride, tok0, num_pages, Hq, Hkv, G, qlen, C, out_f32;
+  // qlen: new tokens (queries) per request; C = G * qlen MFMA columns used
+  int32_t batch, max_pages, num_pages, Hq, Hkv, G, qlen, C, out_f32;
   float sm_scale;
 };
 
@@ -498,7 +495,7 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ int live_pages(const DecodeArgs& a, int b) {
   // the flag is loaded next to the length (without an abort array, from a
   // byte of the length itself, and ignored), not after it
-  const int ctx = a.ctx_lens[b] - a.tok0;
+  const int ctx = a.ctx_lens[b];
   const uint8_t flag =
       *(a.abort ? a.abort + b : reinterpret_cast<const uint8_t*>(a.ctx_lens + b));
   const int n = ctx > 0 ? (ctx + kPage - 1) / kPage : 0;
@@ -751,7 +748,7 @@ void decode_kernel(DecodeArgs a) {
     // a vector load: it retires right after the page loads issued before it,
     // which are waited for first anyway (page ids through the scalar cache
     // measured slower: 12 waves per CU contend for it)
-    if (J.real()) pid = a.page_table[static_cast<int64_t>(J.p.b) * a.pt_stride + J.page(wave)];
+    if (J.real()) pid = a.page_table[static_cast<int64_t>(J.p.b) * a.max_pages + J.page(wave)];
     J.advance(s_pre, B, a.Hkv, X1, wave);
     return pid;
   };
@@ -803,7 +800,7 @@ void decode_kernel(DecodeArgs a) {
     const int cnt = wave_count(P, wave);
     const int iters = (cnt + DEPTH - 1) / DEPTH * DEPTH;
     const int pg0 = static_cast<int>(P.ps - P.sx) + wave;  // my first page in the piece
-    const int ctx = uniform_load(a.ctx_lens, P.b) - a.tok0;
+    const int ctx = uniform_load(a.ctx_lens, P.b);
     // Q is waited for here, once per piece: vector loads retire in order, so
     // this also waits for the pages already in flight (a slice holds only a
     // few pieces).  Waiting at the first MFMA instead would put the wait
@@ -1848,8 +1845,6 @@ fp8kv_status decode_setup(const fp8kv_cache_desc* desc, const void* d_k_cache,
   a.page_stride = static_cast<int64_t>(desc->num_kv_heads) * tile_bytes(desc);
   a.batch = batch;
   a.max_pages = max_pages_per_seq;
-  a.pt_stride = max_pages_per_seq;
-  a.tok0 = 0;
   a.num_pages = desc->num_pages;
   a.Hq = num_q_heads;
   a.Hkv = desc->num_kv_heads;
