@@ -6,7 +6,7 @@ device memory and the current stream; nothing here computes.  If the library
 is missing the import fails -- there is no fallback.
 
 Names mirror the C ABI in ``include/fp8kv.h``:
-  Pool, verify_tags, append, verify_append, decode_attention,
+  Pool, verify_tags, append, verify_append, verify_append_q, decode_attention,
   decode_attention_q, decode_attention_shared, decode_workspace_size,
   decode_workspace_size_q, decode_workspace_size_shared,
   decode_num_workers, cache_offset, cache_bytes, debug_convert_e4m3;
@@ -93,6 +93,9 @@ _decode_shared = _sig("fp8kv_decode_attention_shared", _i32,
 _verify_append = _sig("fp8kv_verify_append", _i32,
                       [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _p,
                        _i32, _p, _p, _p])
+_verify_append_q = _sig("fp8kv_verify_append_q", _i32,
+                        [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p,
+                         _i32, _p, _i32, _p, _p, _p])
 _debug_convert = _sig("fp8kv_debug_convert_e4m3", _i32, [_p, _p, _i32, _i32, _p])
 
 
@@ -302,6 +305,30 @@ def verify_append(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, k_new, v_new
             _dev(ctx_lens, _I32, "ctx_lens"), B, _dev(pool_tags, _U32, "pool_tags"),
             _dev(abort, _U8, "abort"), _stream(stream))
     return _run(_verify_append, args, "verify_append", abort,
+                (d, k_cache, v_cache, k_scale, v_scale, k_new, v_new, new_pos, page_table,
+                 expected_tags, ctx_lens, pool_tags, abort), prepare)
+
+
+def verify_append_q(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, k_new, v_new, new_pos,
+                    page_table, expected_tags, ctx_lens, pool_tags, abort=None, stream=None,
+                    prepare: bool = False):
+    """Tag check + the append of q_len new tokens per request in one launch:
+    k_new / v_new [B][q_len][Hkv][128], token i of request b at position
+    new_pos[b] + i; returns the uint8 abort tensor [B]."""
+    B, T = k_new.shape[0], k_new.shape[1]
+    if abort is None:
+        abort = torch.empty(B, dtype=torch.uint8, device=ctx_lens.device)
+    fp8 = d.cache_dtype == E4M3
+    args = (ctypes.byref(d), _dev(k_cache, _U8 + _BITS16, "k_cache"),
+            _dev(v_cache, _U8 + _BITS16, "v_cache"),
+            _dev(k_scale, _F32, "k_scale", allow_none=not fp8),
+            _dev(v_scale, _F32, "v_scale", allow_none=not fp8),
+            _dev(k_new, _BITS16, "k_new"), _dev(v_new, _BITS16, "v_new"),
+            _dev(new_pos, _I32, "new_pos"), T, _dev(page_table, _I32, "page_table"),
+            _dev(expected_tags, _U32, "expected_tags"), page_table.shape[1],
+            _dev(ctx_lens, _I32, "ctx_lens"), B, _dev(pool_tags, _U32, "pool_tags"),
+            _dev(abort, _U8, "abort"), _stream(stream))
+    return _run(_verify_append_q, args, "verify_append_q", abort,
                 (d, k_cache, v_cache, k_scale, v_scale, k_new, v_new, new_pos, page_table,
                  expected_tags, ctx_lens, pool_tags, abort), prepare)
 

@@ -348,7 +348,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 struct VerifyAppendArgs {
   VerifyArgs v;
   AppendArgs w;
-  const int32_t* new_pos;  // position of each request's new token
+  const int32_t* new_pos;  // position of each request's first new token
+  int32_t qlen;            // new tokens per request (k_new: [B][qlen][Hkv][128])
 };
 
 // The check still runs as its own batched pass ahead of attention; fusing it
@@ -361,8 +362,13 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_append_kernel(VerifyApp
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int ctx = a.v.ctx_lens[b];
-  const int pos = a.new_pos[b];
-  const bool pos_ok = pos >= 0 && pos / kPage < a.w.max_pages;
+  const int pos0 = a.new_pos[b];
+  // items: (new token, kv-head, 4 dims); a thread takes items tid, tid + 512, ..
+  const int per_tok = a.w.Hkv * (kHeadDim / 4);
+  const int items = a.qlen * per_tok;
+  const int tok = tid / per_tok;  // of the first item
+  const int pos = pos0 + tok;
+  const bool pos_ok = pos0 >= 0 && pos / kPage < a.w.max_pages;
   const int n = ctx < 0 ? 0 : (ctx + a.v.page_size - 1) / a.v.page_size;
   int bad = (ctx < 0 || n > a.v.max_pages) ? 1 : 0;
   const int nchk = bad ? 0 : n;
@@ -379,9 +385,10 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_append_kernel(VerifyApp
   }
   // 2. this thread's share of the append (4 dims of one kv-head): the token's
   //    inputs and its page id
-  const bool mine = tid < a.w.Hkv * (kHeadDim / 4);
-  const int h = tid >> 5, c = tid & 31;
-  const int64_t src = (static_cast<int64_t>(b) * a.w.Hkv + h) * kHeadDim + 4 * c;
+  const bool mine = tid < items;
+  const int h = (tid - tok * per_tok) >> 5, c = tid & 31;
+  const int64_t src =
+      ((static_cast<int64_t>(b) * a.qlen + tok) * a.w.Hkv + h) * kHeadDim + 4 * c;
   u32x2_t kin = {0u, 0u}, vin = {0u, 0u};
   int32_t pid = -1;
   if (mine && pos_ok) {
@@ -414,9 +421,24 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_append_kernel(VerifyApp
     bad |= check_round(a.v, pt, et, nchk, i0);
   bad = __syncthreads_or(bad);
   if (tid == 0) a.v.abort[b] = static_cast<uint8_t>(bad ? 1 : 0);
-  if (bad || !mine || !pos_ok) return;
-  if (static_cast<unsigned>(pid) >= static_cast<unsigned>(a.w.num_pages)) return;
-  append_store4<CACHE>(a.w, prep, h, c, pid, pos % kPage);
+  if (bad) return;
+  if (mine && pos_ok && static_cast<unsigned>(pid) < static_cast<unsigned>(a.w.num_pages))
+    append_store4<CACHE>(a.w, prep, h, c, pid, pos % kPage);
+  // more new tokens than one pass of the workgroup: the rest after the check
+  for (int it = tid + kVerifyThreads; it < items; it += kVerifyThreads) {
+    const int t = it / per_tok;
+    const int hh = (it - t * per_tok) >> 5, cc = it & 31;
+    const int p = pos0 + t;
+    if (pos0 < 0 || p / kPage >= a.w.max_pages) continue;
+    const int32_t pg = a.w.page_table[static_cast<int64_t>(b) * a.w.max_pages + p / kPage];
+    if (static_cast<unsigned>(pg) >= static_cast<unsigned>(a.w.num_pages)) continue;
+    const int64_t sx = ((static_cast<int64_t>(b) * a.qlen + t) * a.w.Hkv + hh) * kHeadDim + 4 * cc;
+    const Chunk4 q = append_encode4<CACHE>(*reinterpret_cast<const u32x2_t*>(a.w.k_new + sx),
+                                           *reinterpret_cast<const u32x2_t*>(a.w.v_new + sx),
+                                           CACHE == FP8KV_E4M3 ? a.w.k_scale[hh] : 1.0f,
+                                           CACHE == FP8KV_E4M3 ? a.w.v_scale[hh] : 1.0f);
+    append_store4<CACHE>(a.w, q, hh, cc, pg, p % kPage);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -2143,17 +2165,17 @@ fp8kv_status fp8kv_decode_attention_q(const fp8kv_cache_desc* desc, const void* 
                      d_out, out_dtype, num_workers, d_workspace, workspace_bytes, stream);
 }
 
-fp8kv_status fp8kv_verify_append(const fp8kv_cache_desc* desc, void* d_k_cache, void* d_v_cache,
+fp8kv_status fp8kv_verify_append_q(const fp8kv_cache_desc* desc, void* d_k_cache, void* d_v_cache,
                                  const float* d_k_scale, const float* d_v_scale,
                                  const uint16_t* d_k_new, const uint16_t* d_v_new,
-                                 const int32_t* d_new_pos, const int32_t* d_page_table,
+                                 const int32_t* d_new_pos, int32_t q_len, const int32_t* d_page_table,
                                  const uint32_t* d_expected_tags, int32_t max_pages_per_seq,
                                  const int32_t* d_ctx_lens, int32_t batch,
                                  const uint32_t* d_pool_tags, uint8_t* d_abort,
                                  hipStream_t stream) {
   fp8kv_status st = check_desc(desc);
   if (st != FP8KV_OK) return st;
-  if (batch < 0 || max_pages_per_seq < 0) return FP8KV_INVALID_ARG;
+  if (batch < 0 || max_pages_per_seq < 0 || q_len <= 0) return FP8KV_INVALID_ARG;
   if (batch == 0) return FP8KV_OK;
   if (!d_k_cache || !d_v_cache || !d_k_new || !d_v_new || !d_new_pos || !d_ctx_lens ||
       !d_abort || !d_pool_tags || (max_pages_per_seq > 0 && (!d_page_table || !d_expected_tags)))
@@ -2180,6 +2202,7 @@ fp8kv_status fp8kv_verify_append(const fp8kv_cache_desc* desc, void* d_k_cache, 
   a.w.num_pages = desc->num_pages;
   a.w.Hkv = desc->num_kv_heads;
   a.new_pos = d_new_pos;
+  a.qlen = q_len;
   if (desc->cache_dtype == FP8KV_E4M3)
     hipLaunchKernelGGL(verify_append_kernel<FP8KV_E4M3>, dim3(batch), dim3(kVerifyThreads), 0,
                        stream, a);
@@ -2187,6 +2210,19 @@ fp8kv_status fp8kv_verify_append(const fp8kv_cache_desc* desc, void* d_k_cache, 
     hipLaunchKernelGGL(verify_append_kernel<FP8KV_BF16>, dim3(batch), dim3(kVerifyThreads), 0,
                        stream, a);
   return launched();
+}
+
+fp8kv_status fp8kv_verify_append(const fp8kv_cache_desc* desc, void* d_k_cache, void* d_v_cache,
+                                 const float* d_k_scale, const float* d_v_scale,
+                                 const uint16_t* d_k_new, const uint16_t* d_v_new,
+                                 const int32_t* d_new_pos, const int32_t* d_page_table,
+                                 const uint32_t* d_expected_tags, int32_t max_pages_per_seq,
+                                 const int32_t* d_ctx_lens, int32_t batch,
+                                 const uint32_t* d_pool_tags, uint8_t* d_abort,
+                                 hipStream_t stream) {
+  return fp8kv_verify_append_q(desc, d_k_cache, d_v_cache, d_k_scale, d_v_scale, d_k_new, d_v_new,
+                               d_new_pos, 1, d_page_table, d_expected_tags, max_pages_per_seq,
+                               d_ctx_lens, batch, d_pool_tags, d_abort, stream);
 }
 
 fp8kv_status fp8kv_debug_convert_e4m3(const uint8_t* d_codes, float* d_out, int32_t n,

@@ -213,6 +213,21 @@ fp8kv_status fp8kv_verify_append(const fp8kv_cache_desc *desc, void *d_k_cache, 
                                  const uint32_t *d_pool_tags, uint8_t *d_abort,
                                  hipStream_t stream);
 
+/* The same with q_len new tokens per request (several tokens checked in one  */
+/* step, speculative decoding): d_k_new/d_v_new BF16 [batch][q_len][Hkv][128], */
+/* token i of request b goes to position d_new_pos[b] + i, all only if the    */
+/* request's check passed.  q_len = 1 is fp8kv_verify_append.  Errors as      */
+/* above, and FP8KV_INVALID_ARG for q_len < 1.                                */
+fp8kv_status fp8kv_verify_append_q(const fp8kv_cache_desc *desc, void *d_k_cache,
+                                   void *d_v_cache, const float *d_k_scale,
+                                   const float *d_v_scale, const uint16_t *d_k_new,
+                                   const uint16_t *d_v_new, const int32_t *d_new_pos,
+                                   int32_t q_len, const int32_t *d_page_table,
+                                   const uint32_t *d_expected_tags, int32_t max_pages_per_seq,
+                                   const int32_t *d_ctx_lens, int32_t batch,
+                                   const uint32_t *d_pool_tags, uint8_t *d_abort,
+                                   hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Paged decode attention (one query token per request) over the cache,      */
 /* converting e4m3 on read.  For request b and q-head h (kv-head g = h/G):  */

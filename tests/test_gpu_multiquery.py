@@ -201,3 +201,43 @@ def test_ragged_64_full_size(T):
         cols = slice(g * G, (g + 1) * G)
         err = check_outputs(o32[b, :, cols], o16[b, :, cols], ref[0])
         print(f"ragged q_len={T} b={b} g={g} ctx={n} max abs err {err:.3e}")
+
+
+@pytest.mark.parametrize("Hq,Hkv,T", [(64, 8, 1), (64, 8, 2), (64, 8, 4), (8, 2, 5), (16, 16, 2)])
+def test_fused_check_and_multi_token_append(Hq, Hkv, T):
+    """fp8kv_verify_append_q (one launch) writes the same cache bytes and abort
+    flags as the tag check followed by the gated append of the T tokens, with
+    stale entries in some requests (their tokens are not written)."""
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    hist = [20, 33, 50, 7, 100, 64]
+    outs = []
+    for fused in (True, False):
+        st = _setup(fp8kv, hist, T, Hq, Hkv)
+        B = st["B"]
+        tags = np.random.default_rng(5).integers(0, 2 ** 32, st["N"], dtype=np.uint64).astype(np.uint32)
+        et = np.where(st["pt"] >= 0, tags[np.clip(st["pt"], 0, None)], 0).astype(np.uint32)
+        tags[st["pt"][1, 0]] += np.uint32(1)            # request 1 holds a stale entry
+        tags[st["pt"][4, -1 if st["pt"][4, -1] >= 0 else 0]] += np.uint32(1)
+        pos = (st["ctx"] - T).astype(np.int32)
+        kb = np.stack([st["toks"]["k"][b][pos[b]:pos[b] + T] for b in range(B)])
+        vb = np.stack([st["toks"]["v"][b][pos[b]:pos[b] + T] for b in range(B)])
+        K, V = fp8kv.new_cache(st["d"], "cuda")       # fresh pools: only this step's writes
+        dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        args = (st["d"], K, V, st["ks"], st["vs"])
+        et_d, tags_d = dev(et.view(np.int32)), dev(tags.view(np.int32))
+        if fused:
+            ab = fp8kv.verify_append_q(*args, dev(kb.view(np.int16)), dev(vb.view(np.int16)),
+                                       dev(pos), st["pt_d"], et_d, st["ctx_d"], tags_d)
+        else:
+            ab = fp8kv.verify_tags(st["pt_d"], et_d, st["ctx_d"], tags_d)
+            seq = np.repeat(np.arange(B, dtype=np.int32), T)
+            p = (pos[:, None] + np.arange(T, dtype=np.int32)[None]).ravel().astype(np.int32)
+            fp8kv.append(*args, dev(kb.reshape(B * T, Hkv, 128).view(np.int16)),
+                         dev(vb.reshape(B * T, Hkv, 128).view(np.int16)), dev(seq), dev(p),
+                         st["pt_d"], abort=ab)
+        torch.cuda.synchronize()
+        outs.append((ab.cpu().numpy(), K.cpu().numpy(), V.cpu().numpy()))
+    (a0, k0, v0), (a1, k1, v1) = outs
+    assert list(a0) == [0, 1, 0, 0, 1, 0] and np.array_equal(a0, a1)
+    assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+    assert k0.any()

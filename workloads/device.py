@@ -95,7 +95,8 @@ class SpecStep:
     step is still L_b + 1, its newest q_len tokens (positions L_b+1-q_len ..
     L_b, fewer when the context is shorter) are appended by the step, and
     query i attends to the tokens up to its own.  Tag check and append are
-    separate launches (the fused launch appends one token per request)."""
+    one launch (fp8kv_verify_append_q) when every context holds q_len tokens,
+    else two."""
     base: DeviceStep
     q_len: int
     q: torch.Tensor             # [B][q_len][Hq][128]
@@ -105,6 +106,9 @@ class SpecStep:
     token_pos: torch.Tensor
     workspace: torch.Tensor
     out: torch.Tensor
+    k_new_q: Optional[torch.Tensor] = None   # [B][q_len][Hkv][128] for the fused launch
+    v_new_q: Optional[torch.Tensor] = None
+    first_pos: Optional[torch.Tensor] = None  # [B]: position of each first new token
 
     def verify(self, stream=None):
         self.base.verify(stream)
@@ -124,10 +128,19 @@ class SpecStep:
             abort=s.abort if use_abort else None, out=out, out_dtype=out_dtype,
             num_workers=s.num_workers, workspace=self.workspace, stream=stream)
 
-    def step(self, check_tags=True, out_dtype=fp8kv.OUT_BF16, stream=None):
-        if check_tags:
-            self.verify(stream)
-        self.append(use_abort=check_tags, stream=stream)
+    def verify_append(self, stream=None):
+        s = self.base
+        fp8kv.verify_append_q(s.desc, s.K, s.V, s.k_scale, s.v_scale, self.k_new_q, self.v_new_q,
+                              self.first_pos, s.page_table, s.expected_tags, s.ctx_lens,
+                              s.pool_tags, abort=s.abort, stream=stream)
+
+    def step(self, check_tags=True, out_dtype=fp8kv.OUT_BF16, stream=None, fused=True):
+        if check_tags and fused and self.k_new_q is not None:
+            self.verify_append(stream)
+        else:
+            if check_tags:
+                self.verify(stream)
+            self.append(use_abort=check_tags, stream=stream)
         return self.decode(use_abort=check_tags, out_dtype=out_dtype, stream=stream)
 
 
@@ -147,11 +160,15 @@ def build_spec(s: DeviceStep, q_len: int) -> SpecStep:
         raise ValueError(f"{w.Hq // w.Hkv} q-heads per kv-head x q_len {q_len} exceeds the "
                          "decode kernel's 32 columns")
     ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    full = bool((t1 - t0 == q_len).all())   # every request has q_len new tokens
     torch.cuda.synchronize()
     return SpecStep(base=s, q_len=q_len, q=w.q_bits_multi(q_len, "torch", dev), k_new=kn,
                     v_new=vn, token_seq=torch.from_numpy(seq).to(dev),
                     token_pos=torch.from_numpy(pos).to(dev), workspace=ws,
-                    out=torch.empty((w.B, q_len, w.Hq, 128), dtype=torch.bfloat16, device=dev))
+                    out=torch.empty((w.B, q_len, w.Hq, 128), dtype=torch.bfloat16, device=dev),
+                    k_new_q=kn.view(w.B, q_len, w.Hkv, 128) if full else None,
+                    v_new_q=vn.view(w.B, q_len, w.Hkv, 128) if full else None,
+                    first_pos=torch.from_numpy(t0.astype(np.int32)).to(dev) if full else None)
 
 
 def _bf16(t: torch.Tensor) -> torch.Tensor:
