@@ -432,6 +432,30 @@ def device_copy(n_bytes: int = 2 << 30):
             "gbps": round(2 * n_bytes / t / 1e9, 1)}
 
 
+def cpu_study(args):
+    """The oracle as it stands on the host, single-threaded and on all cores,
+    on bounded samples of the tiny, uniform, ragged and long workloads: context
+    for the GPU figures, not a target."""
+    import oracle
+    import workloads
+    res = {}
+    all_threads = oracle.num_threads()
+    for cfg in (1, 2, 3, 4):
+        w = workloads.make(cfg)
+        for threads in (1, all_threads):
+            oracle.set_num_threads(threads)
+            log(f"bench: CPU oracle, {w.name}, {threads} thread(s)")
+            res.setdefault(w.name, {})[f"{threads}_threads"] = cpu_baseline(w, target_s=5.0)
+    oracle.set_num_threads(all_threads)
+    print(json.dumps({
+        "metric": "CPU oracle (binary64, plain C + OpenMP over output rows): tokens/s and "
+                  "algorithmic GB/s on bounded samples",
+        "value": res[workloads.make(3).name][f"{all_threads}_threads"]["value"],
+        "unit": "tokens/s", "n_gpus": 0, "higher_is_better": True, "data": "synthetic",
+        "config": {"workload": "cpu_study", "threads": [1, all_threads]},
+        "value_is": f"ragged workload, {all_threads} threads", "by_workload": res}), flush=True)
+
+
 def cpu_baseline(w, target_s: float = 15.0):
     """The oracle as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -479,7 +503,11 @@ def cpu_baseline(w, target_s: float = 15.0):
         reqs.append(b)
         est += per_tok * int(w.ctx_lens[b])
     t = run(reqs)
+    mask = np.zeros(w.B, bool)
+    mask[reqs] = True
+    step_bytes, _ = alg_bytes(w, 0, False, active=mask)
     return {"value": len(reqs) / t, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "alg_gbps": round(step_bytes / t / 1e9, 4),
             "kind": "oracle",
             "sample": f"requests 0..{len(reqs) - 1} of the workload ({int(w.ctx_lens[reqs].sum())} "
                       f"attended tokens, all {w.Hq} q-heads): tag check + append + fp64 attention, "
@@ -513,6 +541,8 @@ def main():
     ap.add_argument("--accuracy-configs", type=int, nargs="+", default=[2, 3, 4])
     ap.add_argument("--shared-prefix", action="store_true",
                     help="cache reuse study: a prompt's pages shared by 64 requests vs copies")
+    ap.add_argument("--cpu-study", action="store_true",
+                    help="the oracle on the host, 1 thread and all cores, tiny/uniform/ragged/long")
     ap.add_argument("--qlen", type=int, default=1,
                     help="q_len > 1: speculative-verification study (q_len new tokens per "
                          "request checked in one step)")
@@ -540,6 +570,9 @@ def main():
     import workloads
     from workloads import device
 
+    if args.cpu_study:
+        cpu_study(args)
+        return
     torch.cuda.set_device(0)
     if args.loop:
         loop_study(args)

@@ -51,6 +51,8 @@ def lib():
                                        _p, _i32, _p, _i32, ctypes.c_float, _p, _p, _p, _p, _i32]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
+        L.oracle_set_num_threads.restype = None
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
@@ -173,3 +175,8 @@ def attention_multi(k_cache, v_cache, k_scale, v_scale, q, page_table, ctx_lens,
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the attention rows (timing only; results do not depend on it)."""
+    lib().oracle_set_num_threads(int(n))

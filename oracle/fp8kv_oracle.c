@@ -311,3 +311,13 @@ int oracle_num_threads(void) {
     return 1;
 #endif
 }
+
+/* Threads the attention rows are spread over (timing only; results do not
+ * depend on it: every row is computed by one thread in a fixed order). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

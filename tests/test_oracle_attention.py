@@ -263,3 +263,30 @@ def test_multi_queries_beyond_the_context_are_zero():
     got, gb = oracle.attention_multi(K, V, ks, vs, q, pt, L, SM)
     assert (got[0, :2] == 0).all() and (got[1, :1] == 0).all() and (gb[0, :2] == 0).all()
     assert (got[0, 2] != 0).any() and (got[1, 1] != 0).any()
+
+
+def test_thread_count_does_not_change_results():
+    """Attention rows are computed by one thread each in a fixed order, so the
+    thread count (timing only) leaves every bit unchanged."""
+    rng = np.random.default_rng(12)
+    B, Hq, Hkv, P = 5, 8, 2, 6
+    n = [3, 1, 6, 2, 5]
+    K, V = oracle.new_cache(40, Hkv)
+    K[:] = rng.integers(0, 0x7F, K.shape, dtype=np.uint8)
+    V[:] = rng.integers(0, 0x7F, V.shape, dtype=np.uint8)
+    pt = np.full((B, P), -1, np.int32)
+    perm = rng.permutation(40).astype(np.int32)
+    k = 0
+    for b in range(B):
+        pt[b, :n[b]] = perm[k:k + n[b]]
+        k += n[b]
+    ctx = np.array([16 * x - 3 for x in n], np.int32)
+    q = rng.integers(0, 0x4000, (B, Hq, 128), dtype=np.uint16)
+    ks = np.full(Hkv, 0.05, np.float32)
+    outs = []
+    base = oracle.num_threads()
+    for t in (1, max(2, base)):
+        oracle.set_num_threads(t)
+        outs.append(oracle.attention(K, V, ks, ks, q, pt, ctx, np.float32(0.088))[0])
+    oracle.set_num_threads(base)
+    assert np.array_equal(outs[0], outs[1])
