@@ -432,6 +432,21 @@ def device_copy(n_bytes: int = 2 << 30):
             "gbps": round(2 * n_bytes / t / 1e9, 1)}
 
 
+def stream_read(n_bytes: int = 4 << 30):
+    """The library's streaming-read reference over 4 GiB: 16-byte nontemporal
+    loads like the tile loads, no page indirection."""
+    import torch
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    x = torch.ones(n_bytes, dtype=torch.uint8, device="cuda")
+    sink = fp8kv.debug_read_bandwidth(x)
+    for _ in range(2):
+        fp8kv.debug_read_bandwidth(x, sink)
+    t = statistics.median(event_times([lambda: fp8kv.debug_read_bandwidth(x, sink)], 10)[0]) * 1e-3
+    del x, sink
+    torch.cuda.empty_cache()
+    return {"bytes_read": n_bytes, "us": round(t * 1e6, 1), "gbps": round(n_bytes / t / 1e9, 1)}
+
+
 def cpu_study(args):
     """The oracle as it stands on the host, single-threaded and on all cores,
     on bounded samples of the tiny, uniform, ragged and long workloads: context
@@ -709,6 +724,7 @@ def main():
             torch.cuda.empty_cache()
         res["uniform_32x8192"] = var
         res["device_copy"] = device_copy()
+        res["stream_read"] = stream_read()
     if not args.no_cpu_baseline and cfg == 3:
         log("bench: CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(w)

@@ -97,6 +97,8 @@ _verify_append_q = _sig("fp8kv_verify_append_q", _i32,
                         [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p,
                          _i32, _p, _i32, _p, _p, _p])
 _debug_convert = _sig("fp8kv_debug_convert_e4m3", _i32, [_p, _p, _i32, _i32, _p])
+_read_sink_words = _sig("fp8kv_debug_read_sink_words", _i32, [])
+_read_bandwidth = _sig("fp8kv_debug_read_bandwidth", _i32, [_p, ctypes.c_size_t, _p, _p])
 
 
 class Fp8kvError(RuntimeError):
@@ -489,6 +491,19 @@ def step(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, k_new, v_new, new_
                            abort=abort, out=out, out_dtype=out_dtype, sm_scale=sm_scale,
                            num_workers=num_workers, workspace=workspace, stream=stream)
     return out, abort
+
+
+def debug_read_bandwidth(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None):
+    """Streaming read of every byte of buf (a contiguous device tensor, size a
+    multiple of 16 bytes): the measurement reference for the tile loads.
+    Returns the sink words (an XOR of what was read)."""
+    if sink is None:
+        sink = torch.empty(int(_read_sink_words()), dtype=torch.int32, device=buf.device)
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    _check(_read_bandwidth(buf.data_ptr(), buf.numel() * buf.element_size(),
+                           _dev(sink, _I32, "sink"), _stream(stream)), "debug_read_bandwidth")
+    return sink
 
 
 def debug_convert_e4m3(codes: torch.Tensor, which: int, stream=None) -> torch.Tensor:

@@ -1623,6 +1623,41 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 // ---------------------------------------------------------------------------
 // self-test of the conversions used above
 // ---------------------------------------------------------------------------
+// Streaming-read reference: every byte of a buffer read once, as the tile
+// loads read (16-byte buffer loads with their cache policy, each wave a 4 KiB
+// block at a time, 4 blocks in flight), but in order and with no page
+// indirection; XOR-folded to one word per thread so nothing is optimised away.
+__global__ __launch_bounds__(256) void read_bandwidth_kernel(const uint8_t* buf, int64_t bytes,
+                                                             uint32_t* sink) {
+  constexpr int kBlock = 4096;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave =
+      __builtin_amdgcn_readfirstlane(static_cast<int>((blockIdx.x * 256 + threadIdx.x) >> 6));
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * 4;
+  const int64_t blocks = (bytes + kBlock - 1) / kBlock;
+  uint32_t x = 0;
+  for (int64_t b0 = wave; b0 < blocks; b0 += 4 * waves) {
+    u32x4_t v[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t b = b0 + u * waves;
+      const int64_t base = b < blocks ? b * kBlock : 0;
+      const int n = b < blocks ? static_cast<int>(bytes - base < kBlock ? bytes - base : kBlock) : 0;
+      const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(buf + base), (short)0, n,
+                                                        kRsrcWord3);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        v[u][k] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, k * 1024 + lane * 16, 0, kKvLoadPolicy));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x ^= v[u][k].x ^ v[u][k].y ^ v[u][k].z ^ v[u][k].w;
+  }
+  sink[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = x;
+}
+
 __global__ void debug_convert_kernel(const uint8_t* codes, float* out, int n, int which) {
   const int i = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (i >= n) return;
@@ -2223,6 +2258,19 @@ fp8kv_status fp8kv_verify_append(const fp8kv_cache_desc* desc, void* d_k_cache, 
   return fp8kv_verify_append_q(desc, d_k_cache, d_v_cache, d_k_scale, d_v_scale, d_k_new, d_v_new,
                                d_new_pos, 1, d_page_table, d_expected_tags, max_pages_per_seq,
                                d_ctx_lens, batch, d_pool_tags, d_abort, stream);
+}
+
+int32_t fp8kv_debug_read_sink_words(void) { return device_workers() / kWaves * 256; }
+
+fp8kv_status fp8kv_debug_read_bandwidth(const void* d_buf, size_t bytes, uint32_t* d_sink,
+                                        hipStream_t stream) {
+  if (!d_buf || !d_sink || bytes % 16 != 0) return FP8KV_INVALID_ARG;
+  if (bytes == 0) return FP8KV_OK;
+  const int32_t words = fp8kv_debug_read_sink_words();
+  if (words <= 0) return FP8KV_HIP_ERROR;
+  hipLaunchKernelGGL(read_bandwidth_kernel, dim3(words / 256), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(d_buf), static_cast<int64_t>(bytes), d_sink);
+  return launched();
 }
 
 fp8kv_status fp8kv_debug_convert_e4m3(const uint8_t* d_codes, float* d_out, int32_t n,

@@ -339,6 +339,20 @@ fp8kv_status fp8kv_decode_attention_shared(
     int32_t num_workers, void *d_workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Measurement reference: reads every byte of d_buf (bytes a multiple of 16, */
+/* 16-byte aligned) once, with the attention kernel's tile loads (16-byte    */
+/* buffer loads, same cache policy, 4 KiB per wave at a time) but in order   */
+/* and with no page indirection, and writes an XOR of what it read to d_sink */
+/* (uint32, fp8kv_debug_read_sink_words() of them).                           */
+/* Timing it gives the streaming-read rate the attention kernel is compared  */
+/* with.  FP8KV_INVALID_ARG for null pointers or a size not a multiple of 16. */
+/* ------------------------------------------------------------------------ */
+int32_t fp8kv_debug_read_sink_words(void);
+
+fp8kv_status fp8kv_debug_read_bandwidth(const void *d_buf, size_t bytes, uint32_t *d_sink,
+                                        hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Self-test of the on-read conversion: d_out[i] = the value the attention   */
 /* kernel's e4m3 -> bf16 (which = 0) or e4m3 -> f16 (which = 1) conversion   */
 /* gives for code d_codes[i], widened to fp32.  n a multiple of 4.           */

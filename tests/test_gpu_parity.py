@@ -231,6 +231,21 @@ def test_largest_batch(lib, dev):
     assert e.value.status == -2
 
 
+def test_read_reference_reads_every_byte_once(lib):
+    """The streaming-read reference: the XOR of its sink words is the XOR of all
+    words of the buffer (a chunk read twice or skipped would change it), for a
+    size that is not a multiple of the grid's stride."""
+    rng = np.random.default_rng(16)
+    n = (1 << 26) + 16 * 12345
+    host = rng.integers(0, 256, n, dtype=np.uint8)
+    buf = torch.from_numpy(host).cuda()
+    sink = _host(lib.debug_read_bandwidth(buf))
+    want = np.bitwise_xor.reduce(host.view(np.uint32))
+    assert np.bitwise_xor.reduce(sink.view(np.uint32)) == want
+    with pytest.raises(lib.Fp8kvError):
+        lib.debug_read_bandwidth(buf[:100])
+
+
 def test_empty_context_and_abort_rows_are_zero(lib, dev):
     w = workloads.custom("edge", [40, 100, 7, 300], Hq=8, Hkv=2, seed=3)
     st = dev.build(w, num_workers=8)
