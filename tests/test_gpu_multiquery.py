@@ -241,3 +241,27 @@ def test_fused_check_and_multi_token_append(Hq, Hkv, T):
     assert list(a0) == [0, 1, 0, 0, 1, 0] and np.array_equal(a0, a1)
     assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
     assert k0.any()
+
+
+def test_queries_with_nothing_to_see_give_zero_rows():
+    """A context shorter than q_len (the caller's lengths): the first queries see
+    no token and give +0 rows, the rest attend to their prefix, as the oracle."""
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    T = 4                                               # G 8 x q_len 4: all 32 columns
+    st = _setup(fp8kv, [0, 4, 40], T, 64, 8)
+    ctx = np.array([2, 8, 3], np.int32)                 # shorter than written: allowed
+    st["ctx_d"] = torch.from_numpy(ctx).cuda()
+    st["ctx"] = ctx
+    Ko, Vo = oracle.new_cache(st["N"], st["Hkv"])
+    for b in range(st["B"]):
+        c = int(ctx[b])
+        oracle.append(Ko, Vo, st["scale"]["k"], st["scale"]["v"], st["toks"]["k"][b][:c],
+                      st["toks"]["v"][b][:c], np.full(c, b, np.int32), np.arange(c, dtype=np.int32),
+                      st["pt"])
+    ref, _ = oracle.attention_multi(Ko, Vo, st["scale"]["k"], st["scale"]["v"], st["q"], st["pt"], ctx,
+                                    SM_SCALE)
+    for nw in (0, 8):
+        o = _run(st, fp8kv.OUT_F32, nw)
+        assert (o[0, :2] == 0).all() and (o[2, :1] == 0).all()
+        assert np.abs(o[0, 2:]).max() > 0 and np.abs(o[2, 1:]).max() > 0
+        check_outputs(o, None, ref)
