@@ -32,6 +32,8 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <cfloat>
+#include <type_traits>
 
 #include "fp8kv.h"
 #include "fp8kv_internal.h"
@@ -154,6 +156,17 @@ __device__ __forceinline__ float wave_max_rows(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
   x = fmaxf(x, __shfl_xor(x, 32));
   return x;
+}
+
+// the same through the row-swap instructions (no LDS round trip).  The
+// IEEE maximum builtin (v_maximum3_f32) would skip the canonicalising
+// v_max of each operand, but gave results that varied from call to call on
+// identical inputs here: fmaxf it is.
+__device__ __forceinline__ float wave_max_rows_swap(float x) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float wave_sum_rows(float x) {
@@ -1334,6 +1347,9 @@ __global__ __launch_bounds__(kMergeGroupedThreads) void merge_grouped_kernel(Dec
 // wg_start[k+1]): S[k] page ranges x Hkv x blocks[k] column blocks; its
 // partial states start at row part_base[k] of the workspace.
 constexpr int kMaxPromptGroups = 32;
+// log2 of the largest softmax weight the prompt pass lets build up before it
+// moves its reference max (weights and sums stay far from f16/f32 overflow)
+constexpr float kLazyRescale = 8.0f;
 struct PromptGroups {
   int32_t n;
   int32_t req_start[kMaxPromptGroups];
@@ -1384,8 +1400,12 @@ __global__ __launch_bounds__(256) void view_kernel(PrefixArgs a) {
   if (threadIdx.x == 0) a.view_ctx[b] = a.ctx_lens[b] - p0 * kPage;
 }
 
-template <int CACHE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+// NT column tiles per wave: each page's K and V fragments are loaded and
+// converted once for NT x 16 columns.  Two tiles run two waves per SIMD (an
+// e4m3 cache would fit three, which measured slower: 1.5x the page ranges,
+// hence 1.5x the partial states written and merged).
+template <int CACHE, int NT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 : 2, NT == 1 ? 3 : 2)))
 void prefix_kernel(PrefixArgs a) {
   constexpr int TB = Tile<CACHE>::kBytes;
   constexpr int NC = Tile<CACHE>::kChunks;
@@ -1404,26 +1424,39 @@ void prefix_kernel(PrefixArgs a) {
   const int gs = wg % (a.Hkv * S);
   const int blk = wg / (a.Hkv * S);
   const int g = gs / S, s = gs % S;
-  const int tile = blk * kWaves + wave;
-  if (tile >= a.pg.tiles[k]) return;  // no barrier in this kernel
+  const int tile0 = (blk * kWaves + wave) * NT;
+  if (tile0 >= a.pg.tiles[k]) return;  // no barrier in this kernel
   const int b0 = a.pg.req_start[k];
   const int nreq = a.pg.req_end[k] - b0;
   const int cols = nreq * a.G;
-  const int col = tile * kTileCols + n;
-  const int bl = col / a.G;  // request within the group
-  const int64_t row = static_cast<int64_t>(b0 + bl) * a.Hq + g * a.G + (col - bl * a.G);
   const int32_t* prefix_pages = a.page_table + static_cast<int64_t>(b0) * a.max_pages;
-  bf16x8_t qf[4];
-  {
-    const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(a.q + (col < cols ? row : 0) * kHeadDim +
+  // the score scale's sign goes into Q (negating bf16 is exact), so the
+  // running max is taken on the raw MFMA scores and |scale| joins the
+  // subtraction of the max in one FMA (a zero scale is kept just above 0 so
+  // that masked scores stay -inf)
+  const float sc = a.sm_scale * (a.k_scale ? uniform_load(a.k_scale, g) : 1.0f) * kLog2e;
+  const float asc = sc != sc ? sc : fmaxf(fabsf(sc), FLT_MIN);
+  const unsigned qflip = sc < 0.f ? 0x80008000u : 0u;
+  int col[NT], bl[NT];
+  int64_t row[NT];
+  bf16x8_t qf[NT][4];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    col[ct] = (tile0 + ct) * kTileCols + n;
+    bl[ct] = col[ct] / a.G;  // request within the group
+    row[ct] = static_cast<int64_t>(b0 + bl[ct]) * a.Hq + g * a.G + (col[ct] - bl[ct] * a.G);
+    const bool has = col[ct] < cols;
+    const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(a.q + (has ? row[ct] : 0) * kHeadDim +
                                                            32 * qd);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      qf[kk] = __builtin_bit_cast(bf16x8_t, col < cols ? qrow[kk] : u32x4_t{0u, 0u, 0u, 0u});
+    for (int kk = 0; kk < 4; ++kk) {
+      const u32x4_t w = has ? qrow[kk] : u32x4_t{0u, 0u, 0u, 0u};
+      qf[ct][kk] = __builtin_bit_cast(bf16x8_t, u32x4_t{w.x ^ qflip, w.y ^ qflip, w.z ^ qflip,
+                                                        w.w ^ qflip});
+    }
   }
   const int p0 = static_cast<int>(static_cast<int64_t>(s) * P0 / S);
   const int p1 = static_cast<int>(static_cast<int64_t>(s + 1) * P0 / S);
-  const float sc = a.sm_scale * (a.k_scale ? uniform_load(a.k_scale, g) : 1.0f) * kLog2e;
 
   // pages in flight: the two of one step (a deeper ring measured no faster:
   // this kernel is bound by its per-page arithmetic, not by load latency)
@@ -1451,18 +1484,25 @@ void prefix_kernel(PrefixArgs a) {
 #pragma unroll
   for (int r = 0; r < R; ++r) issue(r, p0 + r);
 
-  f32x4_t acc[8];
+  f32x4_t acc[NT][8];
+  float m_run[NT], l_run[NT];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int ct = 0; ct < NT; ++ct) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[ct][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[ct] = -INFINITY;
+    l_run[ct] = 0.f;
+  }
   // the two pages of the ring are one 32-token step: PV runs on the 16x16x32
   // MFMA, whose k index 8 qd + j holds token 4 qd + (j % 4) of page j / 4 --
   // the lane's own V and P values of the two pages side by side
   for (int p = p0; p < p1; p += 2) {
-    float sv[2][4];
+    float sv[NT][2][4];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t st[NT];
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) st[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         bf16x8_t kfrag;
@@ -1472,78 +1512,107 @@ void prefix_kernel(PrefixArgs a) {
         } else {
           kfrag = __builtin_bit_cast(bf16x8_t, kr[r][kk]);
         }
-        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[kk], st, 0, 0, 0);
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+          st[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[ct][kk], st[ct], 0, 0, 0);
       }
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[ct][r][i] = st[ct][i];
       // the prompt's pages are full; a page past the range or with an id
-      // outside the pool adds nothing
-      const bool use = okp[r] && p + r < p1;
+      // outside the pool adds nothing (a wave-uniform, rare branch)
+      if (!(okp[r] && p + r < p1)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sv[r][i] = use ? st[i] * sc : -INFINITY;
+        for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[ct][r][i] = -INFINITY;
+      }
     }
-    float mx = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
-                     fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
-    mx = wave_max_rows(mx);
-    const float m_new = fmaxf(m_run, mx);
-    if (__any(m_new > m_run)) {
-      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+    // softmax of every tile first, so that each V fragment below is
+    // converted once and feeds all tiles' PV products (one live fragment)
+    using PFrag = std::conditional_t<CACHE == FP8KV_E4M3, f16x8_t, bf16x8_t>;
+    PFrag ph[NT], pl[NT];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) acc[t] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-    float pr[8];
+    for (int ct = 0; ct < NT; ++ct) {
+      float mx = fmaxf(fmaxf(fmaxf(sv[ct][0][0], sv[ct][0][1]), fmaxf(sv[ct][0][2], sv[ct][0][3])),
+                       fmaxf(fmaxf(sv[ct][1][0], sv[ct][1][1]), fmaxf(sv[ct][1][2], sv[ct][1][3])));
+      mx = wave_max_rows_swap(mx) * asc;
+      // lazy rescale: the reference max moves only when a column's max
+      // passes it by more than 2^kLazyRescale, so the weights stay below that
+      // bound and most steps leave the accumulators alone
+      const float m_new = fmaxf(m_run[ct], mx);
+      if (__any(m_new > m_run[ct] + kLazyRescale)) {
+        const float alpha = (m_run[ct] == -INFINITY) ? 0.f : fast_exp2(m_run[ct] - m_new);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pr[j] = fast_exp2(sv[j / 4][j % 4] - mref);
-    l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-    if constexpr (CACHE == FP8KV_E4M3) {
-      f16x8_t ph, pl;
+        for (int t = 0; t < 8; ++t) acc[ct][t] *= alpha;
+        l_run[ct] *= alpha;
+        m_run[ct] = m_new;
+      }
+      const float mref = (m_run[ct] == -INFINITY) ? 0.f : m_run[ct];
+      float pr[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pr[j] = fast_exp2(__builtin_fmaf(sv[ct][j / 4][j % 4], asc, -mref));
+      l_run[ct] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+      // P in two terms (hi + lo) so the weights keep ~22 bits (16 for bf16):
+      // hi is P with its low mantissa bits cleared (exact in the 16-bit type
+      // over the weights' range), lo the exact remainder
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        ph[j] = static_cast<_Float16>(pr[j]);
-        pl[j] = static_cast<_Float16>(pr[j] - static_cast<float>(ph[j]));
+        if constexpr (CACHE == FP8KV_E4M3) {
+          const float h = __uint_as_float(__float_as_uint(pr[j]) & 0xFFFFE000u);
+          ph[ct][j] = static_cast<_Float16>(h);
+          pl[ct][j] = static_cast<_Float16>(pr[j] - h);
+        } else {
+          const float h = __uint_as_float(__float_as_uint(pr[j]) & 0xFFFF0000u);
+          ph[ct][j] = static_cast<__bf16>(h);
+          pl[ct][j] = static_cast<__bf16>(pr[j] - h);
+        }
       }
+    }
+    // PV: V of the step's two pages in the MFMA's operand order
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < 8; ++t) {
+      if constexpr (CACHE == FP8KV_E4M3) {
         const f16x4_t va = e4m3x4_to_f16(vr[0][t >> 2][t & 3]);
         const f16x4_t vb = e4m3x4_to_f16(vr[1][t >> 2][t & 3]);
         const f16x8_t vfrag = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vfrag, ph, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vfrag, pl, acc[t], 0, 0, 0);
-      }
-    } else {
-      bf16x8_t ph, pl;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        ph[j] = static_cast<__bf16>(pr[j]);
-        pl[j] = static_cast<__bf16>(pr[j] - static_cast<float>(ph[j]));
-      }
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
+        for (int ct = 0; ct < NT; ++ct) {
+          acc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vfrag, ph[ct], acc[ct][t], 0, 0, 0);
+          acc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vfrag, pl[ct], acc[ct][t], 0, 0, 0);
+        }
+      } else {
         const u32x4_t wa = vr[0][t >> 1], wb = vr[1][t >> 1];
         const u32x4_t w = (t & 1) ? u32x4_t{wa.z, wa.w, wb.z, wb.w} : u32x4_t{wa.x, wa.y, wb.x, wb.y};
         const bf16x8_t vfrag = __builtin_bit_cast(bf16x8_t, w);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfrag, ph, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfrag, pl, acc[t], 0, 0, 0);
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+          acc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfrag, ph[ct], acc[ct][t], 0, 0, 0);
+          acc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfrag, pl[ct], acc[ct][t], 0, 0, 0);
+        }
       }
     }
 #pragma unroll
     for (int r = 0; r < 2; ++r) issue(r, p + r + 2);
   }
-  const float l_tot = wave_sum_rows(l_run);
-  if (col < cols) {
-    // acc[t][i] of lane (n, qd) holds dim 32 qd + 8 i + t
-    const int64_t pidx = a.pg.part_base[k] + (static_cast<int64_t>(s) * nreq + bl) * a.Hq +
-                         (row - static_cast<int64_t>(b0 + bl) * a.Hq);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f32x4_t* po = reinterpret_cast<f32x4_t*>(a.ws_o + pidx * kHeadDim + 32 * qd + 8 * i);
-      po[0] = f32x4_t{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
-      po[1] = f32x4_t{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
-    }
-    if (qd == 0) {
-      a.ws_ml[pidx * 2] = m_run;
-      a.ws_ml[pidx * 2 + 1] = l_tot;
+  for (int ct = 0; ct < NT; ++ct) {
+    const float l_tot = wave_sum_rows(l_run[ct]);
+    if (col[ct] < cols) {
+      // acc[t][i] of lane (n, qd) holds dim 32 qd + 8 i + t
+      const int64_t pidx = a.pg.part_base[k] + (static_cast<int64_t>(s) * nreq + bl[ct]) * a.Hq +
+                           (row[ct] - static_cast<int64_t>(b0 + bl[ct]) * a.Hq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4_t* po = reinterpret_cast<f32x4_t*>(a.ws_o + pidx * kHeadDim + 32 * qd + 8 * i);
+        po[0] = f32x4_t{acc[ct][0][i], acc[ct][1][i], acc[ct][2][i], acc[ct][3][i]};
+        po[1] = f32x4_t{acc[ct][4][i], acc[ct][5][i], acc[ct][6][i], acc[ct][7][i]};
+      }
+      if (qd == 0) {
+        a.ws_ml[pidx * 2] = m_run[ct];
+        a.ws_ml[pidx * 2 + 1] = l_tot;
+      }
     }
   }
 }
@@ -1987,6 +2056,7 @@ struct SharedLayout {
   size_t o, ml, suf_out, suf_lse, view_pt, view_ctx, total;
   PromptGroups pg;
   int64_t grid;
+  int nt;  // column tiles per prefix wave
 };
 
 // Checks the group description (host arrays) and lays out the workspace.
@@ -2005,6 +2075,14 @@ fp8kv_status shared_layout(int32_t batch, int32_t Hq, int32_t Hkv, int32_t max_p
   pg.wg_start[0] = 0;
   pg.part_base[0] = 0;
   int64_t wgs = 0, part = 0;
+  // two column tiles per prefix wave when every group has at least two per
+  // wave of a workgroup (two waves per SIMD then, so 2/3 as many resident)
+  L.nt = 2;
+  for (int k = 0; k < num_groups; ++k) {
+    const int64_t r = static_cast<int64_t>(h_group_start[k + 1]) - h_group_start[k];
+    if (r > 0 && h_prefix_len[k] > 0 && (r * G + kTileCols - 1) / kTileCols < 2 * kWaves) L.nt = 1;
+  }
+  const int64_t resident = L.nt == 1 ? workers / kWaves : workers * 2 / 3 / kWaves;
   for (int k = 0; k < num_groups; ++k) {
     const int32_t r0 = h_group_start[k], r1 = h_group_start[k + 1], len = h_prefix_len[k];
     if (r1 < r0 || len < 0 || len % kPage != 0 || len / kPage > max_pages)
@@ -2016,9 +2094,9 @@ fp8kv_status shared_layout(int32_t batch, int32_t Hq, int32_t Hkv, int32_t max_p
     pg.prefix_len[m] = len;
     const int32_t P0 = len / kPage;
     pg.tiles[m] = static_cast<int32_t>((static_cast<int64_t>(r1 - r0) * G + kTileCols - 1) / kTileCols);
-    pg.blocks[m] = (pg.tiles[m] + kWaves - 1) / kWaves;
+    pg.blocks[m] = (pg.tiles[m] + kWaves * L.nt - 1) / (kWaves * L.nt);
     const int64_t base = static_cast<int64_t>(Hkv) * pg.blocks[m];
-    const int64_t want = (workers / kWaves + base - 1) / base;
+    const int64_t want = (resident + base - 1) / base;
     const int64_t most = P0 / kPrefixMinPages > 1 ? P0 / kPrefixMinPages : 1;
     pg.S[m] = static_cast<int32_t>(want < 1 ? 1 : (want < most ? want : most));
     pg.wg_start[m] = static_cast<int32_t>(wgs);
@@ -2091,10 +2169,17 @@ fp8kv_status shared_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
   pa.num_pages = desc->num_pages;
   pa.sm_scale = sm_scale;
   pa.pg = L.pg;
-  if (desc->cache_dtype == FP8KV_E4M3)
-    hipLaunchKernelGGL(prefix_kernel<FP8KV_E4M3>, dim3(L.grid), dim3(kThreads), 0, stream, pa);
-  else
-    hipLaunchKernelGGL(prefix_kernel<FP8KV_BF16>, dim3(L.grid), dim3(kThreads), 0, stream, pa);
+  if (desc->cache_dtype == FP8KV_E4M3) {
+    if (L.nt == 2)
+      hipLaunchKernelGGL((prefix_kernel<FP8KV_E4M3, 2>), dim3(L.grid), dim3(kThreads), 0, stream, pa);
+    else
+      hipLaunchKernelGGL((prefix_kernel<FP8KV_E4M3, 1>), dim3(L.grid), dim3(kThreads), 0, stream, pa);
+  } else {
+    if (L.nt == 2)
+      hipLaunchKernelGGL((prefix_kernel<FP8KV_BF16, 2>), dim3(L.grid), dim3(kThreads), 0, stream, pa);
+    else
+      hipLaunchKernelGGL((prefix_kernel<FP8KV_BF16, 1>), dim3(L.grid), dim3(kThreads), 0, stream, pa);
+  }
   st = launched();
   if (st != FP8KV_OK) return st;
   hipLaunchKernelGGL(view_kernel, dim3(batch), dim3(256), 0, stream, pa);
