@@ -484,7 +484,7 @@ struct DecodeArgs {
   void* out;
   float* ws_o;     // [slots][C][128] unnormalised weighted V
   float* ws_ml;    // [slots][C][2]   (max in log2 units, sum)
-  int32_t* ws_pre; // [B+1] page prefix sums of live requests
+  int32_t* ws_pre; // [B+1] prefix sums of the live requests' work-list items
   // log2-sum-exp of each written output row ([B][qlen][Hq], -inf for +0 rows),
   // or null: what a caller needs to merge these rows with attention over
   // other tokens
@@ -557,9 +557,19 @@ __device__ __forceinline__ void store_out8(const DecodeArgs& a, int64_t idx, con
   }
 }
 
+// The work list: segment (b, g) of a live request holds kPieceItems items
+// that read nothing, then one item per page.  Those items stand for a
+// piece's fixed cost (its Q load waits for the page loads already in flight,
+// and its waves merge through LDS), so the equal-work split gives a slice
+// that spans many short segments fewer pages.
+#ifndef FP8KV_PIECE_ITEMS
+#define FP8KV_PIECE_ITEMS 16
+#endif
+constexpr int kPieceItems = FP8KV_PIECE_ITEMS;
+
 // A piece: the part of segment (b, g) inside this workgroup's slice.
 struct Piece {
-  int b, g, n;   // request, kv-head, pages of the segment
+  int b, g, n;   // request, kv-head, items of the segment
   int64_t sx;    // work-list index of the segment's first page
   int64_t ps;    // first item of the piece
   int64_t pe;    // one past its last item
@@ -609,10 +619,16 @@ __device__ __forceinline__ bool next_piece(Piece& p, const int* s_pre, int B, in
   return true;
 }
 
-// pages of piece p that wave `wave` takes (round robin), and that count
-// rounded up to a multiple of `depth`
+// page index (within the request) of piece p's first page
+__device__ __forceinline__ int piece_first_page(const Piece& p) {
+  const int64_t r = p.ps - p.sx - kPieceItems;
+  return r > 0 ? static_cast<int>(r) : 0;
+}
+
+// pages of piece p that wave `wave` takes (round robin from its first page)
 __device__ __forceinline__ int wave_count(const Piece& p, int wave) {
-  const int len = static_cast<int>(p.pe - p.ps);
+  const int64_t r0 = p.sx + kPieceItems > p.ps ? p.sx + kPieceItems : p.ps;  // first page item
+  const int len = p.pe > r0 ? static_cast<int>(p.pe - r0) : 0;
   return len > wave ? (len - wave + kWaves - 1) / kWaves : 0;
 }
 
@@ -644,17 +660,18 @@ struct SeqCursor {
   __device__ __forceinline__ bool real() const { return !done && i < cnt; }
   // page index within the request
   __device__ __forceinline__ int page(int wave) const {
-    return static_cast<int>(p.ps - p.sx) + wave + kWaves * i;
+    return piece_first_page(p) + wave + kWaves * i;
   }
 };
 
-// Slices get at least this many pages (one per wave): with fewer pages than
-// workgroups, one page per slice would cut every segment into pieces that the
-// merge then walks one by one, and longer slices chain more dependent loads per
-// workgroup.  Both kernels derive the count from the page total alone.
+// Slices get at least this many pages' worth of items (one page per wave,
+// plus one piece's items): with fewer pages than workgroups, one page per
+// slice would cut every segment into pieces that the merge then walks one by
+// one, and longer slices chain more dependent loads per workgroup.  Both
+// kernels derive the count from the item total alone.
 constexpr int64_t kMinSlice = 4;
 __device__ __forceinline__ int64_t slice_count(int64_t W, int64_t grid) {
-  const int64_t want = (W + kMinSlice - 1) / kMinSlice;
+  const int64_t want = (W + kMinSlice + kPieceItems - 1) / (kMinSlice + kPieceItems);
   return want < 1 ? 1 : (want < grid ? want : grid);
 }
 
@@ -700,7 +717,7 @@ void decode_kernel(DecodeArgs a) {
     lag[ct] = col < a.C ? a.qlen - 1 - col / a.G : 0;
   }
 
-  // ---- prologue: page prefix sums of the live requests ------------------
+  // ---- prologue: work-list item prefix sums of the live requests --------
   {
     const int per = (B + kThreads - 1) / kThreads;
     const int b0 = min(B, static_cast<int>(threadIdx.x) * per);
@@ -708,8 +725,9 @@ void decode_kernel(DecodeArgs a) {
     int sum = 0;
     for (int b = b0; b < b1; ++b) {
       const int np = live_pages(a, b);
-      s_pre[b] = np;
-      sum += np;
+      const int items = np > 0 ? np + kPieceItems : 0;  // per kv-head segment
+      s_pre[b] = items;
+      sum += items;
     }
     s_part[threadIdx.x] = sum;
     __syncthreads();
@@ -834,7 +852,7 @@ void decode_kernel(DecodeArgs a) {
   for (;;) {
     const int cnt = wave_count(P, wave);
     const int iters = (cnt + DEPTH - 1) / DEPTH * DEPTH;
-    const int pg0 = static_cast<int>(P.ps - P.sx) + wave;  // my first page in the piece
+    const int pg0 = piece_first_page(P) + wave;  // my first page in the piece
     const int ctx = uniform_load(a.ctx_lens, P.b);
     // Q is waited for here, once per piece: vector loads retire in order, so
     // this also waits for the pages already in flight (a slice holds only a
