@@ -192,6 +192,26 @@ def test_step_helper_equals_its_calls(lib, dev, tracker):
         assert ab is None
 
 
+@pytest.mark.parametrize("workers", [0, 256, 3072, 6144])
+def test_short_segments_among_long_ones(lib, dev, workers):
+    """Many 1..40-token requests around a few long ones, 64/8 heads: slices
+    hold many short (request, kv-head) segments, and with many workers some
+    slices end inside a segment's leading work items and hold no page."""
+    rng = np.random.default_rng(77)
+    L = rng.integers(0, 41, 96)
+    L[[5, 40, 77]] = [2047, 3000, 1500]
+    w = workloads.custom("short_long", L, Hq=64, Hkv=8, seed=77, pool_slack=2)
+    st = dev.build(w, num_workers=workers)
+    out16 = st.step(check_tags=True)
+    out32 = st.decode(out_dtype=lib.OUT_F32)
+    Ko, Vo = oracle_state(w, st.k_scale_host, st.v_scale_host)
+    ref, _ = oracle.attention(Ko, Vo, st.k_scale_host, st.v_scale_host, w.q_bits(), w.page_table,
+                              w.ctx_lens, SM_SCALE)
+    err = check_outputs(_host(out32), _host(out16.view(torch.int16)), ref)
+    assert err < 1e-4
+    print(f"short among long, workers={workers}: max abs err {err:.3e}")
+
+
 def test_largest_batch(lib, dev):
     """4096 requests (the largest batch) with short contexts, 1% of them holding
     one stale entry: every abort flag, every cache byte and every output row
