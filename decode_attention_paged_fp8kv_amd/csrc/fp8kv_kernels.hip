@@ -62,6 +62,10 @@ constexpr int kRsrcWord3 = 0x00020000;
 // shared-prompt call reads those with the default policy, once per batch.)
 constexpr int kKvLoadPolicy = 2;
 constexpr float kLog2e = 1.4426950408889634f;
+// log2 of the largest softmax weight the attention loops let build up before
+// they move their reference max (weights and sums stay far from f16/f32
+// overflow; most steps then leave the accumulators alone)
+constexpr float kLazyRescale = 8.0f;
 
 // pages in flight per wave (register ring depth), per cache type
 #ifndef FP8KV_DEPTH_E4M3
@@ -151,17 +155,11 @@ __device__ __forceinline__ unsigned e4m3_encode(float x) {
   return code | sign;
 }
 
-__device__ __forceinline__ float wave_max_rows(float x) {
-  // lanes l, l^16, l^32, l^48 hold the same head: reduce across them
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-
-// the same through the row-swap instructions (no LDS round trip).  The
-// IEEE maximum builtin (v_maximum3_f32) would skip the canonicalising
-// v_max of each operand, but gave results that varied from call to call on
-// identical inputs here: fmaxf it is.
+// The max over the four lanes l, l^16, l^32, l^48 (they hold the same MFMA
+// column), through the row-swap instructions (no LDS round trip).  The IEEE
+// maximum builtin (v_maximum3_f32) would skip the canonicalising v_max of each
+// operand, but gave results that varied from call to call on identical inputs
+// here: fmaxf it is.
 __device__ __forceinline__ float wave_max_rows_swap(float x) {
   const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
@@ -882,13 +880,23 @@ void decode_kernel(DecodeArgs a) {
     }
 
     if (cnt > 0) {
+      // scores in log2 units: s = (q.k_code) * sm_scale * k_scale * log2(e).
+      // The scale's sign goes into Q (negating bf16 is exact), so the running
+      // max is taken on the raw MFMA scores and |scale| joins the subtraction
+      // of the max in one FMA (a zero scale is kept just above 0 so that
+      // masked scores stay -inf)
+      const float sc = a.sm_scale * (a.k_scale ? uniform_load(a.k_scale, P.g) : 1.0f) * kLog2e;
+      const float asc = sc != sc ? sc : fmaxf(fabsf(sc), FLT_MIN);
+      const unsigned qflip = sc < 0.f ? 0x80008000u : 0u;
       bf16x8_t qf[NT][4];
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qf[ct][kk] = __builtin_bit_cast(bf16x8_t, qcur[ct][kk]);
-      // scores in log2 units: s = (q.k_code) * sm_scale * k_scale * log2(e)
-      const float sc = a.sm_scale * (a.k_scale ? uniform_load(a.k_scale, P.g) : 1.0f) * kLog2e;
+        for (int kk = 0; kk < 4; ++kk) {
+          const u32x4_t w = qcur[ct][kk];
+          qf[ct][kk] = __builtin_bit_cast(bf16x8_t, u32x4_t{w.x ^ qflip, w.y ^ qflip, w.z ^ qflip,
+                                                            w.w ^ qflip});
+        }
 
       for (int i0 = 0; i0 < iters; i0 += DEPTH) {
         if constexpr (kPairPV) {
@@ -922,7 +930,7 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-              for (int r = 0; r < 4; ++r) sv[s][ct][r] = st[ct][r] * sc;
+              for (int r = 0; r < 4; ++r) sv[s][ct][r] = st[ct][r];
             vmask[s] = u32x4_t{~0u, ~0u, ~0u, ~0u};
             if (left - (a.qlen - 1) < kPage) {
 #pragma unroll
@@ -946,9 +954,9 @@ void decode_kernel(DecodeArgs a) {
           for (int ct = 0; ct < NT; ++ct) {
             float mx = fmaxf(fmaxf(fmaxf(sv[0][ct][0], sv[0][ct][1]), fmaxf(sv[0][ct][2], sv[0][ct][3])),
                              fmaxf(fmaxf(sv[1][ct][0], sv[1][ct][1]), fmaxf(sv[1][ct][2], sv[1][ct][3])));
-            mx = wave_max_rows(mx);
+            mx = wave_max_rows_swap(mx) * asc;
             const float m_new = fmaxf(m_run[ct], mx);
-            if (__any(m_new > m_run[ct])) {
+            if (__any(m_new > m_run[ct] + kLazyRescale)) {
               const float alpha = (m_run[ct] == -INFINITY) ? 0.f : fast_exp2(m_run[ct] - m_new);
 #pragma unroll
               for (int t = 0; t < 8; ++t) acc[ct][t] *= alpha;
@@ -957,7 +965,7 @@ void decode_kernel(DecodeArgs a) {
             }
             const float mref = (m_run[ct] == -INFINITY) ? 0.f : m_run[ct];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) p[ct][j] = fast_exp2(sv[j / 4][ct][j % 4] - mref);
+            for (int j = 0; j < 8; ++j) p[ct][j] = fast_exp2(__builtin_fmaf(sv[j / 4][ct][j % 4], asc, -mref));
             l_run[ct] += ((p[ct][0] + p[ct][1]) + (p[ct][2] + p[ct][3])) +
                          ((p[ct][4] + p[ct][5]) + (p[ct][6] + p[ct][7]));
           }
@@ -967,8 +975,9 @@ void decode_kernel(DecodeArgs a) {
             for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
               for (int j = 0; j < 8; ++j) {
-                ph[ct][j] = static_cast<_Float16>(p[ct][j]);
-                pl[ct][j] = static_cast<_Float16>(p[ct][j] - static_cast<float>(ph[ct][j]));
+                const float h = __uint_as_float(__float_as_uint(p[ct][j]) & 0xFFFFE000u);
+                ph[ct][j] = static_cast<_Float16>(h);
+                pl[ct][j] = static_cast<_Float16>(p[ct][j] - h);
               }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
@@ -987,8 +996,9 @@ void decode_kernel(DecodeArgs a) {
             for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
               for (int j = 0; j < 8; ++j) {
-                ph[ct][j] = static_cast<__bf16>(p[ct][j]);
-                pl[ct][j] = static_cast<__bf16>(p[ct][j] - static_cast<float>(ph[ct][j]));
+                const float h = __uint_as_float(__float_as_uint(p[ct][j]) & 0xFFFF0000u);
+                ph[ct][j] = static_cast<__bf16>(h);
+                pl[ct][j] = static_cast<__bf16>(p[ct][j] - h);
               }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
@@ -1043,7 +1053,7 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sv[ct][r] = st[ct][r] * sc;
+            for (int r = 0; r < 4; ++r) sv[ct][r] = st[ct][r];
           u32x4_t vmask = {~0u, ~0u, ~0u, ~0u};
           if (left - (a.qlen - 1) < kPage) {  // some column stops inside this page
 #pragma unroll
@@ -1066,9 +1076,9 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct) {
             float mx = fmaxf(fmaxf(sv[ct][0], sv[ct][1]), fmaxf(sv[ct][2], sv[ct][3]));
-            mx = wave_max_rows(mx);
+            mx = wave_max_rows_swap(mx) * asc;
             const float m_new = fmaxf(m_run[ct], mx);
-            if (__any(m_new > m_run[ct])) {
+            if (__any(m_new > m_run[ct] + kLazyRescale)) {
               const float alpha = (m_run[ct] == -INFINITY) ? 0.f : fast_exp2(m_run[ct] - m_new);
 #pragma unroll
               for (int t = 0; t < 8; ++t) acc[ct][t] *= alpha;
@@ -1077,20 +1087,23 @@ void decode_kernel(DecodeArgs a) {
             }
             const float mref = (m_run[ct] == -INFINITY) ? 0.f : m_run[ct];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p[ct][r] = fast_exp2(sv[ct][r] - mref);
+            for (int r = 0; r < 4; ++r) p[ct][r] = fast_exp2(__builtin_fmaf(sv[ct][r], asc, -mref));
             l_run[ct] += (p[ct][0] + p[ct][1]) + (p[ct][2] + p[ct][3]);
           }
 
           // ---- O^T += V^T P^T : rows = dims 8m + t (tile t), cols = columns
           if constexpr (CACHE == FP8KV_E4M3) {
-            // P split into two f16 terms (hi + lo) so the weights keep ~22 bits
+            // P split into two f16 terms (hi + lo) so the weights keep ~22 bits:
+            // hi is P with its low mantissa bits cleared (exact in f16 over the
+            // weights' range), lo the exact remainder
             f16x4_t ph[NT], pl[NT];
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
-                ph[ct][r] = static_cast<_Float16>(p[ct][r]);
-                pl[ct][r] = static_cast<_Float16>(p[ct][r] - static_cast<float>(ph[ct][r]));
+                const float h = __uint_as_float(__float_as_uint(p[ct][r]) & 0xFFFFE000u);
+                ph[ct][r] = static_cast<_Float16>(h);
+                pl[ct][r] = static_cast<_Float16>(p[ct][r] - h);
               }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
@@ -1108,10 +1121,9 @@ void decode_kernel(DecodeArgs a) {
             for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
-                const __bf16 h = static_cast<__bf16>(p[ct][r]);
-                ph[ct][r] = __builtin_bit_cast(short, h);
-                pl[ct][r] =
-                    __builtin_bit_cast(short, static_cast<__bf16>(p[ct][r] - static_cast<float>(h)));
+                const float h = __uint_as_float(__float_as_uint(p[ct][r]) & 0xFFFF0000u);
+                ph[ct][r] = __builtin_bit_cast(short, static_cast<__bf16>(h));
+                pl[ct][r] = __builtin_bit_cast(short, static_cast<__bf16>(p[ct][r] - h));
               }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
@@ -1365,9 +1377,6 @@ __global__ __launch_bounds__(kMergeGroupedThreads) void merge_grouped_kernel(Dec
 // wg_start[k+1]): S[k] page ranges x Hkv x blocks[k] column blocks; its
 // partial states start at row part_base[k] of the workspace.
 constexpr int kMaxPromptGroups = 32;
-// log2 of the largest softmax weight the prompt pass lets build up before it
-// moves its reference max (weights and sums stay far from f16/f32 overflow)
-constexpr float kLazyRescale = 8.0f;
 struct PromptGroups {
   int32_t n;
   int32_t req_start[kMaxPromptGroups];
