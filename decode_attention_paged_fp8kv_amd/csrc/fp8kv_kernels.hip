@@ -682,13 +682,10 @@ __device__ __forceinline__ void segment_workgroups(int64_t first, int64_t last, 
   wl = ((last + 1) * NWG - 1) / W;
 }
 
-// NT: 16-column tiles of (query, head) pairs per kv-head (1 or 2).  Two tiles
-// double the Q fragments and accumulators, so that form runs 2 waves per SIMD
-// instead of 3; each page's K/V fragments are converted once for both tiles.
+// The decode kernel's body, run as workgroup wg_id of wg_count: by its own
+// kernel, or by the decode part of the shared-prompt call's fused grid.
 template <int CACHE, int DEPTH, int NT>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 : 2, NT == 1 ? 3 : 2)))
-void decode_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg_id, int wg_count) {
   constexpr int TB = Tile<CACHE>::kBytes;
   constexpr int NC = Tile<CACHE>::kChunks;
   __shared__ int s_pre[kMaxBatch + 1];
@@ -758,10 +755,10 @@ void decode_kernel(DecodeArgs a) {
       run += np;
     }
     __syncthreads();
-    if (blockIdx.x == 0)
+    if (wg_id == 0)
       for (int b = threadIdx.x; b <= B; b += kThreads) a.ws_pre[b] = s_pre[b];
     // requests with nothing to read get +0 rows (aborted, empty, invalid)
-    for (int b = blockIdx.x; b < B; b += gridDim.x) {
+    for (int b = wg_id; b < B; b += wg_count) {
       if (s_pre[b + 1] != s_pre[b]) continue;
       const int64_t base = static_cast<int64_t>(b) * a.qlen * a.Hq * kHeadDim;
       for (int i = threadIdx.x; i < a.qlen * a.Hq * kHeadDim; i += kThreads) {
@@ -778,8 +775,8 @@ void decode_kernel(DecodeArgs a) {
 
   // ---- this workgroup's slice --------------------------------------------
   const int64_t W = static_cast<int64_t>(a.Hkv) * s_pre[B];
-  const int64_t NWG = slice_count(W, gridDim.x);
-  const int64_t bw = blockIdx.x;
+  const int64_t NWG = slice_count(W, wg_count);
+  const int64_t bw = wg_id;
   if (bw >= NWG) return;  // fewer slices than workgroups (uniform: no barrier follows)
   const int64_t X0 = bw * W / NWG;
   const int64_t X1 = (bw + 1) * W / NWG;
@@ -1214,6 +1211,16 @@ void decode_kernel(DecodeArgs a) {
   }
 }
 
+// NT: 16-column tiles of (query, head) pairs per kv-head (1 or 2).  Two tiles
+// double the Q fragments and accumulators, so that form runs 2 waves per SIMD
+// instead of 3; each page's K/V fragments are converted once for both tiles.
+template <int CACHE, int DEPTH, int NT>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 : 2, NT == 1 ? 3 : 2)))
+void decode_kernel(DecodeArgs a) {
+  decode_body<CACHE, DEPTH, NT>(a, static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+}
+
 // ---------------------------------------------------------------------------
 // 5. merge of the pieces of split segments (fixed order: deterministic)
 // ---------------------------------------------------------------------------
@@ -1377,6 +1384,14 @@ __global__ __launch_bounds__(kMergeGroupedThreads) void merge_grouped_kernel(Dec
 // wg_start[k+1]): S[k] page ranges x Hkv x blocks[k] column blocks; its
 // partial states start at row part_base[k] of the workspace.
 constexpr int kMaxPromptGroups = 32;
+// the fused shared-prompt grid runs the decode over the views with this
+// fraction of the plain decode grid's workgroups: a third, with the default
+// grid one workgroup per CU beside the prompt pass's two (the full grid, a
+// quarter and a sixth measured 2%, 6% and 24% slower)
+#ifndef FP8KV_FUSED_DECODE_DIV
+#define FP8KV_FUSED_DECODE_DIV 3
+#endif
+constexpr int kFusedDecodeDiv = FP8KV_FUSED_DECODE_DIV;
 struct PromptGroups {
   int32_t n;
   int32_t req_start[kMaxPromptGroups];
@@ -1432,8 +1447,7 @@ __global__ __launch_bounds__(256) void view_kernel(PrefixArgs a) {
 // e4m3 cache would fit three, which measured slower: 1.5x the page ranges,
 // hence 1.5x the partial states written and merged).
 template <int CACHE, int NT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 : 2, NT == 1 ? 3 : 2)))
-void prefix_kernel(PrefixArgs a) {
+__device__ __forceinline__ void prefix_body(const PrefixArgs& a, int wg_id) {
   constexpr int TB = Tile<CACHE>::kBytes;
   constexpr int NC = Tile<CACHE>::kChunks;
   const int lane = threadIdx.x & 63;
@@ -1444,10 +1458,10 @@ void prefix_kernel(PrefixArgs a) {
   // 8 they land on one XCD (workgroups go round robin over the 8) and share
   // its L2
   int k = 0;
-  while (k + 1 < a.pg.n && static_cast<int>(blockIdx.x) >= a.pg.wg_start[k + 1]) ++k;
+  while (k + 1 < a.pg.n && wg_id >= a.pg.wg_start[k + 1]) ++k;
   const int S = a.pg.S[k];
   const int P0 = a.pg.prefix_len[k] / kPage;
-  const int wg = static_cast<int>(blockIdx.x) - a.pg.wg_start[k];
+  const int wg = wg_id - a.pg.wg_start[k];
   const int gs = wg % (a.Hkv * S);
   const int blk = wg / (a.Hkv * S);
   const int g = gs / S, s = gs % S;
@@ -1642,6 +1656,28 @@ void prefix_kernel(PrefixArgs a) {
       }
     }
   }
+}
+
+template <int CACHE, int NT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 : 2, NT == 1 ? 3 : 2)))
+void prefix_kernel(PrefixArgs a) {
+  prefix_body<CACHE, NT>(a, static_cast<int>(blockIdx.x));
+}
+
+// The prompt pass and the own-token decode in one grid (e4m3 cache, at most
+// 16 columns): workgroups [0, prefix_wgs) run the prompt pass, the others the
+// decode over the views (its slices numbered from 0).  Workgroups go out in
+// index order, so the decode's fill the slots the prompt pass leaves (three
+// waves per SIMD here) and its memory-bound work runs beside the prompt
+// pass's issue-bound work instead of after it.
+template <int NTP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void shared_fused_kernel(PrefixArgs pa, DecodeArgs da, int32_t prefix_wgs, int32_t decode_wgs) {
+  const int w = static_cast<int>(blockIdx.x);
+  if (w < prefix_wgs)
+    prefix_body<FP8KV_E4M3, NTP>(pa, w);
+  else
+    decode_body<FP8KV_E4M3, FP8KV_DEPTH_E4M3, 1>(da, w - prefix_wgs, decode_wgs);
 }
 
 // Output rows of the shared-prompt call: the prompt's S partial states and
@@ -2010,8 +2046,8 @@ fp8kv_status decode_setup(const fp8kv_cache_desc* desc, const void* d_k_cache,
 }
 
 // The decode kernel and its merge pass.
-fp8kv_status decode_launch(const DecodeArgs& a, int32_t cache_dtype, int32_t workers,
-                           int32_t num_workers, hipStream_t stream) {
+// Workgroups of the decode grid.
+int64_t decode_grid(const DecodeArgs& a, int32_t workers, int32_t num_workers) {
   const int segs = a.batch * a.Hkv;
   // More than 16 (query, head) columns: two column tiles, 2 waves per SIMD
   // instead of 3, so the default grid holds 2/3 as many workgroups.  With the
@@ -2025,6 +2061,29 @@ fp8kv_status decode_launch(const DecodeArgs& a, int32_t cache_dtype, int32_t wor
   if (num_workers == 0 && two_tiles) blocks = blocks / 3 * 2;
   if (num_workers == 0 && static_cast<int64_t>(kDefaultPiecesPerSegment) * segs < blocks)
     blocks = kDefaultPiecesPerSegment * segs;
+  return blocks;
+}
+
+// The merge pass after a decode grid of `blocks` workgroups.
+fp8kv_status merge_launch(const DecodeArgs& a, int64_t blocks, hipStream_t stream) {
+  const int segs = a.batch * a.Hkv;
+  // at least 256 threads, one per (column, 4 dims) pair up to 1024
+  const int pairs = a.C * (kHeadDim / 4);
+  const int flat_threads =
+      pairs < 256 ? 256 : (pairs > kMergeFlatMaxThreads ? kMergeFlatMaxThreads : pairs);
+  const dim3 mgrid(segs < 1024 ? segs : 1024);
+  if (blocks >= static_cast<int64_t>(kMergeGroupedMinPieces) * segs)
+    hipLaunchKernelGGL(merge_grouped_kernel, mgrid, dim3(kMergeGroupedThreads), 0, stream, a,
+                       blocks);
+  else
+    hipLaunchKernelGGL(merge_flat_kernel, mgrid, dim3(flat_threads), 0, stream, a, blocks);
+  return launched();
+}
+
+fp8kv_status decode_launch(const DecodeArgs& a, int32_t cache_dtype, int32_t workers,
+                           int32_t num_workers, hipStream_t stream) {
+  const bool two_tiles = a.C > kTileCols;
+  const int64_t blocks = decode_grid(a, workers, num_workers);
   if (cache_dtype == FP8KV_E4M3) {
     if (two_tiles)
       hipLaunchKernelGGL((decode_kernel<FP8KV_E4M3, FP8KV_DEPTH_E4M3_2T, 2>), dim3(blocks),
@@ -2042,18 +2101,7 @@ fp8kv_status decode_launch(const DecodeArgs& a, int32_t cache_dtype, int32_t wor
   }
   fp8kv_status st = launched();
   if (st != FP8KV_OK) return st;
-  // at least 256 threads, one per (column, 4 dims) pair up to 1024
-  const int pairs = a.C * (kHeadDim / 4);
-  const int flat_threads =
-      pairs < 256 ? 256 : (pairs > kMergeFlatMaxThreads ? kMergeFlatMaxThreads : pairs);
-  const dim3 mgrid(segs < 1024 ? segs : 1024);
-  if (blocks >= static_cast<int64_t>(kMergeGroupedMinPieces) * segs)
-    hipLaunchKernelGGL(merge_grouped_kernel, mgrid, dim3(kMergeGroupedThreads), 0, stream, a,
-                       static_cast<int64_t>(blocks));
-  else
-    hipLaunchKernelGGL(merge_flat_kernel, mgrid, dim3(flat_threads), 0, stream, a,
-                       static_cast<int64_t>(blocks));
-  return launched();
+  return merge_launch(a, blocks, stream);
 }
 
 fp8kv_status decode_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
@@ -2196,19 +2244,8 @@ fp8kv_status shared_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
   pa.num_pages = desc->num_pages;
   pa.sm_scale = sm_scale;
   pa.pg = L.pg;
-  if (desc->cache_dtype == FP8KV_E4M3) {
-    if (L.nt == 2)
-      hipLaunchKernelGGL((prefix_kernel<FP8KV_E4M3, 2>), dim3(L.grid), dim3(kThreads), 0, stream, pa);
-    else
-      hipLaunchKernelGGL((prefix_kernel<FP8KV_E4M3, 1>), dim3(L.grid), dim3(kThreads), 0, stream, pa);
-  } else {
-    if (L.nt == 2)
-      hipLaunchKernelGGL((prefix_kernel<FP8KV_BF16, 2>), dim3(L.grid), dim3(kThreads), 0, stream, pa);
-    else
-      hipLaunchKernelGGL((prefix_kernel<FP8KV_BF16, 1>), dim3(L.grid), dim3(kThreads), 0, stream, pa);
-  }
-  st = launched();
-  if (st != FP8KV_OK) return st;
+  // the own-token views first (the decode over them may start beside the
+  // prompt pass)
   hipLaunchKernelGGL(view_kernel, dim3(batch), dim3(256), 0, stream, pa);
   st = launched();
   if (st != FP8KV_OK) return st;
@@ -2220,7 +2257,36 @@ fp8kv_status shared_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
   a.out = ws + L.suf_out;
   a.out_f32 = 1;
   a.lse = reinterpret_cast<float*>(ws + L.suf_lse);
-  st = decode_launch(a, desc->cache_dtype, workers, num_workers, stream);
+  if (desc->cache_dtype == FP8KV_E4M3 && a.C <= kTileCols) {
+    // one grid: the prompt pass, then the decode's workgroups beside it
+    const int64_t dblocks = decode_grid(a, workers, num_workers) / kFusedDecodeDiv;
+    const int64_t d = dblocks < 1 ? 1 : dblocks;
+    if (L.grid + d > 0x7FFFFFFF) return FP8KV_UNSUPPORTED;
+    if (L.nt == 2)
+      hipLaunchKernelGGL(shared_fused_kernel<2>, dim3(L.grid + d), dim3(kThreads), 0, stream, pa,
+                         a, static_cast<int32_t>(L.grid), static_cast<int32_t>(d));
+    else
+      hipLaunchKernelGGL(shared_fused_kernel<1>, dim3(L.grid + d), dim3(kThreads), 0, stream, pa,
+                         a, static_cast<int32_t>(L.grid), static_cast<int32_t>(d));
+    st = launched();
+    if (st != FP8KV_OK) return st;
+    st = merge_launch(a, d, stream);
+  } else {
+    if (desc->cache_dtype == FP8KV_E4M3) {
+      if (L.nt == 2)
+        hipLaunchKernelGGL((prefix_kernel<FP8KV_E4M3, 2>), dim3(L.grid), dim3(kThreads), 0, stream, pa);
+      else
+        hipLaunchKernelGGL((prefix_kernel<FP8KV_E4M3, 1>), dim3(L.grid), dim3(kThreads), 0, stream, pa);
+    } else {
+      if (L.nt == 2)
+        hipLaunchKernelGGL((prefix_kernel<FP8KV_BF16, 2>), dim3(L.grid), dim3(kThreads), 0, stream, pa);
+      else
+        hipLaunchKernelGGL((prefix_kernel<FP8KV_BF16, 1>), dim3(L.grid), dim3(kThreads), 0, stream, pa);
+    }
+    st = launched();
+    if (st != FP8KV_OK) return st;
+    st = decode_launch(a, desc->cache_dtype, workers, num_workers, stream);
+  }
   if (st != FP8KV_OK) return st;
 
   CombineArgs ca;
