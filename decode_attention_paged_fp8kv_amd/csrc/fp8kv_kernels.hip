@@ -525,16 +525,63 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ __forceinline__ int live_pages(const DecodeArgs& a, int b) {
+// Prompts shared by groups of requests.  Requests [req_start[k], req_end[k])
+// continue prompt k of prefix_len[k] tokens, on the pages their tables list
+// first (read from the table of the group's first request).  Group k's
+// prompt-pass workgroups are [wg_start[k], wg_start[k+1]): S[k] page ranges x
+// Hkv x blocks[k] column blocks; its partial states start at row
+// part_base[k] of the workspace.
+constexpr int kMaxPromptGroups = 32;
+// the fused shared-prompt grid runs the decode over the views with this
+// fraction of the plain decode grid's workgroups: a third, with the default
+// grid one workgroup per CU beside the prompt pass's two (the full grid, a
+// quarter and a sixth measured 2%, 6% and 24% slower)
+#ifndef FP8KV_FUSED_DECODE_DIV
+#define FP8KV_FUSED_DECODE_DIV 3
+#endif
+constexpr int kFusedDecodeDiv = FP8KV_FUSED_DECODE_DIV;
+struct PromptGroups {
+  int32_t n;
+  int32_t req_start[kMaxPromptGroups];
+  int32_t req_end[kMaxPromptGroups];
+  int32_t prefix_len[kMaxPromptGroups];
+  int32_t S[kMaxPromptGroups];
+  int32_t tiles[kMaxPromptGroups];
+  int32_t blocks[kMaxPromptGroups];
+  int32_t wg_start[kMaxPromptGroups + 1];
+  int64_t part_base[kMaxPromptGroups + 1];
+};
+
+// the group of request b, or -1
+__device__ __forceinline__ int prompt_group(const PromptGroups& pg, int b) {
+  for (int k = 0; k < pg.n; ++k)
+    if (b >= pg.req_start[k] && b < pg.req_end[k]) return k;
+  return -1;
+}
+
+// pages of request b's table the decode skips: its prompt's, when the body
+// runs over the own tokens of a shared-prompt call (VIEWS), else none
+template <bool VIEWS>
+__device__ __forceinline__ int view_skip(const PromptGroups* pg, int b) {
+  if constexpr (!VIEWS) {
+    return 0;
+  } else {
+    const int k = prompt_group(*pg, b);
+    return k < 0 ? 0 : pg->prefix_len[k] / kPage;
+  }
+}
+
+// pages the decode reads for request b past the `skip` pages it skips
+__device__ __forceinline__ int live_pages(const DecodeArgs& a, int b, int skip) {
   // the flag is loaded next to the length (without an abort array, from a
   // byte of the length itself, and ignored), not after it
-  const int ctx = a.ctx_lens[b];
+  const int ctx = a.ctx_lens[b] - skip * kPage;
   const uint8_t flag =
       *(a.abort ? a.abort + b : reinterpret_cast<const uint8_t*>(a.ctx_lens + b));
   const int n = ctx > 0 ? (ctx + kPage - 1) / kPage : 0;
   // nothing read for: no context, a length that does not fit the table (fail
   // closed), an aborted request (+0 rows)
-  const bool none = n == 0 || n > a.max_pages || (a.abort != nullptr && flag != 0);
+  const bool none = n == 0 || n + skip > a.max_pages || (a.abort != nullptr && flag != 0);
   return none ? 0 : n;
 }
 
@@ -683,9 +730,12 @@ __device__ __forceinline__ void segment_workgroups(int64_t first, int64_t last, 
 }
 
 // The decode kernel's body, run as workgroup wg_id of wg_count: by its own
-// kernel, or by the decode part of the shared-prompt call's fused grid.
-template <int CACHE, int DEPTH, int NT>
-__device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg_id, int wg_count) {
+// kernel, or by the decode part of the shared-prompt call's fused grid, which
+// sets VIEWS: each request's table and context are then read past its
+// prompt's pages (pg).
+template <int CACHE, int DEPTH, int NT, bool VIEWS = false>
+__device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg_id, int wg_count,
+                                            const PromptGroups* pg = nullptr) {
   constexpr int TB = Tile<CACHE>::kBytes;
   constexpr int NC = Tile<CACHE>::kChunks;
   __shared__ int s_pre[kMaxBatch + 1];
@@ -719,7 +769,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg_id, int 
     const int b1 = min(B, b0 + per);
     int sum = 0;
     for (int b = b0; b < b1; ++b) {
-      const int np = live_pages(a, b);
+      const int np = live_pages(a, b, view_skip<VIEWS>(pg, b));
       const int items = np > 0 ? np + kPieceItems : 0;  // per kv-head segment
       s_pre[b] = items;
       sum += items;
@@ -796,7 +846,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg_id, int 
     // a vector load: it retires right after the page loads issued before it,
     // which are waited for first anyway (page ids through the scalar cache
     // measured slower: 12 waves per CU contend for it)
-    if (J.real()) pid = a.page_table[static_cast<int64_t>(J.p.b) * a.max_pages + J.page(wave)];
+    if (J.real())
+      pid = a.page_table[static_cast<int64_t>(J.p.b) * a.max_pages + view_skip<VIEWS>(pg, J.p.b) +
+                         J.page(wave)];
     J.advance(s_pre, B, a.Hkv, X1, wave);
     return pid;
   };
@@ -848,7 +900,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg_id, int 
     const int cnt = wave_count(P, wave);
     const int iters = (cnt + DEPTH - 1) / DEPTH * DEPTH;
     const int pg0 = piece_first_page(P) + wave;  // my first page in the piece
-    const int ctx = uniform_load(a.ctx_lens, P.b);
+    const int ctx = uniform_load(a.ctx_lens, P.b) - kPage * view_skip<VIEWS>(pg, P.b);
     // Q is waited for here, once per piece: vector loads retire in order, so
     // this also waits for the pages already in flight (a slice holds only a
     // few pieces).  Waiting at the first MFMA instead would put the wait
@@ -1378,39 +1430,8 @@ __global__ __launch_bounds__(kMergeGroupedThreads) void merge_grouped_kernel(Dec
 // serve once.  Each (column, page range) leaves (max, sum, weighted V) for
 // the combine pass.  The requests' own tokens go through decode_kernel over
 // the rest of their tables, with its log-sum-exp output.
-// Requests [req_start[k], req_end[k]) continue prompt k of prefix_len[k]
-// tokens, on the pages their tables list first (read from the table of the
-// group's first request).  Group k's workgroups are [wg_start[k],
-// wg_start[k+1]): S[k] page ranges x Hkv x blocks[k] column blocks; its
-// partial states start at row part_base[k] of the workspace.
-constexpr int kMaxPromptGroups = 32;
-// the fused shared-prompt grid runs the decode over the views with this
-// fraction of the plain decode grid's workgroups: a third, with the default
-// grid one workgroup per CU beside the prompt pass's two (the full grid, a
-// quarter and a sixth measured 2%, 6% and 24% slower)
-#ifndef FP8KV_FUSED_DECODE_DIV
-#define FP8KV_FUSED_DECODE_DIV 3
-#endif
-constexpr int kFusedDecodeDiv = FP8KV_FUSED_DECODE_DIV;
-struct PromptGroups {
-  int32_t n;
-  int32_t req_start[kMaxPromptGroups];
-  int32_t req_end[kMaxPromptGroups];
-  int32_t prefix_len[kMaxPromptGroups];
-  int32_t S[kMaxPromptGroups];
-  int32_t tiles[kMaxPromptGroups];
-  int32_t blocks[kMaxPromptGroups];
-  int32_t wg_start[kMaxPromptGroups + 1];
-  int64_t part_base[kMaxPromptGroups + 1];
-};
-
-// the group of request b, or -1
-__device__ __forceinline__ int prompt_group(const PromptGroups& pg, int b) {
-  for (int k = 0; k < pg.n; ++k)
-    if (b >= pg.req_start[k] && b < pg.req_end[k]) return k;
-  return -1;
-}
-
+// The groups are described by PromptGroups (before the decode kernel, whose
+// body can skip each request's prompt pages).
 struct PrefixArgs {
   const uint8_t* k_cache;
   const uint8_t* v_cache;
@@ -1677,7 +1698,7 @@ void shared_fused_kernel(PrefixArgs pa, DecodeArgs da, int32_t prefix_wgs, int32
   if (w < prefix_wgs)
     prefix_body<FP8KV_E4M3, NTP>(pa, w);
   else
-    decode_body<FP8KV_E4M3, FP8KV_DEPTH_E4M3, 1>(da, w - prefix_wgs, decode_wgs);
+    decode_body<FP8KV_E4M3, FP8KV_DEPTH_E4M3, 1, true>(da, w - prefix_wgs, decode_wgs, &pa.pg);
 }
 
 // Output rows of the shared-prompt call: the prompt's S partial states and
@@ -1695,6 +1716,12 @@ struct CombineArgs {
   void* out;
   int32_t batch, Hq, G, max_tokens, out_f32;
   PromptGroups pg;
+  // fold_merge: the own-token decode's split segments are merged here from
+  // its pieces (decode = its arguments, decode_grid = its workgroups); the
+  // rows it wrote whole are read as above
+  int32_t fold_merge;
+  int64_t decode_grid;
+  DecodeArgs decode;
 };
 
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
@@ -1734,9 +1761,25 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       for (int u = 0; u < kMergeUnroll; ++u) merge_state(M, L, O, m[u], l[u], o[u]);
     }
     O *= vsc;  // the prompt's partial sums are in cache units
-    // the own-token rows are normalised: as a state, (lse, 1, row)
-    merge_state(M, L, O, a.suf_lse[row], 1.0f,
-                *reinterpret_cast<const f32x4_t*>(a.suf_out + row * kHeadDim + d));
+    int64_t wf = 0, wl = 0;
+    bool split = false;
+    const int g = h / a.G;
+    const int seg = b * a.decode.Hkv + g;
+    if (a.fold_merge) {
+      const int64_t W = static_cast<int64_t>(a.decode.Hkv) * a.decode.ws_pre[a.batch];
+      split = segment_span(a.decode, seg, W, slice_count(W, a.decode_grid), wf, wl);
+    }
+    if (split) {
+      // the own-token pieces' states (sums in cache units)
+      float Ms = -INFINITY, Ls = 0.f;
+      f32x4_t Os = {0.f, 0.f, 0.f, 0.f};
+      merge_pieces(a.decode, seg, h - g * a.G, d, wf, wl + 1, Ms, Ls, Os);
+      merge_state(M, L, O, Ms, Ls, Os * vsc);
+    } else {
+      // the own-token rows are normalised: as a state, (lse, 1, row)
+      merge_state(M, L, O, a.suf_lse[row], 1.0f,
+                  *reinterpret_cast<const f32x4_t*>(a.suf_out + row * kHeadDim + d));
+    }
     if (L > 0.f) res = O * (1.0f / L);
   }
   const int64_t io = row * kHeadDim + d;
@@ -2244,21 +2287,16 @@ fp8kv_status shared_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
   pa.num_pages = desc->num_pages;
   pa.sm_scale = sm_scale;
   pa.pg = L.pg;
-  // the own-token views first (the decode over them may start beside the
-  // prompt pass)
-  hipLaunchKernelGGL(view_kernel, dim3(batch), dim3(256), 0, stream, pa);
-  st = launched();
-  if (st != FP8KV_OK) return st;
 
-  // the own tokens: the plain decode over the views, f32 rows with their
-  // log-sum-exp, into the workspace
-  a.page_table = pa.view_pt;
-  a.ctx_lens = pa.view_ctx;
+  // the own tokens: the decode past each request's prompt pages, f32 rows
+  // with their log-sum-exp, into the workspace
+  int64_t fused_decode_grid = 0;
   a.out = ws + L.suf_out;
   a.out_f32 = 1;
   a.lse = reinterpret_cast<float*>(ws + L.suf_lse);
   if (desc->cache_dtype == FP8KV_E4M3 && a.C <= kTileCols) {
-    // one grid: the prompt pass, then the decode's workgroups beside it
+    // one grid: the prompt pass, then the decode's workgroups beside it (the
+    // decode skips the prompt pages of the original tables itself)
     const int64_t dblocks = decode_grid(a, workers, num_workers) / kFusedDecodeDiv;
     const int64_t d = dblocks < 1 ? 1 : dblocks;
     if (L.grid + d > 0x7FFFFFFF) return FP8KV_UNSUPPORTED;
@@ -2269,9 +2307,14 @@ fp8kv_status shared_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
       hipLaunchKernelGGL(shared_fused_kernel<1>, dim3(L.grid + d), dim3(kThreads), 0, stream, pa,
                          a, static_cast<int32_t>(L.grid), static_cast<int32_t>(d));
     st = launched();
-    if (st != FP8KV_OK) return st;
-    st = merge_launch(a, d, stream);
+    fused_decode_grid = d;  // combine_kernel merges the split segments
   } else {
+    // the plain decode over materialised views of the tables
+    hipLaunchKernelGGL(view_kernel, dim3(batch), dim3(256), 0, stream, pa);
+    st = launched();
+    if (st != FP8KV_OK) return st;
+    a.page_table = pa.view_pt;
+    a.ctx_lens = pa.view_ctx;
     if (desc->cache_dtype == FP8KV_E4M3) {
       if (L.nt == 2)
         hipLaunchKernelGGL((prefix_kernel<FP8KV_E4M3, 2>), dim3(L.grid), dim3(kThreads), 0, stream, pa);
@@ -2304,6 +2347,9 @@ fp8kv_status shared_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
   ca.max_tokens = max_pages_per_seq * kPage;
   ca.out_f32 = out_dtype == FP8KV_OUT_F32 ? 1 : 0;
   ca.pg = L.pg;
+  ca.fold_merge = fused_decode_grid > 0 ? 1 : 0;
+  ca.decode_grid = fused_decode_grid;
+  ca.decode = a;
   const int64_t threads = static_cast<int64_t>(batch) * num_q_heads * (kHeadDim / 4);
   hipLaunchKernelGGL(combine_kernel, dim3((threads + 255) / 256), dim3(256), 0, stream, ca);
   return launched();
