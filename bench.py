@@ -91,6 +91,33 @@ def time_steps(fn, steps: int):
     return (time.perf_counter() - t0) / steps
 
 
+def warm_up(fns, min_seconds: float = 0.1):
+    """Run the steps in turn for at least min_seconds of wall time.  Right
+    after a state is built the first tens of milliseconds of GPU work run
+    slower (a multi-query step measured 410 us first, 371 us later), so the
+    studies that compare several steps warm each up this way and interleave
+    their timed rounds."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_seconds:
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+
+
+def interleaved_steps(fns, steps: int, rounds: int = 4):
+    """Seconds per step of each fn: rounds of steps // rounds steps each,
+    the fns alternating round by round; the median round of each."""
+    per = max(1, steps // rounds)
+    out = [[] for _ in fns]
+    for r in range(rounds):
+        order = list(range(len(fns))) if r % 2 == 0 else list(range(len(fns)))[::-1]
+        for i in order:
+            out[i].append(time_steps(fns[i], per))
+    return [statistics.median(v) for v in out]
+
+
 def event_times(fns, steps: int):
     """Per-stage HIP-event durations (ms) on the current stream."""
     import torch
@@ -288,8 +315,8 @@ def spec_study(args):
     for _ in range(args.warmup):
         sp.step(True)
         base.step(True)
-    t_spec = time_steps(lambda: sp.step(True), args.steps)
-    t_one = time_steps(lambda: base.step(True), args.steps)
+    warm_up([lambda: sp.step(True), lambda: base.step(True)])
+    t_spec, t_one = interleaved_steps([lambda: sp.step(True), lambda: base.step(True)], args.steps)
     nev = max(20, args.steps // 2)
     td_spec, td_one = event_times([lambda: sp.decode(True), lambda: base.decode(True)], nev)
     ta = event_times([lambda: sp.verify_append() if sp.k_new_q is not None else sp.append(True)],
@@ -350,6 +377,7 @@ def shared_study(args):
         unique_kv = 2 * w.Hkv * 128 * kv_tok
         for _ in range(args.warmup):
             st.step(check_tags=True)
+        warm_up([lambda: st.step(check_tags=True)])
         t = time_steps(lambda: st.step(check_tags=True), args.steps)
         td = statistics.median(event_times([lambda: st.decode(True)], max(20, args.steps // 2))[0]) * 1e-3
         res["shared" if shared else "private"] = {
@@ -376,6 +404,7 @@ def shared_study(args):
                 call()
             for _ in range(args.warmup):
                 cstep()
+            warm_up([cstep])
             tc = time_steps(cstep, args.steps)
             tdc = statistics.median(event_times([call], max(20, args.steps // 2))[0]) * 1e-3
             res["shared_call"] = {
@@ -713,6 +742,7 @@ def main():
             st2 = cycle([lambda s=s: s.step(True) for s in c2])
             for _ in range(10):
                 st2()
+            warm_up([st2])
             t2 = time_steps(st2, 100)
             b2, a2 = alg_bytes(w2, cd, True)
             td2 = statistics.median(
