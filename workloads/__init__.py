@@ -20,8 +20,8 @@ BF16 number approximately N(0,1) distributed.  The low 16 bits decide
 outliers where a workload asks for them.
 
 Workloads follow the five synthetic decode configurations of the design
-(tiny, uniform, ragged, long-context, capacity+integrity).  "Context length"
-L_b is the number of tokens cached *before* the step: the step appends token
+(tiny, uniform, ragged, long-context, capacity+integrity).  A workload's
+context length L_b is the number of tokens cached *before* the step: the step appends token
 L_b and attends over L_b + 1 tokens, i.e. n_b = ceil((L_b+1)/16) pages.
 """
 from __future__ import annotations
