@@ -363,7 +363,7 @@ def shared_study(args):
     from workloads import device
 
     res = {}
-    for shared in (True, False):
+    for shared in ((True,) if args.no_private else (True, False)):
         w = workloads.shared_prefix(shared=shared)
         log(f"bench: {w.name}")
         st = device.build(w)
@@ -418,8 +418,9 @@ def shared_study(args):
                 (out_c - res["out_shared"]).abs().max())
         del st
         torch.cuda.empty_cache()
-    same = bool(torch.equal(res.pop("out_shared"), res.pop("out_private")))
-    sh, pr, sc = res["shared"], res["private"], res["shared_call"]
+    out_pr = res.pop("out_private", None)
+    same = bool(torch.equal(res.pop("out_shared"), out_pr)) if out_pr is not None else None
+    sh, pr, sc = res["shared"], res.get("private"), res["shared_call"]
     print(json.dumps({
         "metric": "shared-prompt decode step (64 requests, one 16,384-token prompt mapped by all "
                   "+ U[16, 2048] own tokens): tokens/s, shared pages vs private copies",
@@ -431,8 +432,8 @@ def shared_study(args):
                    "kv_cache": "e4m3", "tag_check": True},
         "value_is": "shared pages, shared-prompt call (fp8kv_decode_attention_shared)",
         "shared_call": sc, "shared": sh, "private": pr,
-        "step_speedup_shared_pages": round(pr["ms_per_step"] / sh["ms_per_step"], 3),
-        "step_speedup_shared_call": round(pr["ms_per_step"] / sc["ms_per_step"], 3),
+        "step_speedup_shared_pages": round(pr["ms_per_step"] / sh["ms_per_step"], 3) if pr else None,
+        "step_speedup_shared_call": round(pr["ms_per_step"] / sc["ms_per_step"], 3) if pr else None,
         "outputs_bit_identical": same}), flush=True)
 
 
@@ -585,6 +586,8 @@ def main():
     ap.add_argument("--accuracy-configs", type=int, nargs="+", default=[2, 3, 4])
     ap.add_argument("--shared-prefix", action="store_true",
                     help="cache reuse study: a prompt's pages shared by 64 requests vs copies")
+    ap.add_argument("--no-private", action="store_true",
+                    help="--shared-prefix: skip the private-copies workload (shared pages only)")
     ap.add_argument("--cpu-study", action="store_true",
                     help="the oracle on the host, 1 thread and all cores, tiny/uniform/ragged/long")
     ap.add_argument("--qlen", type=int, default=1,
