@@ -45,6 +45,9 @@ class DeviceStep:
     num_workers: int
     workspace: Optional[torch.Tensor]
     out: torch.Tensor
+    # the default step's launches, prepared once per stream (a serving loop's
+    # way: no per-call argument checks on the host)
+    _prepared: Optional[tuple] = dataclasses.field(default=None, repr=False)
 
     @property
     def cache_dtype(self) -> int:
@@ -78,7 +81,22 @@ class DeviceStep:
 
     def step(self, check_tags=True, out_dtype=fp8kv.OUT_BF16, stream=None, fused=True):
         """One decode step: tag check + append (one launch when fused), then
-        attention.  check_tags=False is the no-op tracker path."""
+        attention.  check_tags=False is the no-op tracker path.  The default
+        form (fused, bf16 rows, current stream) runs prepared launches."""
+        if check_tags and fused and out_dtype == fp8kv.OUT_BF16 and stream is None:
+            h = torch.cuda.current_stream().cuda_stream
+            if self._prepared is None or self._prepared[0] != h:
+                va = fp8kv.verify_append(self.desc, self.K, self.V, self.k_scale, self.v_scale,
+                                         self.k_new, self.v_new, self.token_pos, self.page_table,
+                                         self.expected_tags, self.ctx_lens, self.pool_tags,
+                                         abort=self.abort, prepare=True)
+                dec = fp8kv.decode_attention(
+                    self.desc, self.K, self.V, self.k_scale, self.v_scale, self.q, self.page_table,
+                    self.ctx_lens, abort=self.abort, out=self.out, out_dtype=fp8kv.OUT_BF16,
+                    num_workers=self.num_workers, workspace=self.workspace, prepare=True)
+                self._prepared = (h, va, dec)
+            self._prepared[1]()
+            return self._prepared[2]()
         if check_tags and fused:
             self.verify_append(stream)
         else:
@@ -109,6 +127,7 @@ class SpecStep:
     k_new_q: Optional[torch.Tensor] = None   # [B][q_len][Hkv][128] for the fused launch
     v_new_q: Optional[torch.Tensor] = None
     first_pos: Optional[torch.Tensor] = None  # [B]: position of each first new token
+    _prepared: Optional[tuple] = dataclasses.field(default=None, repr=False)
 
     def verify(self, stream=None):
         self.base.verify(stream)
@@ -135,6 +154,23 @@ class SpecStep:
                               s.pool_tags, abort=s.abort, stream=stream)
 
     def step(self, check_tags=True, out_dtype=fp8kv.OUT_BF16, stream=None, fused=True):
+        s = self.base
+        if (check_tags and fused and self.k_new_q is not None and out_dtype == fp8kv.OUT_BF16
+                and stream is None):
+            # prepared launches, once per stream
+            h = torch.cuda.current_stream().cuda_stream
+            if self._prepared is None or self._prepared[0] != h:
+                va = fp8kv.verify_append_q(s.desc, s.K, s.V, s.k_scale, s.v_scale, self.k_new_q,
+                                           self.v_new_q, self.first_pos, s.page_table,
+                                           s.expected_tags, s.ctx_lens, s.pool_tags,
+                                           abort=s.abort, prepare=True)
+                dec = fp8kv.decode_attention_q(
+                    s.desc, s.K, s.V, s.k_scale, s.v_scale, self.q, s.page_table, s.ctx_lens,
+                    abort=s.abort, out=self.out, out_dtype=fp8kv.OUT_BF16,
+                    num_workers=s.num_workers, workspace=self.workspace, prepare=True)
+                self._prepared = (h, va, dec)
+            self._prepared[1]()
+            return self._prepared[2]()
         if check_tags and fused and self.k_new_q is not None:
             self.verify_append(stream)
         else:
