@@ -84,7 +84,11 @@ class DeviceStep:
         attention.  check_tags=False is the no-op tracker path.  The default
         form (fused, bf16 rows, current stream) runs prepared launches."""
         if check_tags and fused and out_dtype == fp8kv.OUT_BF16 and stream is None:
-            h = torch.cuda.current_stream().cuda_stream
+            # prepared again when the stream or any tensor the launches hold changes
+            h = (torch.cuda.current_stream().cuda_stream, self.num_workers,
+                 *map(id, (self.K, self.V, self.k_scale, self.v_scale, self.k_new, self.v_new,
+                           self.token_pos, self.page_table, self.expected_tags, self.ctx_lens,
+                           self.pool_tags, self.abort, self.q, self.out, self.workspace)))
             if self._prepared is None or self._prepared[0] != h:
                 va = fp8kv.verify_append(self.desc, self.K, self.V, self.k_scale, self.v_scale,
                                          self.k_new, self.v_new, self.token_pos, self.page_table,
@@ -157,8 +161,11 @@ class SpecStep:
         s = self.base
         if (check_tags and fused and self.k_new_q is not None and out_dtype == fp8kv.OUT_BF16
                 and stream is None):
-            # prepared launches, once per stream
-            h = torch.cuda.current_stream().cuda_stream
+            # prepared launches, again when the stream or any tensor they hold changes
+            h = (torch.cuda.current_stream().cuda_stream, s.num_workers,
+                 *map(id, (s.K, s.V, s.k_scale, s.v_scale, self.k_new_q, self.v_new_q,
+                           self.first_pos, s.page_table, s.expected_tags, s.ctx_lens, s.pool_tags,
+                           s.abort, self.q, self.out, self.workspace)))
             if self._prepared is None or self._prepared[0] != h:
                 va = fp8kv.verify_append_q(s.desc, s.K, s.V, s.k_scale, s.v_scale, self.k_new_q,
                                            self.v_new_q, self.first_pos, s.page_table,
