@@ -197,25 +197,29 @@ def test_shared_call_matches_oracle(Hq, Hkv, cd):
         print(f"shared call Hq={Hq} Hkv={Hkv} cache={cd} workers={nw}: max abs err {err:.3e}")
 
 
-def test_shared_call_edges():
-    """No prompt is the plain call (bitwise); aborted requests and contexts that
-    stop inside the prompt give +0 rows, the others stay exact; bad prompt
-    lengths are rejected before anything runs."""
+@pytest.mark.parametrize("cd", [0, 1])
+def test_shared_call_edges(cd):
+    """No prompt is the plain call (bitwise); aborted requests, contexts that
+    stop inside the prompt and contexts longer than the table holds give +0
+    rows, the others stay exact; bad prompt lengths are rejected before
+    anything runs.  The e4m3 cache takes the one-grid path (prompt pass and
+    own-token decode together), the bf16 cache the separate launches."""
     import decode_attention_paged_fp8kv_amd as fp8kv
     from _helpers import oracle_state
-    w, st = _shared_state(8, 2)
+    w, st = _shared_state(8, 2, cd, B=6)
     plain = st.decode(True, out_dtype=fp8kv.OUT_F32).cpu().numpy()
     assert np.array_equal(_shared_call(fp8kv, w, st, fp8kv.OUT_F32, prefix=0), plain)
-    ab = torch.tensor([0, 1, 0, 0, 0], dtype=torch.uint8, device="cuda")
+    ab = torch.tensor([0, 1, 0, 0, 0, 0], dtype=torch.uint8, device="cuda")
     ctx = w.ctx_lens.copy()
+    ctx[2] = 16 * w.max_pages + 1    # longer than the table holds (fail closed)
     ctx[3] = w.prefix_len            # ends exactly at the end of the prompt
     ctx[4] = 20                      # ends inside the prompt
     o = _shared_call(fp8kv, w, st, fp8kv.OUT_F32, ctx=torch.from_numpy(ctx).cuda(), abort=ab)
-    assert (o[[1, 3, 4]] == 0).all()
-    Ko, Vo = oracle_state(w, st.k_scale_host, st.v_scale_host)
+    assert (o[[1, 2, 3, 4]] == 0).all()
+    Ko, Vo = oracle_state(w, st.k_scale_host, st.v_scale_host, cd)
     ref, _ = oracle.attention(Ko, Vo, st.k_scale_host, st.v_scale_host, w.q_bits(), w.page_table,
-                              w.ctx_lens, SM_SCALE)
-    check_outputs(o[[0, 2]], None, ref[[0, 2]])
+                              w.ctx_lens, SM_SCALE, cache_dtype=cd)
+    check_outputs(o[[0, 5]], None, ref[[0, 5]])
     assert fp8kv.decode_workspace_size_shared(st.desc, w.B, w.Hq, w.max_pages, [0, w.B], [8]) == 0
     for bad in (8, -16, 16 * (w.max_pages + 1)):
         with pytest.raises(fp8kv.Fp8kvError) as e:
