@@ -22,12 +22,16 @@
 //                           (max, sum, weighted V) partial for a split segment
 //   merge_flat_kernel,      log-sum-exp merge of the partials in workgroup
 //   merge_grouped_kernel    order (few pieces per segment / many)
-//   prefix_kernel<C>        prompts shared by groups of requests: each one's
+//   prefix_kernel<C, NT>    prompts shared by groups of requests: each one's
 //                           pages read once per kv-head with the group's
 //                           (request, q-head) pairs as MFMA columns
+//   shared_fused_kernel<NT> that prompt pass and the decode of the requests'
+//                           own tokens in one grid (e4m3, up to 16 columns)
 //   view_kernel             each request's table and context past its prompt
+//                           (the separate-launch form)
 //   combine_kernel          the prompt's partials and the own-token rows joined
-//                           by log-sum-exp
+//                           by log-sum-exp (after the fused grid it also merges
+//                           the own-token decode's split segments)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -455,11 +459,12 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_append_kernel(VerifyApp
 // ---------------------------------------------------------------------------
 // 4. decode: persistent workgroups, equal work per workgroup
 // ---------------------------------------------------------------------------
-// Work list: for every live request b (in order) and kv-head g, the n_b pages
-// the step reads: W = Hkv * sum_b n_b page-tiles (one tile = 16 tokens of one
-// kv-head: 2 KiB of K + 2 KiB of V for e4m3).  Workgroup w of NWG takes items
-// [w*W/NWG, (w+1)*W/NWG), so every workgroup moves the same number of bytes
-// however ragged the lengths.  Its slice is cut at (request, kv-head)
+// Work list: for every live request b (in order) and kv-head g, a segment of
+// kPieceItems items that read nothing (a piece's fixed cost) and then the n_b
+// pages the step reads: W = Hkv * sum_b (kPieceItems + n_b) items (one page
+// item = 16 tokens of one kv-head: 2 KiB of K + 2 KiB of V for e4m3).
+// Workgroup w of NWG takes items [w*W/NWG, (w+1)*W/NWG), so every workgroup
+// gets the same cost however ragged the lengths.  Its slice is cut at (request, kv-head)
 // boundaries into pieces; inside a piece the 4 waves take pages round robin,
 // each with its own online softmax, and are merged through LDS at the end of
 // the piece.  A piece that is a whole segment writes the output; any other
