@@ -15,8 +15,8 @@ from _helpers import SM_SCALE, check_outputs, oracle_state, unswizzle
 
 pytestmark = pytest.mark.gpu
 
-PLAIN_CASES = 24
-SHARED_CASES = 12
+PLAIN_CASES = 96
+SHARED_CASES = 48
 
 
 def _host(t):
