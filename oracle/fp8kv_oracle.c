@@ -69,25 +69,34 @@ void oracle_e4m3_table(double *out256) {
 /* |v| beyond the largest magnitude saturates to 0x7E (448); +-inf too.       */
 /* The sign bit is copied from v (so -0 and negative underflow give 0x80).    */
 /* NaN gives 0x7F with the sign of v.                                         */
+/* The 127 magnitudes and the 126 midpoints between neighbours are taken     */
+/* once from the decode above (each midpoint is exact in binary64: a few     */
+/* significant bits); encoding is a binary search over the magnitudes and    */
+/* one exact comparison with the midpoint.                                   */
 /* ------------------------------------------------------------------------ */
+static double g_mag[127];  /* magnitude of code c, c = 0..126 */
+static double g_mid[126];  /* midpoint of codes c and c+1     */
+
+__attribute__((constructor)) static void build_encode_tables(void) {
+    for (int c = 0; c < 127; ++c) g_mag[c] = oracle_e4m3_decode((uint8_t)c);
+    for (int c = 0; c < 126; ++c) g_mid[c] = (g_mag[c] + g_mag[c + 1]) / 2.0;
+}
+
 uint8_t oracle_e4m3_encode(double v) {
     uint8_t sign = signbit(v) ? 0x80 : 0x00;
     if (isnan(v)) return (uint8_t)(sign | 0x7F);
     double a = fabs(v);
-    double top = oracle_e4m3_decode(0x7E);
-    if (a >= top) return (uint8_t)(sign | 0x7E);
+    if (a >= g_mag[126]) return (uint8_t)(sign | 0x7E);
     /* largest c in [0,126) with mag(c) <= a, by binary search */
     int lo = 0, hi = 126; /* invariant: mag(lo) <= a < mag(hi) */
     while (hi - lo > 1) {
         int mid = (lo + hi) / 2;
-        if (oracle_e4m3_decode((uint8_t)mid) <= a)
+        if (g_mag[mid] <= a)
             lo = mid;
         else
             hi = mid;
     }
-    double m_lo = oracle_e4m3_decode((uint8_t)lo);
-    double m_hi = oracle_e4m3_decode((uint8_t)hi);
-    double midpoint = (m_lo + m_hi) / 2.0; /* exact: few significant bits */
+    double midpoint = g_mid[lo]; /* between lo and hi = lo + 1 */
     int c;
     if (a < midpoint)
         c = lo;
@@ -188,10 +197,16 @@ int oracle_append(int32_t cache_dtype, int32_t num_pages, int32_t page_size,
                   const uint16_t *v_new, int32_t num_tokens, const int32_t *token_seq,
                   const int32_t *token_pos, const int32_t *page_table,
                   int32_t max_pages, const uint8_t *abort_flags) {
+    /* 1. where each token goes: page and slot (page -1: nowhere) */
+    size_t nt = (size_t)(num_tokens > 0 ? num_tokens : 1);
+    int32_t *dst_page = (int32_t *)malloc(sizeof(int32_t) * nt);
+    int32_t *dst_slot = (int32_t *)malloc(sizeof(int32_t) * nt);
     int skipped = 0;
     for (long t = 0; t < num_tokens; ++t) {
         int b = token_seq[t];
         int pos = token_pos[t];
+        dst_page[t] = -1;
+        dst_slot[t] = 0;
         if (abort_flags && abort_flags[b]) continue;
         if (pos < 0 || pos / page_size >= max_pages) {
             ++skipped;
@@ -202,11 +217,25 @@ int oracle_append(int32_t cache_dtype, int32_t num_pages, int32_t page_size,
             ++skipped;
             continue;
         }
-        int slot = pos % page_size;
-        for (int h = 0; h < num_kv_heads; ++h) {
-            long dst = (((long)page * num_kv_heads + h) * page_size + slot) * head_dim;
+        dst_page[t] = page;
+        dst_slot[t] = pos % page_size;
+    }
+    /* 2. the elements: every (kv-head, dim) column is independent of the
+     *    others; inside a column the tokens go in order, so a slot named by
+     *    several tokens keeps the last one, as a plain loop over tokens would.
+     *    Columns are taken 32 dims at a time (one task per block). */
+    const int blk = 32;
+    long blocks = (long)num_kv_heads * ((head_dim + blk - 1) / blk);
+#pragma omp parallel for schedule(static)
+    for (long k = 0; k < blocks; ++k) {
+        int h = (int)(k / ((head_dim + blk - 1) / blk));
+        int d0 = (int)(k % ((head_dim + blk - 1) / blk)) * blk;
+        int d1 = d0 + blk < head_dim ? d0 + blk : head_dim;
+        for (long t = 0; t < num_tokens; ++t) {
+            if (dst_page[t] < 0) continue;
+            long dst = (((long)dst_page[t] * num_kv_heads + h) * page_size + dst_slot[t]) * head_dim;
             long src = ((long)t * num_kv_heads + h) * head_dim;
-            for (int d = 0; d < head_dim; ++d) {
+            for (int d = d0; d < d1; ++d) {
                 if (cache_dtype == 0) {
                     float kq = (float)(bf16_value(k_new[src + d]) / (double)k_scale[h]);
                     float vq = (float)(bf16_value(v_new[src + d]) / (double)v_scale[h]);
@@ -219,6 +248,8 @@ int oracle_append(int32_t cache_dtype, int32_t num_pages, int32_t page_size,
             }
         }
     }
+    free(dst_slot);
+    free(dst_page);
     return skipped;
 }
 

@@ -98,3 +98,24 @@ def test_bf16_cache_copies_bits():
     for b in range(B):
         assert (K[pt[b, L[b] // 16], :, L[b] % 16] == kn[b]).all()
         assert (V[pt[b, L[b] // 16], :, L[b] % 16] == vn[b]).all()
+
+
+def test_slot_named_twice_keeps_the_later_token():
+    """Tokens are written in order: when two tokens name the same slot the
+    cache holds the later one (the plain loop's result, whatever the threads)."""
+    L, pt, kn, vn = _one_step_inputs()
+    B, Hkv, D = kn.shape
+    sc = np.ones(Hkv, np.float32)
+    seq = np.array([0, 2, 0, 1, 0], np.int32)
+    pos = np.array([L[0], L[2], L[0], L[1], L[0]], np.int32)
+    kk = np.stack([kn[0], kn[2], kn[1], kn[1], kn[2]])
+    vv = np.stack([vn[0], vn[2], vn[1], vn[1], vn[2]])
+    K, V = oracle.new_cache(12, Hkv)
+    oracle.append(K, V, sc, sc, kk, vv, seq, pos, pt)
+    K1, V1 = oracle.new_cache(12, Hkv)
+    for t in range(5):   # one token per call: the order is explicit
+        oracle.append(K1, V1, sc, sc, kk[t:t + 1], vv[t:t + 1], seq[t:t + 1], pos[t:t + 1], pt)
+    assert (K == K1).all() and (V == V1).all()
+    page, slot = pt[0, L[0] // 16], L[0] % 16
+    for h in range(Hkv):
+        assert (K[page, h, slot] == bitlevel_encode(workloads.bf16_bits_to_f32(kn[2, h]))).all()

@@ -14,6 +14,32 @@ def test_backends_bit_identical():
             assert (a.view(np.int16) == b.numpy()).all()
 
 
+def test_host_backend_matches_numpy():
+    """The C backend (full-size oracle inputs) against the numpy definition:
+    keys across the 32-bit range, counters that wrap past 2^32, outliers."""
+    rng = np.random.default_rng(5)
+    cases = [(1, 0, 10), (0xDEADBEEF, 12345, 70_001), (2 ** 32 - 1, 2 ** 32 - 5000, 9_000),
+             (7, 3 * 2 ** 31, 4_096)]
+    cases += [(int(rng.integers(0, 2 ** 32)), int(rng.integers(0, 2 ** 34)),
+               int(rng.integers(1, 200_000))) for _ in range(12)]
+    for key, start, count in cases:
+        for outl, ob in ((0, workloads.BF16_20), (66, workloads.BF16_20), (4000, workloads.BF16_25)):
+            a = workloads.draw_bits(key, start, count, "numpy", outlier_per_65536=outl,
+                                    outlier_bits=ob)
+            b = workloads.draw_bits(key, start, count, "host", outlier_per_65536=outl,
+                                    outlier_bits=ob)
+            assert a.dtype == b.dtype == np.uint16 and (a == b).all(), (key, start, count, outl)
+    w = workloads.make(4, batch=2)
+    L = int(w.ctx_before[1])
+    for which in "kv":
+        assert (w.kv_tokens(which, 1, L - 40, L + 1) ==
+                w.kv_tokens(which, 1, L - 40, L + 1, backend="host")).all()
+    s = workloads.shared_prompts([(3, 64)], plain=2)
+    for b in range(s.B):
+        n = int(s.ctx_before[b]) + 1
+        assert (s.kv_tokens("k", b, 0, n) == s.kv_tokens("k", b, 0, n, backend="host")).all()
+
+
 def test_workload_streams_bit_identical():
     w = workloads.make(4, batch=1)
     L = int(w.ctx_before[0])

@@ -10,7 +10,10 @@ tensor can be regenerated on its own, bit-identically, by two backends:
 
 * ``numpy`` (host, uint32 arithmetic) -- used by the oracle side;
 * ``torch`` (any device, int64 arithmetic masked to 32 bits) -- used to build
-  full-size inputs directly in device memory.
+  full-size inputs directly in device memory;
+* ``host`` (the same generator in C with OpenMP, ``gen.c``) -- the numpy
+  backend's values at full-size speed, for oracle-side inputs of the full
+  workloads (checked against the numpy backend bit for bit).
 
 Generator: the 32-bit integer finaliser "lowbias32" (x ^= x>>16; x *= 0x7feb352d;
 x ^= x>>15; x *= 0x846ca68b; x ^= x>>16), applied to (element counter + stream
@@ -65,6 +68,42 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # counter-based generator, two backends
 # --------------------------------------------------------------------------
+_GEN_LIB = None
+
+
+def _gen_lib():
+    """ctypes handle of libgen.so (built with gcc on first use)."""
+    global _GEN_LIB
+    if _GEN_LIB is None:
+        import ctypes
+        import os
+        here = os.path.dirname(os.path.abspath(__file__))
+        path = os.path.join(here, "libgen.so")
+        if not os.path.exists(path):
+            import importlib.util
+            spec = importlib.util.spec_from_file_location("workloads_build",
+                                                          os.path.join(here, "build.py"))
+            mod = importlib.util.module_from_spec(spec)
+            spec.loader.exec_module(mod)
+            mod.build()
+        lib = ctypes.CDLL(path)
+        lib.gen_draw_bits.restype = None
+        lib.gen_draw_bits.argtypes = [ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int64,
+                                      ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint16,
+                                      ctypes.c_void_p]
+        _GEN_LIB = lib
+    return _GEN_LIB
+
+
+def _draw_host(key: int, start: int, count: int, outlier_per_65536: int,
+               outlier_bits) -> np.ndarray:
+    out = np.empty(count, np.uint16)
+    _gen_lib().gen_draw_bits(int(key) & _M32, int(start), int(count),
+                             NORMAL_BF16.ctypes.data, int(outlier_per_65536),
+                             int(outlier_bits), out.ctypes.data)
+    return out
+
+
 def _hash_np(x: np.ndarray) -> np.ndarray:
     x = x.astype(np.uint32, copy=True)
     x ^= x >> np.uint32(16)
@@ -105,14 +144,17 @@ def draw_bits(key: int, start: int, count: int, backend: str = "numpy",
               device=None, outlier_per_65536: int = 0, outlier_bits=BF16_20):
     """BF16 bit patterns for counters [start, start+count) of one stream.
 
-    numpy backend returns uint16; torch backend returns int16 (same bits).
+    numpy and host backends return uint16; torch backend returns int16 (same
+    bits).
     """
     if count == 0:
-        if backend == "numpy":
+        if backend in ("numpy", "host"):
             return np.zeros(0, np.uint16)
         import torch
         return torch.zeros(0, dtype=torch.int16, device=device)
     key, start, count = int(key), int(start), int(count)
+    if backend == "host":
+        return _draw_host(key, start, count, outlier_per_65536, outlier_bits)
     if backend == "numpy":
         ctr = np.arange(start, start + count, dtype=np.uint64)
         x = ((ctr + np.uint64(key)) & np.uint64(_M32)).astype(np.uint32)
@@ -270,14 +312,15 @@ class Workload:
         parts = [draw_bits(self._prefix_key(which, k) if pre else self._kv_key(which, b),
                            a * per_tok, (c - a) * per_tok, backend, device, self.outlier_per_65536)
                  for pre, a, c in self._split(b, t0, t1)]
+        host = backend in ("numpy", "host")
         if len(parts) == 1:
             bits = parts[0]
-        elif backend == "numpy":
+        elif host:
             bits = np.concatenate(parts)
         else:
             import torch
             bits = torch.cat(parts)
-        if backend == "numpy":
+        if host:
             bits = bits.reshape(t1 - t0, self.Hkv, self.D)
         else:
             bits = bits.view(t1 - t0, self.Hkv, self.D)
@@ -285,7 +328,7 @@ class Workload:
         if with_saturation and self.saturate_new and t0 <= L < t1:
             for d, sgn in zip((5, 40, 77, 120), (0, 0x8000, 0, 0x8000)):
                 v = np.uint16(int(BF16_25) | sgn)
-                if backend == "numpy":
+                if host:
                     bits[L - t0, 0, d] = v
                 else:
                     bits[L - t0, 0, d] = int(v.view(np.int16))
