@@ -135,6 +135,46 @@ def _dev(t: Optional[torch.Tensor], dtypes, name: str, allow_none: bool = False)
     return t.data_ptr()
 
 
+def _shape(t, shape, name: str):
+    """t has exactly this shape (None: any extent along that axis)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dim() != len(shape) or any(e is not None and t.shape[i] != e for i, e in enumerate(shape)):
+        want = "[" + ", ".join("*" if e is None else str(e) for e in shape) + "]"
+        raise ValueError(f"{name}: shape {list(t.shape)}, expected {want}")
+
+
+def _min_numel(t, n: int, name: str):
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{name}: {t.numel()} elements, at least {n} needed")
+
+
+def _min_bytes(t, n: int, name: str):
+    if t is not None and t.numel() * t.element_size() < n:
+        raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, at least {n} needed")
+
+
+def _check_cache(d: "CacheDesc", k_cache, v_cache, k_scale, v_scale):
+    """The pools hold cache_bytes(d) bytes each; an e4m3 cache has Hkv scales."""
+    n = cache_bytes(d)
+    if n == 0:
+        raise ValueError("invalid cache descriptor")
+    _min_bytes(k_cache, n, "k_cache")
+    _min_bytes(v_cache, n, "v_cache")
+    if d.cache_dtype == E4M3:
+        _min_numel(k_scale, d.num_kv_heads, "k_scale")
+        _min_numel(v_scale, d.num_kv_heads, "v_scale")
+
+
+def _check_out(out, shape, out_dtype: int):
+    _shape(out, shape, "out")
+    ok = (torch.bfloat16, torch.int16, torch.uint16) if out_dtype == OUT_BF16 else (torch.float32,)
+    if out_dtype not in (OUT_BF16, OUT_F32):
+        raise ValueError(f"out_dtype {out_dtype}: OUT_BF16 or OUT_F32")
+    if out.dtype not in ok:
+        raise ValueError(f"out: dtype {out.dtype} does not hold out_dtype {out_dtype}")
+
+
 _BITS16 = (torch.bfloat16, torch.int16, torch.uint16)
 _I32 = (torch.int32,)
 _U32 = (torch.int32, torch.uint32)
@@ -224,6 +264,7 @@ class Pool:
         return out
 
     def sync(self, d_tags: torch.Tensor, stream=None):
+        _min_numel(d_tags, self.num_pages, "d_tags")
         _dev(d_tags, _U32, "d_tags")
         _check(_pool_sync(self._h, d_tags.data_ptr(), _stream(stream)), "pool_sync")
 
@@ -259,10 +300,15 @@ def verify_tags(page_table, expected_tags, ctx_lens, pool_tags, abort=None, stre
                 prepare: bool = False):
     """Batched page-tag check; returns the uint8 abort tensor [B] (or, with
     prepare=True, a Launch that runs the check and returns it)."""
+    _shape(ctx_lens, (None,), "ctx_lens")
     B = ctx_lens.shape[0]
+    _shape(page_table, (B, None), "page_table")
+    P = page_table.shape[1]
+    _shape(expected_tags, (B, P), "expected_tags")
+    _shape(pool_tags, (None,), "pool_tags")
+    _min_numel(abort, B, "abort")
     if abort is None:
         abort = torch.empty(B, dtype=torch.uint8, device=ctx_lens.device)
-    P = page_table.shape[1] if page_table.dim() == 2 else 0
     args = (_dev(page_table, _I32, "page_table"), _dev(expected_tags, _U32, "expected_tags"),
             P, _dev(ctx_lens, _I32, "ctx_lens"), B, _dev(pool_tags, _U32, "pool_tags"),
             pool_tags.shape[0], PAGE_SIZE, _dev(abort, _U8, "abort"), _stream(stream))
@@ -273,7 +319,14 @@ def verify_tags(page_table, expected_tags, ctx_lens, pool_tags, abort=None, stre
 def append(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, k_new, v_new, token_seq, token_pos,
            page_table, abort=None, stream=None, prepare: bool = False):
     """Quantize-on-append of num_tokens new K/V rows ([T][Hkv][128] BF16)."""
+    _shape(token_seq, (None,), "token_seq")
     T = token_seq.shape[0]
+    _shape(token_pos, (T,), "token_pos")
+    _shape(k_new, (T, d.num_kv_heads, HEAD_DIM), "k_new")
+    _shape(v_new, (T, d.num_kv_heads, HEAD_DIM), "v_new")
+    _shape(page_table, (None, None), "page_table")
+    _min_numel(abort, page_table.shape[0], "abort")
+    _check_cache(d, k_cache, v_cache, k_scale, v_scale)
     fp8 = d.cache_dtype == E4M3
     args = (ctypes.byref(d), _dev(k_cache, _U8 + _BITS16, "k_cache"),
             _dev(v_cache, _U8 + _BITS16, "v_cache"),
@@ -288,12 +341,29 @@ def append(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, k_new, v_new, token
                  page_table, abort), prepare)
 
 
+def _check_verify_append(d, k_cache, v_cache, k_scale, v_scale, new_pos, page_table,
+                         expected_tags, pool_tags, abort, B):
+    _check_cache(d, k_cache, v_cache, k_scale, v_scale)
+    _shape(new_pos, (B,), "new_pos")
+    _shape(page_table, (B, None), "page_table")
+    _shape(expected_tags, tuple(page_table.shape), "expected_tags")
+    _shape(pool_tags, (None,), "pool_tags")
+    # the kernel reads the current tag of any page id below num_pages
+    _min_numel(pool_tags, d.num_pages, "pool_tags")
+    _min_numel(abort, B, "abort")
+
+
 def verify_append(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, k_new, v_new, new_pos,
                   page_table, expected_tags, ctx_lens, pool_tags, abort=None, stream=None,
                   prepare: bool = False):
     """Tag check + the step's append in one launch (one new token per request);
     returns the uint8 abort tensor [B]."""
+    _shape(ctx_lens, (None,), "ctx_lens")
     B = ctx_lens.shape[0]
+    _check_verify_append(d, k_cache, v_cache, k_scale, v_scale, new_pos, page_table,
+                         expected_tags, pool_tags, abort, B)
+    _shape(k_new, (B, d.num_kv_heads, HEAD_DIM), "k_new")
+    _shape(v_new, (B, d.num_kv_heads, HEAD_DIM), "v_new")
     if abort is None:
         abort = torch.empty(B, dtype=torch.uint8, device=ctx_lens.device)
     fp8 = d.cache_dtype == E4M3
@@ -317,7 +387,13 @@ def verify_append_q(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, k_new, v_n
     """Tag check + the append of q_len new tokens per request in one launch:
     k_new / v_new [B][q_len][Hkv][128], token i of request b at position
     new_pos[b] + i; returns the uint8 abort tensor [B]."""
-    B, T = k_new.shape[0], k_new.shape[1]
+    _shape(ctx_lens, (None,), "ctx_lens")
+    B = ctx_lens.shape[0]
+    _shape(k_new, (B, None, d.num_kv_heads, HEAD_DIM), "k_new")
+    T = k_new.shape[1]
+    _shape(v_new, (B, T, d.num_kv_heads, HEAD_DIM), "v_new")
+    _check_verify_append(d, k_cache, v_cache, k_scale, v_scale, new_pos, page_table,
+                         expected_tags, pool_tags, abort, B)
     if abort is None:
         abort = torch.empty(B, dtype=torch.uint8, device=ctx_lens.device)
     fp8 = d.cache_dtype == E4M3
@@ -343,17 +419,27 @@ def decode_workspace_size(d: CacheDesc, batch: int, num_q_heads: int, num_worker
     return int(_ws_size(ctypes.byref(d), batch, num_q_heads, num_workers))
 
 
+def _check_decode(d, k_cache, v_cache, k_scale, v_scale, page_table, ctx_lens, abort, B):
+    _check_cache(d, k_cache, v_cache, k_scale, v_scale)
+    _shape(page_table, (B, None), "page_table")
+    _shape(ctx_lens, (B,), "ctx_lens")
+    _min_numel(abort, B, "abort")
+
+
 def decode_attention(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, page_table, ctx_lens,
                      abort=None, out=None, out_dtype: int = OUT_BF16,
                      sm_scale: Optional[float] = None, num_workers: int = 0, workspace=None,
                      stream=None, prepare: bool = False):
     """Paged decode attention; returns out [B][Hq][128] (bf16 or f32)."""
+    _shape(q, (None, None, HEAD_DIM), "q")
     B, Hq, D = q.shape
+    _check_decode(d, k_cache, v_cache, k_scale, v_scale, page_table, ctx_lens, abort, B)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((B, Hq, D), device=q.device,
                           dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32)
+    _check_out(out, (B, Hq, D), out_dtype)
     need = decode_workspace_size(d, B, Hq, num_workers)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -385,12 +471,15 @@ def decode_attention_q(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, page
     """Decode attention with q_len queries per request (several new tokens checked
     at once; query i attends the cache up to its own token).  q [B][q_len][Hq][128];
     ctx_lens counts tokens after all q_len new ones; returns out [B][q_len][Hq][128]."""
+    _shape(q, (None, None, None, HEAD_DIM), "q")
     B, T, Hq, D = q.shape
+    _check_decode(d, k_cache, v_cache, k_scale, v_scale, page_table, ctx_lens, abort, B)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((B, T, Hq, D), device=q.device,
                           dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32)
+    _check_out(out, (B, T, Hq, D), out_dtype)
     need = decode_workspace_size_q(d, B, Hq, T, num_workers)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -436,13 +525,16 @@ def decode_attention_shared(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q,
     group_start[k+1]) continue prompt k of prefix_len[k] tokens (a multiple of
     16), on the pages their tables list first: each prompt's pages are read
     once per kv-head for its whole group.  Returns out [B][Hq][128]."""
+    _shape(q, (None, None, HEAD_DIM), "q")
     B, Hq, D = q.shape
+    _check_decode(d, k_cache, v_cache, k_scale, v_scale, page_table, ctx_lens, abort, B)
     gs, pl = _groups(group_start, prefix_len)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((B, Hq, D), device=q.device,
                           dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32)
+    _check_out(out, (B, Hq, D), out_dtype)
     P = page_table.shape[1]
     need = decode_workspace_size_shared(d, B, Hq, P, gs, pl, num_workers)
     if workspace is None or workspace.numel() * workspace.element_size() < need:

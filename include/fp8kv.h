@@ -202,7 +202,12 @@ fp8kv_status fp8kv_append(const fp8kv_cache_desc *desc, void *d_k_cache, void *d
 /* quantizes the request's new token (d_k_new/d_v_new row b, BF16             */
 /* [batch][Hkv][128]) into position d_new_pos[b].  The check is still its    */
 /* own batched pass ahead of attention, as the integrity section describes.  */
-/* Hkv <= 16 (one workgroup encodes the whole token).                        */
+/* Fail closed: the new token must lie inside the context that was checked   */
+/* (0 <= d_new_pos[b] < d_ctx_lens[b]), so that every page written is one    */
+/* whose tag was compared; otherwise the request is aborted (d_abort[b] = 1) */
+/* and nothing is written.  Page counts are computed in 64 bits: a length    */
+/* near INT32_MAX aborts (its pages do not fit the table) instead of         */
+/* wrapping.  Hkv <= 16 (one workgroup encodes the whole token).             */
 /* ------------------------------------------------------------------------ */
 fp8kv_status fp8kv_verify_append(const fp8kv_cache_desc *desc, void *d_k_cache, void *d_v_cache,
                                  const float *d_k_scale, const float *d_v_scale,
@@ -216,8 +221,10 @@ fp8kv_status fp8kv_verify_append(const fp8kv_cache_desc *desc, void *d_k_cache, 
 /* The same with q_len new tokens per request (several tokens checked in one  */
 /* step, speculative decoding): d_k_new/d_v_new BF16 [batch][q_len][Hkv][128], */
 /* token i of request b goes to position d_new_pos[b] + i, all only if the    */
-/* request's check passed.  q_len = 1 is fp8kv_verify_append.  Errors as      */
-/* above, and FP8KV_INVALID_ARG for q_len < 1.                                */
+/* request's check passed and all q_len positions lie inside the checked     */
+/* context (d_new_pos[b] >= 0 and d_new_pos[b] + q_len <= d_ctx_lens[b]; else  */
+/* the request aborts and writes nothing).  q_len = 1 is fp8kv_verify_append. */
+/* Errors as above, and FP8KV_INVALID_ARG for q_len < 1.                      */
 fp8kv_status fp8kv_verify_append_q(const fp8kv_cache_desc *desc, void *d_k_cache,
                                    void *d_v_cache, const float *d_k_scale,
                                    const float *d_v_scale, const uint16_t *d_k_new,
@@ -316,11 +323,14 @@ fp8kv_status fp8kv_decode_attention_q(const fp8kv_cache_desc *desc, const void *
 /*   h_prefix_len: host int32 [num_groups], tokens of group k's prompt, a     */
 /*   multiple of 16, at most 16*max_pages_per_seq (0: no shared prompt).      */
 /*   Every request of group k lists the prompt's prefix_len/16 pages first in */
-/*   its table; they are read from the table of the group's first request    */
-/*   (the caller's contract; the tag check reads each request's own table).  */
-/*   Rows of requests whose context does not extend past their prompt (ctx <= */
-/*   prefix_len), of aborted requests and of contexts the table cannot hold   */
-/*   are +0.  The host arrays are read during the call only.                 */
+/*   its table; they are read from the table of the group's first request.   */
+/*   The tag check reads each request's own table, so the call fails closed: */
+/*   a member whose first prefix_len/16 entries differ from the first        */
+/*   request's gets +0 rows (whatever its abort flag), and each member's rows */
+/*   depend only on its own flag (an aborted first request does not affect   */
+/*   the others).  Rows of requests whose context does not extend past their  */
+/*   prompt (ctx <= prefix_len), of aborted requests and of contexts the table */
+/*   cannot hold are +0 too.  The host arrays are read during the call only.  */
 /*   d_workspace: at least fp8kv_decode_workspace_size_shared() bytes (same  */
 /*   groups; 0 for invalid arguments).  Errors as fp8kv_decode_attention,     */
 /*   and FP8KV_INVALID_ARG for a bad group description.                      */

@@ -71,21 +71,49 @@ def bf16_to_f32(bits) -> np.ndarray:
     return workloads.bf16_bits_to_f32(np.asarray(bits).view(np.uint16))
 
 
+def bf16_neighbours_ok(bf16_bits: np.ndarray, ref64: np.ndarray) -> np.ndarray:
+    """Whether each bf16 value is one of the two bf16 numbers that bracket the
+    binary64 value (the value itself when it is a bf16 number).  Normal range
+    only (|ref| >= 2^-126): bf16 keeps 8 significant bits there."""
+    got = bf16_to_f32(bf16_bits).astype(np.float64)
+    a = np.abs(ref64)
+    _, e = np.frexp(a)                       # a = m * 2^e, m in [0.5, 1)
+    sp = np.ldexp(1.0, e - 8)                # bf16 spacing at a
+    lo = np.floor(a / sp) * sp
+    hi = np.ceil(a / sp) * sp
+    same_sign = (np.signbit(got) == np.signbit(ref64)) | (got == 0)
+    return same_sign & ((np.abs(got) == lo) | (np.abs(got) == hi))
+
+
 def check_outputs(got_f32: np.ndarray, got_bf16_bits: np.ndarray, ref64: np.ndarray,
                   tol: float = 2e-3):
-    """Tolerance of the attention output (f32 and bf16 modes).
+    """Tolerance of the attention output (reading A9 of the 2e-3 bound).
 
     f32 mode: |o_gpu - o_oracle| <= tol everywhere.
-    bf16 mode: the bf16 output is the round-to-nearest-even of the f32 output
-    (bitwise), hence within tol + half a bf16 step (2^-8 relative) of the
-    oracle."""
+    bf16 mode: the bf16 output is bitwise the round-to-nearest-even of the f32
+    output; where |o_oracle| < 1 it is within tol of the oracle, where
+    |o_oracle| >= 1 it is one of the two bf16 neighbours of the oracle's
+    value (bf16 spacing alone exceeds tol there).
+    Returns the max abs error of the f32 output."""
     err = np.abs(got_f32.astype(np.float64) - ref64)
     assert np.isfinite(got_f32).all()
     assert err.max() <= tol, f"max abs err {err.max():.3e}"
     if got_bf16_bits is not None:
+        gb = np.asarray(got_bf16_bits).view(np.uint16)
         f = np.ascontiguousarray(got_f32, np.float32).view(np.uint32).astype(np.uint64)
         rne = ((f + 0x7FFF + ((f >> 16) & 1)) >> 16).astype(np.uint16)
-        assert (np.asarray(got_bf16_bits).view(np.uint16) == rne).all()
-        eb = np.abs(bf16_to_f32(got_bf16_bits).astype(np.float64) - ref64)
-        assert (eb <= tol + np.abs(ref64) * 2.0 ** -8 + 1e-30).all()
+        assert (gb == rne).all(), "bf16 output is not the RNE of the f32 output"
+        small = np.abs(ref64) < 1.0
+        eb = np.abs(bf16_to_f32(gb).astype(np.float64) - ref64)
+        assert (eb[small] <= tol).all(), f"bf16 err {eb[small].max():.3e} where |o| < 1"
+        assert bf16_neighbours_ok(gb[~small], ref64[~small]).all(), \
+            "bf16 output not a neighbour of the oracle where |o| >= 1"
     return float(err.max())
+
+
+def bf16_differences(got_bf16_bits: np.ndarray, ref_bf16_bits: np.ndarray) -> int:
+    """bf16 output elements that differ from the oracle's own bf16 rounding of
+    its binary64 result (reported, not bounded: a value within the f32 error
+    of a rounding midpoint may go either way)."""
+    return int((np.asarray(got_bf16_bits).view(np.uint16) !=
+                np.asarray(ref_bf16_bits).view(np.uint16)).sum())

@@ -174,3 +174,110 @@ def test_shared_prompt_workspace():
                    ([10, 5], [16]), ([-1, 5], [16]), ([0] * 34, [16] * 33)):
         assert ws(d, 64, 64, 1100, gs, pl, 3072) == 0, (gs, pl)
     assert ws(d, 64, 66, 1100, [0, 64], [1024], 3072) == 0          # Hq % Hkv != 0
+
+
+def _cpu_args(B=3, P=4, Hkv=2, G=4, T=2, N=16, cache=0):
+    """A well-shaped argument set on the host: any call with it fails only at
+    the device check, so a perturbed argument must fail earlier, on its shape."""
+    import torch
+    d = fp8kv.desc(N, Hkv, cache)
+    nb = fp8kv.cache_bytes(d)
+    z = lambda *s, dt=torch.int32: torch.zeros(*s, dtype=dt)  # noqa: E731
+    return d, dict(
+        k_cache=z(nb, dt=torch.uint8), v_cache=z(nb, dt=torch.uint8),
+        k_scale=z(Hkv, dt=torch.float32), v_scale=z(Hkv, dt=torch.float32),
+        q=z(B, Hkv * G, 128, dt=torch.bfloat16), q_multi=z(B, T, Hkv * G, 128, dt=torch.bfloat16),
+        page_table=z(B, P), expected_tags=z(B, P), ctx_lens=z(B), pool_tags=z(N),
+        abort=z(B, dt=torch.uint8), k_new=z(B, Hkv, 128, dt=torch.bfloat16),
+        v_new=z(B, Hkv, 128, dt=torch.bfloat16), k_new_q=z(B, T, Hkv, 128, dt=torch.bfloat16),
+        v_new_q=z(B, T, Hkv, 128, dt=torch.bfloat16), new_pos=z(B), token_seq=z(B),
+        out=z(B, Hkv * G, 128, dt=torch.bfloat16), out_q=z(B, T, Hkv * G, 128, dt=torch.bfloat16))
+
+
+def _calls(d, a):
+    """Every hot-path wrapper with the argument set a (keyword names as in a)."""
+    return {
+        "verify_tags": lambda: fp8kv.verify_tags(a["page_table"], a["expected_tags"], a["ctx_lens"],
+                                                 a["pool_tags"], abort=a["abort"]),
+        "append": lambda: fp8kv.append(d, a["k_cache"], a["v_cache"], a["k_scale"], a["v_scale"],
+                                       a["k_new"], a["v_new"], a["token_seq"], a["new_pos"],
+                                       a["page_table"], abort=a["abort"]),
+        "verify_append": lambda: fp8kv.verify_append(
+            d, a["k_cache"], a["v_cache"], a["k_scale"], a["v_scale"], a["k_new"], a["v_new"],
+            a["new_pos"], a["page_table"], a["expected_tags"], a["ctx_lens"], a["pool_tags"],
+            abort=a["abort"]),
+        "verify_append_q": lambda: fp8kv.verify_append_q(
+            d, a["k_cache"], a["v_cache"], a["k_scale"], a["v_scale"], a["k_new_q"], a["v_new_q"],
+            a["new_pos"], a["page_table"], a["expected_tags"], a["ctx_lens"], a["pool_tags"],
+            abort=a["abort"]),
+        "decode_attention": lambda: fp8kv.decode_attention(
+            d, a["k_cache"], a["v_cache"], a["k_scale"], a["v_scale"], a["q"], a["page_table"],
+            a["ctx_lens"], abort=a["abort"], out=a["out"], workspace=a["k_cache"]),
+        "decode_attention_q": lambda: fp8kv.decode_attention_q(
+            d, a["k_cache"], a["v_cache"], a["k_scale"], a["v_scale"], a["q_multi"],
+            a["page_table"], a["ctx_lens"], abort=a["abort"], out=a["out_q"],
+            workspace=a["k_cache"]),
+        "decode_attention_shared": lambda: fp8kv.decode_attention_shared(
+            d, a["k_cache"], a["v_cache"], a["k_scale"], a["v_scale"], a["q"], a["page_table"],
+            a["ctx_lens"], [0, 2], [16], abort=a["abort"], out=a["out"], workspace=a["k_cache"]),
+    }
+
+
+def _expect(fn, *words):
+    try:
+        fn()
+    except ValueError as e:
+        msg = str(e)
+        assert all(w in msg for w in words), (msg, words)
+        return msg
+    raise AssertionError(f"accepted; expected an error naming {words}")
+
+
+def test_wrappers_check_shapes_before_any_device_call():
+    """Each hot-path wrapper rejects arguments whose shape or size would make a
+    kernel read or write outside a buffer, before taking any pointer."""
+    import torch
+    d, good = _cpu_args()
+    for name, fn in _calls(d, good).items():
+        _expect(fn, "device tensor")          # well-shaped: fails only on the device check
+    z = torch.zeros
+    bad = {  # argument -> (replacement, wrappers that must reject it)
+        "page_table": (z(2, 4, dtype=torch.int32), ["verify_tags", "verify_append",
+                                                      "verify_append_q", "decode_attention",
+                                                      "decode_attention_q",
+                                                      "decode_attention_shared"]),
+        "expected_tags": (z(3, 5, dtype=torch.int32), ["verify_tags", "verify_append",
+                                                         "verify_append_q"]),
+        "abort": (z(2, dtype=torch.uint8), list(_calls(d, good))),
+        "pool_tags": (z(15, dtype=torch.int32), ["verify_append", "verify_append_q"]),
+        "k_cache": (z(fp8kv.cache_bytes(d) - 1, dtype=torch.uint8),
+                    ["append", "verify_append", "verify_append_q", "decode_attention",
+                     "decode_attention_q", "decode_attention_shared"]),
+        "v_scale": (z(1, dtype=torch.float32), ["append", "verify_append", "decode_attention"]),
+        "k_new": (z(3, 2, 64, dtype=torch.bfloat16), ["append", "verify_append"]),
+        "v_new_q": (z(3, 3, 2, 128, dtype=torch.bfloat16), ["verify_append_q"]),
+        "new_pos": (z(4, dtype=torch.int32), ["verify_append", "verify_append_q"]),
+        "token_seq": (z(4, dtype=torch.int32), ["append"]),
+        "q": (z(3, 8, 64, dtype=torch.bfloat16), ["decode_attention", "decode_attention_shared"]),
+        "out": (z(3, 8, 128, dtype=torch.float32), ["decode_attention",
+                                                    "decode_attention_shared"]),
+        "out_q": (z(3, 1, 8, 128, dtype=torch.bfloat16), ["decode_attention_q"]),
+        "ctx_lens": (z(2, dtype=torch.int32), ["decode_attention", "decode_attention_q"]),
+    }
+    for arg, (value, names) in bad.items():
+        a = dict(good)
+        a[arg] = value
+        calls = _calls(d, a)
+        for name in names:
+            msg = _expect(calls[name], "")
+            assert "device tensor" not in msg, (arg, name, msg)
+    # out of the wrong dtype for out_dtype (a bf16 buffer asked for f32 rows)
+    _expect(lambda: fp8kv.decode_attention(d, good["k_cache"], good["v_cache"], good["k_scale"],
+                                           good["v_scale"], good["q"], good["page_table"],
+                                           good["ctx_lens"], out=good["out"],
+                                           out_dtype=fp8kv.OUT_F32, workspace=good["k_cache"]),
+            "out", "dtype")
+    # a pool's device tag array must hold every page
+    pool = fp8kv.Pool(16)
+    _expect(lambda: pool.sync(z(15, dtype=torch.int32)), "d_tags", "16")
+    pool.close()

@@ -392,3 +392,57 @@ def test_pool_sync_and_device_check(lib):
     exp = oracle.verify(pt, et, cl, pool.tags())
     assert (_host(ab) == exp).all() and list(exp) == [0, 1, 0, 0]
     pool.close()
+
+
+def test_fused_check_fails_closed(lib, dev):
+    """The fused check + append writes only into pages it checked: a request
+    whose new token lies outside the context it was checked for (the token at
+    a page boundary left out of ctx, a position past ctx, a negative position)
+    aborts and writes nothing; a length near INT32_MAX aborts as the oracle's
+    check does (its page count does not wrap)."""
+    w = workloads.custom("failclosed", [31, 47, 63, 64, 100, 20], Hq=8, Hkv=2, seed=11)
+    st = dev.build(w, num_workers=8)
+    ctx = w.ctx_lens.copy()
+    pos = w.ctx_before.astype(np.int32).copy()
+    ctx[3] = 64            # token 64 opens page 4, which a 64-token context never checks
+    pos[1] = -1
+    ctx[2] = 2 ** 31 - 2
+    pos[4] = ctx[4]        # one past the context
+    st.ctx_lens.copy_(torch.from_numpy(ctx))
+    st.token_pos.copy_(torch.from_numpy(pos))
+    K0, V0 = _host(st.K).copy(), _host(st.V).copy()
+    lib.verify_append(st.desc, st.K, st.V, st.k_scale, st.v_scale, st.k_new, st.v_new,
+                      st.token_pos, st.page_table, st.expected_tags, st.ctx_lens, st.pool_tags,
+                      abort=st.abort)
+    ab = _host(st.abort)
+    check = oracle.verify(w.page_table, w.expected_tags, ctx, w.pool_tags)
+    inside = (pos >= 0) & (pos.astype(np.int64) + 1 <= ctx)
+    assert (ab == (check | ~inside)).all() and ab.tolist() == [0, 1, 1, 1, 1, 0]
+    # the separate check agrees on the lengths alone
+    assert (_host(lib.verify_tags(st.page_table, st.expected_tags, st.ctx_lens,
+                                  st.pool_tags)) == check).all() and check[2] == 1
+    # only requests 0 and 5 wrote their token: every other byte is unchanged
+    K1, V1 = _host(st.K), _host(st.V)
+    written = np.zeros(K0.size, bool)
+    for b in (0, 5):
+        page = int(w.page_table[b, pos[b] // 16])
+        for h in range(w.Hkv):
+            for dim in range(128):
+                for is_v in (0, 1):
+                    written[lib.cache_offset(st.desc, is_v, page, h, int(pos[b]) % 16, dim)] = True
+    assert (K1[~written] == K0[~written]).all() and (V1[~written] == V0[~written]).all()
+    # attention without the tracker never reads past a length the table cannot hold
+    out = _host(lib.decode_attention(st.desc, st.K, st.V, st.k_scale, st.v_scale, st.q,
+                                     st.page_table, st.ctx_lens, out_dtype=lib.OUT_F32,
+                                     num_workers=8))
+    assert (out[2].view(np.uint32) == 0).all()
+    # several new tokens per request: all of them inside the context, or abort
+    B = w.B
+    kq = torch.stack([st.k_new, st.k_new], 1).contiguous()
+    vq = torch.stack([st.v_new, st.v_new], 1).contiguous()
+    first = torch.from_numpy(w.ctx_lens - 2).to(st.token_pos.device)
+    first[0] = int(w.ctx_lens[0]) - 1          # its second token would be at ctx
+    st.ctx_lens.copy_(torch.from_numpy(w.ctx_lens))
+    abq = _host(lib.verify_append_q(st.desc, st.K, st.V, st.k_scale, st.v_scale, kq, vq, first,
+                                    st.page_table, st.expected_tags, st.ctx_lens, st.pool_tags))
+    assert abq.tolist() == [1] + [0] * (B - 1)

@@ -289,3 +289,55 @@ def test_shared_call_prompt_groups(cd):
         with pytest.raises(fp8kv.Fp8kvError) as e:
             _shared_call(fp8kv, w, st, fp8kv.OUT_F32, groups=(gs, pl))
         assert e.value.status == -1
+
+
+@pytest.mark.parametrize("cd", [0, 1])
+def test_shared_call_fails_closed(cd):
+    """The prompt's pages are read through the group's first table, and each
+    member's tag check covers its own table only: a member whose table lists
+    other pages in the prompt range (valid ones, its check passes) gets +0
+    rows; an aborted first member does not stop the others; a stale tag on a
+    shared prompt page aborts exactly the members whose recorded tag it is."""
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    from _helpers import oracle_state
+    w, st = _shared_state(8, 2, cd, B=6)
+    Ko, Vo = oracle_state(w, st.k_scale_host, st.v_scale_host, cd)
+    ref, _ = oracle.attention(Ko, Vo, st.k_scale_host, st.v_scale_host, w.q_bits(), w.page_table,
+                              w.ctx_lens, SM_SCALE, cache_dtype=cd)
+    P0 = w.prefix_len // 16
+    pt, et, tags = w.page_table.copy(), w.expected_tags.copy(), w.pool_tags.copy()
+    # member 3 lists its own first page in place of the prompt's second one
+    pt[3, 1], et[3, 1] = pt[3, P0], et[3, P0]
+    pt_d = torch.from_numpy(pt).cuda()
+    et_d = torch.from_numpy(et.view(np.int32)).cuda()
+    ab = fp8kv.verify_tags(pt_d, et_d, st.ctx_lens, st.pool_tags)
+    assert (ab.cpu().numpy() == 0).all()
+    for nw in (0, 8):
+        out = fp8kv.decode_attention_shared(st.desc, st.K, st.V, st.k_scale, st.v_scale, st.q,
+                                            pt_d, st.ctx_lens, [0, w.B], [w.prefix_len],
+                                            abort=ab, out_dtype=fp8kv.OUT_F32, num_workers=nw)
+        o = out.cpu().numpy()
+        assert (o[3].view(np.uint32) == 0).all()
+        keep = [0, 1, 2, 4, 5]
+        check_outputs(o[keep], None, ref[keep])
+    # the group's first request aborted: the others are exact
+    ab0 = torch.tensor([1, 0, 0, 0, 0, 0], dtype=torch.uint8, device="cuda")
+    o = _shared_call(fp8kv, w, st, fp8kv.OUT_F32, abort=ab0)
+    assert (o[0].view(np.uint32) == 0).all()
+    check_outputs(o[1:], None, ref[1:])
+    # a member recorded a stale tag for a shared prompt page: it alone aborts
+    et2 = w.expected_tags.copy()
+    et2[2, 0] ^= 0x10
+    ab2 = fp8kv.verify_tags(st.page_table, torch.from_numpy(et2.view(np.int32)).cuda(),
+                            st.ctx_lens, st.pool_tags)
+    assert ab2.cpu().numpy().tolist() == [0, 0, 1, 0, 0, 0]
+    o = _shared_call(fp8kv, w, st, fp8kv.OUT_F32, abort=ab2)
+    assert (o[2].view(np.uint32) == 0).all()
+    check_outputs(o[[0, 1, 3, 4, 5]], None, ref[[0, 1, 3, 4, 5]])
+    # the shared page itself was handed out again: every member aborts
+    tags[pt[0, 1]] += np.uint32(1)
+    ab3 = fp8kv.verify_tags(st.page_table, st.expected_tags, st.ctx_lens,
+                            torch.from_numpy(tags.view(np.int32)).cuda())
+    assert (ab3.cpu().numpy() == 1).all()
+    o = _shared_call(fp8kv, w, st, fp8kv.OUT_F32, abort=ab3)
+    assert (o.view(np.uint32) == 0).all()
