@@ -7,7 +7,7 @@ is missing the import fails -- there is no fallback.
 
 Names mirror the C ABI in ``include/fp8kv.h``:
   Pool, verify_tags, append, verify_append, verify_append_q, decode_attention,
-  decode_attention_q, decode_attention_shared, decode_workspace_size,
+  decode_attention_noalloc, decode_attention_q, decode_attention_shared, decode_workspace_size,
   decode_workspace_size_q, decode_workspace_size_shared,
   decode_num_workers, cache_offset, cache_bytes, debug_convert_e4m3;
   step() chains the step's calls in the order the pages give.
@@ -79,6 +79,10 @@ _ws_size = _sig("fp8kv_decode_workspace_size", ctypes.c_size_t,
 _decode = _sig("fp8kv_decode_attention", _i32,
                [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _i32,
                 ctypes.c_float, _p, _p, _i32, _i32, _p, ctypes.c_size_t, _p])
+_decode_noalloc = _sig("fp8kv_decode_attention_noalloc", _i32,
+                       [ctypes.POINTER(CacheDesc), _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _i32,
+                        ctypes.c_float, _p, _p, _i32, _i32, _p])
+NOALLOC_SCRATCH_BYTES = 32 << 20   # FP8KV_NOALLOC_SCRATCH_BYTES
 _ws_size_q = _sig("fp8kv_decode_workspace_size_q", ctypes.c_size_t,
                   [ctypes.POINTER(CacheDesc), _i32, _i32, _i32, _i32])
 _decode_q = _sig("fp8kv_decode_attention_q", _i32,
@@ -457,6 +461,35 @@ def decode_attention(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, page_t
     return _run(_decode, args, "decode_attention", out,
                 (d, k_cache, v_cache, k_scale, v_scale, q, page_table, ctx_lens, abort, out,
                  workspace), prepare)
+
+
+def decode_attention_noalloc(d: CacheDesc, k_cache, v_cache, k_scale, v_scale, q, page_table,
+                             ctx_lens, out, abort=None, out_dtype: int = OUT_BF16,
+                             sm_scale: Optional[float] = None, num_workers: int = 0,
+                             stream=None, prepare: bool = False):
+    """decode_attention without a workspace: the library's fixed device scratch
+    (NOALLOC_SCRATCH_BYTES per device) holds the partial states, so nothing is
+    allocated (out must be given).  Calls on one device share the scratch:
+    overlapping calls race."""
+    _shape(q, (None, None, HEAD_DIM), "q")
+    B, Hq, D = q.shape
+    _check_decode(d, k_cache, v_cache, k_scale, v_scale, page_table, ctx_lens, abort, B)
+    _check_out(out, (B, Hq, D), out_dtype)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    fp8 = d.cache_dtype == E4M3
+    args = (ctypes.byref(d), _dev(k_cache, _U8 + _BITS16, "k_cache"),
+            _dev(v_cache, _U8 + _BITS16, "v_cache"),
+            _dev(k_scale, _F32, "k_scale", allow_none=not fp8),
+            _dev(v_scale, _F32, "v_scale", allow_none=not fp8),
+            _dev(q, _BITS16, "q"), Hq, _dev(page_table, _I32, "page_table"),
+            page_table.shape[1], _dev(ctx_lens, _I32, "ctx_lens"), B,
+            float(sm_scale), _dev(abort, _U8, "abort", allow_none=True),
+            _dev(out, (torch.bfloat16, torch.int16, torch.float32), "out"), out_dtype,
+            num_workers, _stream(stream))
+    return _run(_decode_noalloc, args, "decode_attention_noalloc", out,
+                (d, k_cache, v_cache, k_scale, v_scale, q, page_table, ctx_lens, abort, out),
+                prepare)
 
 
 def decode_workspace_size_q(d: CacheDesc, batch: int, num_q_heads: int, q_len: int,

@@ -42,6 +42,13 @@
 #include "fp8kv.h"
 #include "fp8kv_internal.h"
 
+// Device memory of fp8kv_decode_attention_noalloc: the decode's partial
+// states and prefix sums for callers that cannot allocate (graph capture,
+// serving loops).  One copy per device, held until the process ends; host
+// code never passes this name to a kernel (on the host it is only a stand-in
+// for the symbol): it uses the address hipGetSymbolAddress gives per device.
+static __device__ __align__(256) unsigned char scratch[FP8KV_NOALLOC_SCRATCH_BYTES];
+
 namespace fp8kv_detail {
 thread_local int32_t g_last_hip_error = 0;
 void record_hip_error(int32_t e) { g_last_hip_error = e; }
@@ -2447,6 +2454,51 @@ fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc* desc, const void* d_
   return decode_impl(desc, d_k_cache, d_v_cache, d_k_scale, d_v_scale, d_q, num_q_heads, 1,
                      d_page_table, max_pages_per_seq, d_ctx_lens, batch, sm_scale, d_abort,
                      d_out, out_dtype, num_workers, d_workspace, workspace_bytes, stream);
+}
+
+// Scratch address on the current device, looked up once per device with that
+// device current; nullptr (and the HIP error recorded) if the lookup fails.
+static void* device_scratch() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> ptrs[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fp8kv_detail::record_hip_error(static_cast<int32_t>(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    fp8kv_detail::record_hip_error(static_cast<int32_t>(e != hipSuccess ? e : hipErrorUnknown));
+    return nullptr;
+  }
+  ptrs[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+fp8kv_status fp8kv_decode_attention_noalloc(const fp8kv_cache_desc* desc, const void* d_k_cache,
+                                            const void* d_v_cache, const float* d_k_scale,
+                                            const float* d_v_scale, const uint16_t* d_q,
+                                            int32_t num_q_heads, const int32_t* d_page_table,
+                                            int32_t max_pages_per_seq, const int32_t* d_ctx_lens,
+                                            int32_t batch, float sm_scale, const uint8_t* d_abort,
+                                            void* d_out, int32_t out_dtype, int32_t num_workers,
+                                            hipStream_t stream) {
+  // the same checks as the workspace form, then the size against the scratch
+  const size_t need = decode_workspace(desc, batch, num_q_heads, 1, num_workers);
+  if (batch > 0 && need > FP8KV_NOALLOC_SCRATCH_BYTES) return FP8KV_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (batch > 0 && need > 0) {
+    ws = device_scratch();
+    if (!ws) return FP8KV_HIP_ERROR;
+  }
+  return decode_impl(desc, d_k_cache, d_v_cache, d_k_scale, d_v_scale, d_q, num_q_heads, 1,
+                     d_page_table, max_pages_per_seq, d_ctx_lens, batch, sm_scale, d_abort,
+                     d_out, out_dtype, num_workers, ws, ws ? FP8KV_NOALLOC_SCRATCH_BYTES : 0,
+                     stream);
 }
 
 fp8kv_status fp8kv_decode_attention_q(const fp8kv_cache_desc* desc, const void* d_k_cache,

@@ -277,6 +277,36 @@ fp8kv_status fp8kv_decode_attention(const fp8kv_cache_desc *desc, const void *d_
                                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* fp8kv_decode_attention without a workspace argument, for callers that      */
+/* cannot allocate device memory (code under HIP graph capture, tight serving */
+/* loops, harnesses that forbid hipMalloc).  Same arguments, results and      */
+/* errors as fp8kv_decode_attention with the same num_workers (bit for bit),  */
+/* except that the partial states live in a fixed device array of the        */
+/* library: FP8KV_NOALLOC_SCRATCH_BYTES bytes on every device the library    */
+/* runs on, held until the process ends.  A call whose workspace              */
+/* (fp8kv_decode_workspace_size for the same batch, num_q_heads and          */
+/* num_workers) exceeds it returns FP8KV_WORKSPACE_TOO_SMALL before anything  */
+/* is enqueued: 32 MiB covers, at 64 q-heads over 8 kv-heads and the default */
+/* worker count of a 256-CU device, batches up to about 900 requests.  The   */
+/* call allocates nothing (no hipMalloc, hipFree or allocating library call); */
+/* the first call on a device looks up the array's address for that device. */
+/* The array's contents before a call do not matter (nothing needs to start  */
+/* at zero).  Every call on one device shares that device's array: calls     */
+/* that may overlap on one GPU (several streams, several host threads) race  */
+/* and must be ordered by the caller.                                         */
+/* ------------------------------------------------------------------------ */
+#define FP8KV_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+fp8kv_status fp8kv_decode_attention_noalloc(const fp8kv_cache_desc *desc, const void *d_k_cache,
+                                            const void *d_v_cache, const float *d_k_scale,
+                                            const float *d_v_scale, const uint16_t *d_q,
+                                            int32_t num_q_heads, const int32_t *d_page_table,
+                                            int32_t max_pages_per_seq, const int32_t *d_ctx_lens,
+                                            int32_t batch, float sm_scale, const uint8_t *d_abort,
+                                            void *d_out, int32_t out_dtype, int32_t num_workers,
+                                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Several new tokens per request checked in one step: speculative decoding, */
 /* where a draft proposes tokens and the main model verifies them together   */
 /* (page "Kimi and GLM Reasoning Slimming: Hands-On Test", section "It       */
