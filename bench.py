@@ -196,6 +196,10 @@ def loop_study(args):
                 lat[m].append(x)
         d = np.array([(a - b) / b for a, b in zip(tot["on"], tot["off"])])
         boots = [rng.choice(d, d.size).mean() for _ in range(2000)]
+        # p95 step latency per round, on against off in the same round pair
+        d95 = np.array([np.percentile(a, 95) / np.percentile(b, 95) - 1
+                        for a, b in zip(lat["on"], lat["off"])])
+        boots95 = [rng.choice(d95, d95.size).mean() for _ in range(2000)]
         res = {}
         for m in ("on", "off"):
             allx = np.concatenate(lat[m])
@@ -207,8 +211,9 @@ def loop_study(args):
                                         round(100 * float(np.percentile(boots, 97.5)), 3)]}
         res["overhead_us_per_step"] = round(
             1e6 * (float(np.median(tot["on"])) - float(np.median(tot["off"]))) / args.loop_steps, 2)
-        res["p95_overhead_pct"] = round(
-            100 * (res["on"]["step_ms_p95"] / res["off"]["step_ms_p95"] - 1), 3)
+        res["p95_overhead_pct"] = {"mean": round(100 * float(d95.mean()), 3),
+                                   "ci95": [round(100 * float(np.percentile(boots95, 2.5)), 3),
+                                            round(100 * float(np.percentile(boots95, 97.5)), 3)]}
         per.setdefault(launch, {}).setdefault(f"{nl}_layers", {})[str(c)] = res
         for lp in loops.values():
             lp.close()
@@ -569,6 +574,9 @@ def main():
                     choices=["tiny", "uniform", "ragged", "long", "capacity"],
                     help="which synthetic workload (the headline is 'ragged')")
     ap.add_argument("--cache", default="e4m3", choices=["e4m3", "bf16"])
+    ap.add_argument("--q-heads", type=int, default=0,
+                    help="query heads per request instead of the workload's own (same kv-heads): "
+                         "the GQA group size G = q-heads / kv-heads, e.g. 8 for G = 1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip bf16 variant and tag overhead")
     ap.add_argument("--overhead-rounds", type=int, default=20)
@@ -646,6 +654,11 @@ def main():
     cfg = {"tiny": 1, "uniform": 2, "ragged": 3, "long": 4, "capacity": 5}[args.workload]
     cache = 0 if args.cache == "e4m3" else 1
     w = workloads.make(cfg)
+    if args.q_heads:
+        if args.q_heads % w.Hkv:
+            sys.exit(f"--q-heads {args.q_heads} is not a multiple of {w.Hkv} kv-heads")
+        w.Hq = args.q_heads
+        w.name = f"{w.name}_{w.Hq}q{w.Hkv}kv"
     R = args.rotate if args.rotate > 0 else (2 if cfg == 2 else 1)
     log(f"bench: building workload {w.name} ({w.B} requests, {args.cache} cache, {R} cop"
         f"{'y' if R == 1 else 'ies'})")
@@ -719,10 +732,14 @@ def main():
     }
     if not args.no_extras and cfg == 3:
         log("bench: tag-check overhead (interleaved on/off)")
+        # both forms run prepared launches (one C call per kernel, no per-call
+        # argument checks); enough steps per round that the host's latency
+        # before a round's first kernel is amortised
         step = lambda: st.step(check_tags=True)  # noqa: E731
         off = lambda: st.step(check_tags=False)  # noqa: E731
+        warm_up([step, off])
         deltas = []
-        M = 10
+        M = 50
         for r in range(args.overhead_rounds):
             a = time_steps(step, M)
             b = time_steps(off, M)

@@ -46,8 +46,8 @@ class DeviceStep:
     workspace: Optional[torch.Tensor]
     out: torch.Tensor
     # the default step's launches, prepared once per stream (a serving loop's
-    # way: no per-call argument checks on the host)
-    _prepared: Optional[tuple] = dataclasses.field(default=None, repr=False)
+    # way: no per-call argument checks on the host), with and without the tracker
+    _prepared: Optional[dict] = dataclasses.field(default=None, repr=False)
 
     @property
     def cache_dtype(self) -> int:
@@ -79,28 +79,45 @@ class DeviceStep:
             out_dtype=out_dtype, num_workers=nw,
             workspace=self.workspace if nw == self.num_workers else None, stream=stream)
 
+    def _prepare(self, check_tags: bool):
+        """The default step's launches (fused check + append and attention with
+        the tracker; append and attention without it), checked and marshalled
+        once per stream and set of tensors: both forms then run the same launch
+        path, one C call per kernel launch."""
+        h = (check_tags, torch.cuda.current_stream().cuda_stream, self.num_workers,
+             *map(id, (self.K, self.V, self.k_scale, self.v_scale, self.k_new, self.v_new,
+                       self.token_seq, self.token_pos, self.page_table, self.expected_tags,
+                       self.ctx_lens, self.pool_tags, self.abort, self.q, self.out,
+                       self.workspace)))
+        cache = self._prepared if self._prepared is not None else {}
+        self._prepared = cache
+        if cache.get(check_tags, (None,))[0] != h:
+            if check_tags:
+                first = fp8kv.verify_append(self.desc, self.K, self.V, self.k_scale, self.v_scale,
+                                            self.k_new, self.v_new, self.token_pos,
+                                            self.page_table, self.expected_tags, self.ctx_lens,
+                                            self.pool_tags, abort=self.abort, prepare=True)
+            else:
+                first = fp8kv.append(self.desc, self.K, self.V, self.k_scale, self.v_scale,
+                                     self.k_new, self.v_new, self.token_seq, self.token_pos,
+                                     self.page_table, prepare=True)
+            dec = fp8kv.decode_attention(
+                self.desc, self.K, self.V, self.k_scale, self.v_scale, self.q, self.page_table,
+                self.ctx_lens, abort=self.abort if check_tags else None, out=self.out,
+                out_dtype=fp8kv.OUT_BF16, num_workers=self.num_workers, workspace=self.workspace,
+                prepare=True)
+            cache[check_tags] = (h, first, dec)
+        return cache[check_tags]
+
     def step(self, check_tags=True, out_dtype=fp8kv.OUT_BF16, stream=None, fused=True):
         """One decode step: tag check + append (one launch when fused), then
         attention.  check_tags=False is the no-op tracker path.  The default
-        form (fused, bf16 rows, current stream) runs prepared launches."""
-        if check_tags and fused and out_dtype == fp8kv.OUT_BF16 and stream is None:
-            # prepared again when the stream or any tensor the launches hold changes
-            h = (torch.cuda.current_stream().cuda_stream, self.num_workers,
-                 *map(id, (self.K, self.V, self.k_scale, self.v_scale, self.k_new, self.v_new,
-                           self.token_pos, self.page_table, self.expected_tags, self.ctx_lens,
-                           self.pool_tags, self.abort, self.q, self.out, self.workspace)))
-            if self._prepared is None or self._prepared[0] != h:
-                va = fp8kv.verify_append(self.desc, self.K, self.V, self.k_scale, self.v_scale,
-                                         self.k_new, self.v_new, self.token_pos, self.page_table,
-                                         self.expected_tags, self.ctx_lens, self.pool_tags,
-                                         abort=self.abort, prepare=True)
-                dec = fp8kv.decode_attention(
-                    self.desc, self.K, self.V, self.k_scale, self.v_scale, self.q, self.page_table,
-                    self.ctx_lens, abort=self.abort, out=self.out, out_dtype=fp8kv.OUT_BF16,
-                    num_workers=self.num_workers, workspace=self.workspace, prepare=True)
-                self._prepared = (h, va, dec)
-            self._prepared[1]()
-            return self._prepared[2]()
+        form (fused, bf16 rows, current stream) runs prepared launches, with
+        the tracker and without it alike."""
+        if fused and out_dtype == fp8kv.OUT_BF16 and stream is None:
+            _, first, dec = self._prepare(check_tags)
+            first()
+            return dec()
         if check_tags and fused:
             self.verify_append(stream)
         else:
