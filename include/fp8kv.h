@@ -173,6 +173,10 @@ fp8kv_status fp8kv_verify_tags(const int32_t *d_page_table, const uint32_t *d_ex
 
 /* ------------------------------------------------------------------------ */
 /* Quantize-on-append: write new tokens' K and V into their cache pages.     */
+/* (Cloudflare, "Smaller, faster, safer: running Kimi and GLM at scale",     */
+/* KV-cache section: the cache holds keys and values as FP8 e4m3 instead of  */
+/* BF16; integrity section: a request whose mapping failed the check must not */
+/* touch the cache, so its writes are skipped too.)                          */
 /* Token t of num_tokens belongs to request d_token_seq[t] (a row of the     */
 /* page table, < num_seqs) at position p = d_token_pos[t]; it goes to page   */
 /* d_page_table[seq][p / 16], slot p % 16.  For e4m3 every element is        */
@@ -237,7 +241,14 @@ fp8kv_status fp8kv_verify_append_q(const fp8kv_cache_desc *desc, void *d_k_cache
 
 /* ------------------------------------------------------------------------ */
 /* Paged decode attention (one query token per request) over the cache,      */
-/* converting e4m3 on read.  For request b and q-head h (kv-head g = h/G):  */
+/* converting e4m3 on read (Cloudflare, "Smaller, faster, safer: running Kimi */
+/* and GLM at scale", KV-cache section: the attention kernel turns the stored */
+/* FP8 values back into wider numbers as it loads them; integrity section: a  */
+/* request flagged by the check reads nothing and produces no output; the    */
+/* check is a separate pass and a deployment without it runs a no-op tracker, */
+/* here a NULL d_abort).  The formula itself is not on the pages: it is      */
+/* textbook single-query scaled dot-product attention with grouped kv-heads. */
+/* For request b and q-head h (kv-head g = h/G):                             */
 /*   s_j = sm_scale * k_scale[g] * sum_d q[b][h][d] * DEC(K[j][g][d]),        */
 /*   o   = v_scale[g] * sum_j e^{s_j - max s} DEC(V[j][g]) / sum_j e^{s_j-max s}*/
 /* over the d_ctx_lens[b] tokens j of the request (token j at page           */

@@ -1,9 +1,12 @@
 """Pins for the oracle's page-tag check (CPU only).
 
-The check is pinned by (a) hand cases written from the pseudocode in the
+The check is pinned by (a) hand cases written from the rule of the
 commentary page's section "Giving Every Physical Cache Page a 'Generation
-Number'" (tests/golden/verify_cases.txt) and (b) a literal transcription of
-that pseudocode, run on random cases with stale entries planted.
+Number'" (tests/golden/verify_cases.txt) and (b) the same rule restated as a
+set comparison, run on random cases with stale entries planted.  The rule: a
+request may go on only if every page it expects to read still carries the
+tag the request recorded for it; any other case (a changed tag, a page id
+the allocator does not know) aborts the request.
 """
 import os
 
@@ -53,18 +56,15 @@ def test_golden_hand_cases():
             assert got[b] == exp, name
 
 
-def literal_pseudocode(request_pages, current_tag):
-    """for page in request.expected_cache_pages:
-           if cache_allocator.tag(page.id) != page.expected_tag: abort
-    (an id the allocator does not know is a mismatch)."""
-    for page_id, expected in request_pages:
-        tag = current_tag(page_id)
-        if tag is None or tag != expected:
-            return 1
-    return 0
+def restated_rule(request_pages, current_tags: dict) -> int:
+    """1 if the request must abort: the (page id, recorded tag) pairs it expects
+    are not all among the allocator's (page id, current tag) pairs."""
+    expected = set(request_pages)
+    known = {(pid, current_tags[pid]) for pid, _ in expected if pid in current_tags}
+    return 0 if expected <= known else 1
 
 
-def test_matches_literal_pseudocode_random():
+def test_matches_restated_rule_random():
     rng = np.random.default_rng(3)
     for trial in range(40):
         N = int(rng.integers(1, 300))
@@ -78,13 +78,11 @@ def test_matches_literal_pseudocode_random():
         cl = rng.integers(0, P * 16 + 1, B).astype(np.int32)
         got = oracle.verify(pt, et, cl, tags)
 
-        def current_tag(pid):
-            return int(tags[pid]) if 0 <= pid < N else None
-
+        current = {i: int(tags[i]) for i in range(N)}
         for b in range(B):
             n = (int(cl[b]) + 15) // 16
             pages = [(int(pt[b, i]), int(et[b, i])) for i in range(n)]
-            assert got[b] == literal_pseudocode(pages, current_tag), (trial, b)
+            assert got[b] == restated_rule(pages, current), (trial, b)
 
 
 def test_workload_stale_entries_abort_exactly():
