@@ -975,7 +975,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg_id, int 
           // on the 16x16x32 MFMA whose k index 8 qd + j holds token
           // 4 qd + (j % 4) of page j / 4 (the lane's own V and P of both pages)
           float sv[2][NT][4];
-          u32x4_t vmask[2];
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
             const int i = i0 + s;
@@ -1002,22 +1001,26 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg_id, int 
             for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
               for (int r = 0; r < 4; ++r) sv[s][ct][r] = st[ct][r];
-            vmask[s] = u32x4_t{~0u, ~0u, ~0u, ~0u};
             if (left - (a.qlen - 1) < kPage) {
 #pragma unroll
               for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                   if (4 * qd + r >= left - lag[ct]) sv[s][ct][r] = -INFINITY;
+              // tokens past the end may hold any bytes: clear their V (in the
+              // ring, on this page only) so 0*x stays 0
               const int keep = min(max(valid - 4 * qd, 0), 4);
+              u32x4_t vmask;
               if constexpr (CACHE == FP8KV_E4M3) {
                 const unsigned m = keep >= 4 ? ~0u : ((1u << (8 * keep)) - 1u);
-                vmask[s] = u32x4_t{m, m, m, m};
+                vmask = u32x4_t{m, m, m, m};
               } else {
                 const unsigned m0 = keep >= 2 ? ~0u : (keep == 1 ? 0xFFFFu : 0u);
                 const unsigned m1 = keep >= 4 ? ~0u : (keep == 3 ? 0xFFFFu : 0u);
-                vmask[s] = u32x4_t{m0, m1, m0, m1};
+                vmask = u32x4_t{m0, m1, m0, m1};
               }
+#pragma unroll
+              for (int c = 0; c < NC; ++c) vr[s][c] &= vmask;
             }
           }
           float p[NT][8];
@@ -1052,8 +1055,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg_id, int 
               }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-              const f16x4_t va = e4m3x4_to_f16(vr[0][t >> 2][t & 3] & vmask[0][t & 3]);
-              const f16x4_t vb = e4m3x4_to_f16(vr[1][t >> 2][t & 3] & vmask[1][t & 3]);
+              const f16x4_t va = e4m3x4_to_f16(vr[0][t >> 2][t & 3]);
+              const f16x4_t vb = e4m3x4_to_f16(vr[1][t >> 2][t & 3]);
               const f16x8_t vfrag = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
 #pragma unroll
               for (int ct = 0; ct < NT; ++ct) {
@@ -1074,10 +1077,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg_id, int 
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
               const u32x4_t wa = vr[0][t >> 1], wb = vr[1][t >> 1];
-              const u32x4_t w = (t & 1) ? u32x4_t{wa.z & vmask[0].x, wa.w & vmask[0].y,
-                                                  wb.z & vmask[1].x, wb.w & vmask[1].y}
-                                        : u32x4_t{wa.x & vmask[0].x, wa.y & vmask[0].y,
-                                                  wb.x & vmask[1].x, wb.y & vmask[1].y};
+              const u32x4_t w = (t & 1) ? u32x4_t{wa.z, wa.w, wb.z, wb.w}
+                                        : u32x4_t{wa.x, wa.y, wb.x, wb.y};
               const bf16x8_t vfrag = __builtin_bit_cast(bf16x8_t, w);
 #pragma unroll
               for (int ct = 0; ct < NT; ++ct) {
@@ -1125,15 +1126,16 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg_id, int 
           for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
             for (int r = 0; r < 4; ++r) sv[ct][r] = st[ct][r];
-          u32x4_t vmask = {~0u, ~0u, ~0u, ~0u};
           if (left - (a.qlen - 1) < kPage) {  // some column stops inside this page
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
               for (int r = 0; r < 4; ++r)
                 if (4 * qd + r >= left - lag[ct]) sv[ct][r] = -INFINITY;
-            // tokens past the end may hold any bytes: clear their V so 0*x stays 0
+            // tokens past the end may hold any bytes: clear their V (in the
+            // ring, on this page only) so 0*x stays 0
             const int keep = min(max(valid - 4 * qd, 0), 4);  // tokens 4qd+j, j<keep
+            u32x4_t vmask;
             if constexpr (CACHE == FP8KV_E4M3) {
               const unsigned m = keep >= 4 ? ~0u : ((1u << (8 * keep)) - 1u);
               vmask = u32x4_t{m, m, m, m};
@@ -1142,6 +1144,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg_id, int 
               const unsigned m1 = keep >= 4 ? ~0u : (keep == 3 ? 0xFFFFu : 0u);
               vmask = u32x4_t{m0, m1, m0, m1};
             }
+#pragma unroll
+            for (int c = 0; c < NC; ++c) vr[s][c] &= vmask;
           }
           float p[NT][4];
 #pragma unroll
@@ -1178,7 +1182,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg_id, int 
               }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-              const unsigned w = vr[s][t >> 2][t & 3] & vmask[t & 3];
+              const unsigned w = vr[s][t >> 2][t & 3];
               const f16x4_t vfrag = e4m3x4_to_f16(w);
 #pragma unroll
               for (int ct = 0; ct < NT; ++ct) {
@@ -1200,8 +1204,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg_id, int 
             for (int t = 0; t < 8; ++t) {
               const u32x4_t w = vr[s][t >> 1];
               u32x2_t pair;
-              pair.x = ((t & 1) ? w.z : w.x) & vmask.x;
-              pair.y = ((t & 1) ? w.w : w.y) & vmask.y;
+              pair.x = (t & 1) ? w.z : w.x;
+              pair.y = (t & 1) ? w.w : w.y;
               const s16x4_t vfrag = __builtin_bit_cast(s16x4_t, pair);
 #pragma unroll
               for (int ct = 0; ct < NT; ++ct) {
