@@ -86,6 +86,8 @@ def test_loop_matches_oracle(fp8kv):
     out = loop.out.cpu().numpy()
     err = check_outputs(out, None, ref)
     print(f"loop B={B} P={P} T={T}: max abs err {err:.3e}")
+    # the tags that went up with the tables are the pool's
+    assert np.array_equal(loop.tags.cpu().numpy().view(np.uint32), loop.pool.tags())
     loop.close()
 
 
@@ -124,6 +126,35 @@ def test_stale_tag_aborts_only_that_request(fp8kv):
     out = loop.out.cpu().numpy()
     assert (out[1] == 0).all()
     check_outputs(out[[0, 2]], None, ref[[0, 2]])
+    loop.close()
+
+
+def test_page_reclaimed_through_the_pool_aborts_its_holder(fp8kv):
+    """The pool gives one of request 0's prompt pages to another holder (its
+    tag changes); the new tag reaches the device with the tables and the next
+    step aborts request 0 only; the page stays with its new holder."""
+    loop = _loop(fp8kv, tracker=True)
+    loop.run(4)
+    pid = loop.pages[0][1]
+    old_tag = loop.pool.tag(pid)
+    loop.reclaim(0, 1)
+    assert loop.pool.tag(pid) != old_tag and loop.pool.refcount(pid) == 1
+    assert np.array_equal(loop.tags.cpu().numpy().view(np.uint32), loop.pool.tags())
+    loop.step()
+    assert list(loop.abort.cpu().numpy()) == [1, 0, 0]
+    assert loop.live == [False, True, True] and loop.pool.refcount(pid) == 1
+    assert (loop.out[0] == 0).all()
+    loop.run(T - 5)
+    live = [False, True, True]
+    K, V, ks, vs, pt = _oracle_run(loop, T, live)
+    _check_cache(loop, K, V, live)
+    q = np.stack([token_bits(SEED, "q", b, T - 1, T, HQ)[0] for b in range(B)])
+    cl = np.array([0, P + T, P + T], np.int32)
+    ref, _ = oracle.attention(K, V, ks, vs, q, pt, cl, SM_SCALE,
+                              abort=np.array([1, 0, 0], np.uint8))
+    out = loop.out.cpu().numpy()
+    assert (out[0] == 0).all()
+    check_outputs(out[[1, 2]], None, ref[[1, 2]])
     loop.close()
 
 

@@ -12,13 +12,14 @@ A model step runs `layers` layers; every layer has its own K/V pool addressed
 by the same page table (page ids and their tags are per page, for all layers),
 so the tag check runs once per step while append and attention run per layer.
 
-tracker=True : after a page allocation the pool's tags are uploaded
-               (pool_sync); the batched tag check runs before the first layer's
-               append (fused check + append), later layers' appends and every
-               attention honour the abort flags, and aborted requests are
-               retired (their pages freed).
-tracker=False: the no-op tracker: the same page allocation, plain appends and
-               attention without abort flags.
+tracker=True : after a page allocation the new pages' tags go to the device
+               with the page table, in one copy (the loop mirrors the pool's
+               tags from what the pool's alloc returns); the batched tag check
+               runs before the first layer's append (fused check + append),
+               later layers' appends and every attention honour the abort
+               flags, and aborted requests are retired (their pages freed).
+tracker=False: the no-op tracker: the same page allocation and page-table
+               upload, plain appends and attention without abort flags.
 
 Both modes copy B bytes back to the host after each step (the abort flags,
 which stay zero without the tracker), standing in for the per-step read-back
@@ -82,7 +83,6 @@ class DecodeLoop:
         self.pool = fp8kv.Pool(self.num_pages, seed=seed)
         ids, _ = self.pool.alloc(self.num_pages)
         self.pool.free(np.random.default_rng(seed).permutation(ids))
-        self.tags = torch.zeros(self.num_pages, dtype=torch.int32, device=device)
 
         # per-step inputs, generated on the device before any step runs
         S = gen_len if step_sets is None else min(step_sets, gen_len)
@@ -118,16 +118,36 @@ class DecodeLoop:
         self.Vs = [pool_bytes() for _ in range(layers)]
         self.K, self.V = self.Ks[0], self.Vs[0]
 
-        # page table and expected tags side by side, so one upload carries both:
-        # a pinned host mirror and its device copy
-        self.tables_host = torch.zeros((2, batch, self.max_pages), dtype=torch.int32).pin_memory()
-        self.tables_host[0] = -1
-        self.pt_host, self.et_host = self.tables_host[0], self.tables_host[1]
-        self.tables = torch.empty_like(self.tables_host, device=device)
-        self.page_table, self.expected = self.tables[0], self.tables[1]
+        # page table, expected tags and the pool's tags in one buffer, so that
+        # one upload carries all three after an allocation (a second copy for
+        # the tags, as fp8kv_pool_sync makes, would put one more transfer
+        # ahead of that step's kernels): a pinned host mirror and its device
+        # copy, each region starting on a 256-byte boundary
+        def up(n):
+            return -(-n // 64) * 64
+        n_tab = batch * self.max_pages
+        o_et, o_tags = up(n_tab), 2 * up(n_tab)
+        self.meta_host = torch.zeros(o_tags + up(self.num_pages), dtype=torch.int32).pin_memory()
+        self.meta = torch.empty_like(self.meta_host, device=device)
+
+        def regions(t):
+            return (t[:n_tab].view(batch, self.max_pages),
+                    t[o_et:o_et + n_tab].view(batch, self.max_pages),
+                    t[o_tags:o_tags + self.num_pages])
+        self.pt_host, self.et_host, self.tags_host = regions(self.meta_host)
+        self.page_table, self.expected, self.tags = regions(self.meta)
+        self.pt_host.fill_(-1)
+        # numpy views of the host regions for the per-step writes (a torch
+        # index assignment costs microseconds of host time)
+        self._pt_np, self._et_np, self._tags_np = (x.numpy() for x in regions(self.meta_host))
+        self._meta_bytes = {True: self.meta, False: self.meta[:n_tab]}
+        self._meta_src = {True: self.meta_host, False: self.meta_host[:n_tab]}
         self.lens = torch.empty((2, batch), dtype=torch.int32, device=device)  # new_pos; ctx_lens
         self.abort = torch.zeros(batch, dtype=torch.uint8, device=device)
         self.abort_host = torch.zeros(batch, dtype=torch.uint8).pin_memory()
+        # the flags as bytes, compared with the flags of the requests already
+        # retired (a byte compare; numpy's any() costs microseconds per step)
+        self._flag_bytes = memoryview(self.abort_host.numpy())
         self.out = torch.empty((batch, num_q_heads, D_HEAD), device=device,
                                dtype=torch.bfloat16 if out_dtype == fp8kv.OUT_BF16 else torch.float32)
         self.token_seq = torch.arange(batch, dtype=torch.int32, device=device)
@@ -144,9 +164,27 @@ class DecodeLoop:
     def _take_pages(self, b: int, n: int):
         ids, tags = self.pool.alloc(n)
         k = len(self.pages[b])
-        self.pt_host[b, k:k + n] = torch.from_numpy(ids)
-        self.et_host[b, k:k + n] = torch.from_numpy(tags.view(np.int32))
-        self.pages[b].extend(int(i) for i in ids)
+        self._pt_np[b, k:k + n] = ids
+        if self.tracker:       # the request remembers the tags; the pool's go up too
+            self._et_np[b, k:k + n] = tags.view(np.int32)
+            self._tags_np[ids] = tags.view(np.int32)
+        self.pages[b].extend(ids.tolist())
+
+    def _grow(self):
+        """One new page for each live request, in one pool call and a few
+        vectorized writes (the host work of an allocation step)."""
+        rows = self._live_rows
+        if rows.size == 0:
+            return
+        ids, tags = self.pool.alloc(rows.size)
+        cols = np.array([len(self.pages[b]) for b in rows.tolist()])
+        self._pt_np[rows, cols] = ids
+        if self.tracker:
+            t = tags.view(np.int32)
+            self._et_np[rows, cols] = t
+            self._tags_np[ids] = t
+        for b, i in zip(rows.tolist(), ids.tolist()):
+            self.pages[b].append(i)
 
     def _fill_prompt(self):
         n = -(-self.P // PAGE)
@@ -168,20 +206,23 @@ class DecodeLoop:
     def reset(self):
         """Back to the state right after the prompt: generated pages returned.
         Not after an abort (a retired request's prompt pages are gone)."""
-        if not all(getattr(self, "live", [True])):
-            raise RuntimeError("reset after an abort: build a new loop")
+        if not all(getattr(self, "live", [True])) or getattr(self, "reclaimed", None):
+            raise RuntimeError("reset after an abort or a reclaimed page: build a new loop")
         for b in range(self.B):
             extra = self.pages[b][len(self.prompt_pages[b]):]
             if extra:
                 self.pool.free(extra)
             self.pages[b] = list(self.prompt_pages[b])
             self.pt_host[b, len(self.pages[b]):] = -1
-        self.tables.copy_(self.tables_host)
-        self.pool.sync(self.tags)
+        self.tags_host.copy_(torch.from_numpy(self.pool.tags().view(np.int32)))
+        self.meta.copy_(self.meta_host)
         self.lens[0].fill_(self.P)
         self.lens[1].fill_(self.P + 1)
         self.abort.zero_()
         self.live = [True] * self.B
+        self._live_rows = np.arange(self.B)
+        self._retired_flags = bytes(self.B)
+        self.reclaimed = set()
         self.step_index = 0
         torch.cuda.synchronize()
 
@@ -226,14 +267,10 @@ class DecodeLoop:
         s = self.step_index
         pos = self.P + s
         if pos % PAGE == 0:                       # the new token opens a page
-            for b in range(self.B):
-                if self.live[b]:
-                    self._take_pages(b, 1)
-            if self.tracker:
-                self.tables.copy_(self.tables_host, non_blocking=True)
-                self.pool.sync(self.tags)         # the new pages' tags
-            else:
-                self.page_table.copy_(self.pt_host, non_blocking=True)
+            self._grow()
+            # one copy: the page table, with the tracker also the expected
+            # tags and the new pages' tags
+            self._meta_bytes[self.tracker].copy_(self._meta_src[self.tracker], non_blocking=True)
         if self._graphs is not None:
             self._graphs[s % self.step_sets].replay()
         else:
@@ -242,9 +279,8 @@ class DecodeLoop:
         self.abort_host.copy_(self.abort, non_blocking=True)
         self.lens.add_(1)
         torch.cuda.synchronize()
-        flags = self.abort_host.numpy()
-        if self.tracker and flags.any():
-            self._retire(np.flatnonzero(flags))
+        if self.tracker and self._flag_bytes.tobytes() != self._retired_flags:
+            self._retire(np.flatnonzero(self.abort_host.numpy()))
         self.step_index += 1
         return time.perf_counter() - t0
 
@@ -256,13 +292,30 @@ class DecodeLoop:
             return          # already retired: their flags stay set, nothing to do
         for b in rows:
             self.live[b] = False
-            self.pool.free(self.pages[b])
+            self._retired_flags = bytes(0 if lv else 1 for lv in self.live)
+            self._live_rows = np.flatnonzero(self.live)
+            self.pool.free([p for p in self.pages[b] if p not in self.reclaimed])
             self.pages[b] = []
             self.pt_host[b, :] = -1
         self.page_table.copy_(self.pt_host)
         dead = torch.tensor([b for b in range(self.B) if not self.live[b]], device=self.dev)
         self.lens[0, dead] = -(1 << 30)       # no position: nothing is appended
         self.lens[1, dead] = -(1 << 30) + 1   # stays negative: no pages are read
+
+    def reclaim(self, b: int, page_index: int):
+        """Give one of request b's pages to another holder behind its back: the
+        pool frees it and hands it out again, which changes its tag; request b
+        still maps it with the tag it remembers.  The new tag goes up with the
+        tables, as after any allocation.  Request b no longer holds the page:
+        retiring it leaves the page with its new holder."""
+        pid = self.pages[b][page_index]
+        self.pool.free([pid])
+        ids, tags = self.pool.alloc(self.pool.num_free)   # first in, first out: pid last
+        assert int(ids[-1]) == pid
+        self._tags_np[ids] = tags.view(np.int32)
+        self.pool.free(ids[:-1])
+        self.reclaimed.add(pid)
+        self.meta.copy_(self.meta_host)
 
     def corrupt_expected(self, b: int, page_index: int):
         """Make request b remember a wrong tag for one of its pages (the view a
