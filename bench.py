@@ -679,8 +679,10 @@ def main():
         return run
 
     steps_ = [lambda s=s: s.step(check_tags=True) for s in states]
-    vas = [s.verify_append for s in states]
-    decs = [lambda s=s: s.decode(True) for s in states]
+    # the step's two calls on their own, through the step's prepared launches
+    # (for the current stream: a graph capture prepares its own)
+    vas = [lambda s=s: s.prepared(True)[0]() for s in states]
+    decs = [lambda s=s: s.prepared(True)[1]() for s in states]
     if args.graph:
         caps = [capture_graphs(s, [a, b, c]) for s, a, b, c in zip(states, steps_, vas, decs)]
         steps_, vas, decs = ([c[i] for c in caps] for i in range(3))
@@ -766,7 +768,7 @@ def main():
             t2 = time_steps(st2, 100)
             b2, a2 = alg_bytes(w2, cd, True)
             td2 = statistics.median(
-                event_times([cycle([lambda s=s: s.decode(True) for s in c2])], 50)[0]) * 1e-3
+                event_times([cycle([lambda s=s: s.prepared(True)[1]() for s in c2])], 50)[0]) * 1e-3
             var[name] = {"ms_per_step": round(t2 * 1e3, 4), "tokens_s": round(w2.B / t2, 1),
                          "hbm_gbps": round(b2 / t2 / 1e9, 1),
                          "attn_gbps": round(a2 / td2 / 1e9, 1)}

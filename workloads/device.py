@@ -109,6 +109,13 @@ class DeviceStep:
             cache[check_tags] = (h, first, dec)
         return cache[check_tags]
 
+    def prepared(self, check_tags: bool = True):
+        """The default step's two prepared launches for the current stream:
+        (fused check + append, or the plain append without the tracker;
+        attention into the bf16 rows)."""
+        _, first, dec = self._prepare(check_tags)
+        return first, dec
+
     def step(self, check_tags=True, out_dtype=fp8kv.OUT_BF16, stream=None, fused=True):
         """One decode step: tag check + append (one launch when fused), then
         attention.  check_tags=False is the no-op tracker path.  The default
@@ -173,6 +180,13 @@ class SpecStep:
         fp8kv.verify_append_q(s.desc, s.K, s.V, s.k_scale, s.v_scale, self.k_new_q, self.v_new_q,
                               self.first_pos, s.page_table, s.expected_tags, s.ctx_lens,
                               s.pool_tags, abort=s.abort, stream=stream)
+
+    def prepared(self, check_tags: bool = True):
+        """The default step's two prepared launches for the current stream:
+        (fused check + append, or the plain append without the tracker;
+        attention into the bf16 rows)."""
+        _, first, dec = self._prepare(check_tags)
+        return first, dec
 
     def step(self, check_tags=True, out_dtype=fp8kv.OUT_BF16, stream=None, fused=True):
         s = self.base
