@@ -2095,6 +2095,11 @@ fp8kv_status decode_setup(const fp8kv_cache_desc* desc, const void* d_k_cache,
   const int G = num_q_heads / desc->num_kv_heads;
   // the (query, head) pairs of a kv-head fill one or two 16-column MFMA tiles
   if (G * q_len > kMaxGroup || batch > kMaxBatch) return FP8KV_UNSUPPORTED;
+  // the work split's prefix sums are 32-bit: each request counts at most the
+  // table's width in pages plus its segments' fixed items
+  if (static_cast<int64_t>(batch) * (static_cast<int64_t>(max_pages_per_seq) + kPieceItems) >
+      static_cast<int64_t>(INT32_MAX))
+    return FP8KV_UNSUPPORTED;
   if (out_dtype != FP8KV_OUT_BF16 && out_dtype != FP8KV_OUT_F32) return FP8KV_INVALID_ARG;
   if (batch == 0) return FP8KV_OK;
   if (!d_k_cache || !d_v_cache || !d_q || !d_ctx_lens || !d_out ||

@@ -266,7 +266,9 @@ fp8kv_status fp8kv_verify_append_q(const fp8kv_cache_desc *desc, void *d_k_cache
 /*   +0 rows.  Without the check, page ids outside [0, num_pages) are still   */
 /*   never dereferenced; their tokens are left out (results for such a        */
 /*   request are unspecified).                                                */
-/*   batch <= 4096.  num_workers: 0 picks the device's resident wave count    */
+/*   batch <= 4096 and batch * (max_pages_per_seq + 16) < 2^31 (the work      */
+/*   split counts pages in 32 bits), else FP8KV_UNSUPPORTED (every decode      */
+/*   entry point).  num_workers: 0 picks the device's resident wave count     */
 /*   (compute units x 12); otherwise rounded up to a multiple of 4.           */
 /*   d_workspace: at least fp8kv_decode_workspace_size() bytes for the same   */
 /*   batch, num_q_heads and num_workers on the current device.  Calls that    */

@@ -82,6 +82,13 @@ def test_argument_validation_before_any_device_call():
     t3 = list(args_tail)
     t3[0] = ctypes.c_int32(66)
     assert f(ctypes.byref(ok), fake, fake, fake, fake, fake, *t3) == -2
+    # a table so wide that the work split's 32-bit page counts could overflow
+    t7 = list(args_tail)
+    t7[4] = ctypes.c_int32(4096)
+    t7[2] = ctypes.c_int32((1 << 31) // 4096 - 16)
+    assert f(ctypes.byref(ok), fake, fake, fake, fake, fake, *t7) == -2
+    t7[2] = ctypes.c_int32((1 << 31) // 4096 - 17)   # the widest accepted: fails later (no GPU)
+    assert f(ctypes.byref(ok), fake, fake, fake, fake, fake, *t7) != -2
     # null output
     t4 = list(args_tail)
     t4[7] = None
