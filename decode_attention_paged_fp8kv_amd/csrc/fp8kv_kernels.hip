@@ -332,14 +332,12 @@ __device__ __forceinline__ void append_store4(const AppendArgs& a, const Chunk4&
   }
 }
 
-// One thread per (token, kv-head, 4-dim chunk).  The new values and the
-// token's request and position are loaded together, then the request's abort
-// flag and page id together; the encode runs while those are in flight, so a
-// thread waits for two load latencies before its store.
+// One (token, kv-head, 4-dim chunk) item.  The new values and the token's
+// request and position are loaded together, then the request's abort flag and
+// page id together; the encode runs while those are in flight, so an item
+// waits for two load latencies before its store.
 template <int CACHE>
-__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (item >= a.total_items) return;
+__device__ __forceinline__ void append_item(const AppendArgs& a, int64_t item) {
   const int c = static_cast<int>(item & 31);
   const int64_t th = item >> 5;
   const int h = static_cast<int>(th % a.Hkv);
@@ -368,6 +366,16 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const Chunk4 r = append_encode4<CACHE>(kin, vin, ks, vs);
   if (!ok || aborted || static_cast<unsigned>(pid) >= static_cast<unsigned>(a.num_pages)) return;
   append_store4<CACHE>(a, r, h, c, pid, pos % kPage);
+}
+
+// A grid-stride loop: a bulk fill of any size fits the 32-bit grid.
+constexpr int64_t kAppendMaxBlocks = 1 << 16;
+template <int CACHE>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t item = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+       item < a.total_items; item += stride)
+    append_item<CACHE>(a, item);
 }
 
 // ---------------------------------------------------------------------------
@@ -2046,8 +2054,9 @@ fp8kv_status fp8kv_append(const fp8kv_cache_desc* desc, void* d_k_cache, void* d
   a.max_pages = max_pages_per_seq;
   a.num_pages = desc->num_pages;
   a.Hkv = desc->num_kv_heads;
-  const int64_t blocks = (a.total_items + 255) / 256;
-  if (blocks > 0x7FFFFFFF) return FP8KV_INVALID_ARG;
+  // a grid-stride kernel: at most kAppendMaxBlocks workgroups of 256 threads
+  const int64_t need = (a.total_items + 255) / 256;
+  const int64_t blocks = need < kAppendMaxBlocks ? need : kAppendMaxBlocks;
   if (desc->cache_dtype == FP8KV_E4M3)
     hipLaunchKernelGGL(append_kernel<FP8KV_E4M3>, dim3(blocks), dim3(256), 0, stream, a);
   else
