@@ -1768,7 +1768,8 @@ struct CombineArgs {
   const uint8_t* member_ok;  // [B], written by the prompt pass for grouped requests
   const float* v_scale;
   void* out;
-  int32_t batch, Hq, G, max_tokens, out_f32;
+  int32_t batch, Hq, G, out_f32;
+  int64_t max_tokens;     // the table's width in tokens
   PromptGroups pg;
   // fold_merge: the own-token decode's split segments are merged here from
   // its pieces (decode = its arguments, decode_grid = its workgroups); the
@@ -2408,7 +2409,7 @@ fp8kv_status shared_impl(const fp8kv_cache_desc* desc, const void* d_k_cache,
   ca.batch = batch;
   ca.Hq = num_q_heads;
   ca.G = a.G;
-  ca.max_tokens = max_pages_per_seq * kPage;
+  ca.max_tokens = static_cast<int64_t>(max_pages_per_seq) * kPage;
   ca.out_f32 = out_dtype == FP8KV_OUT_F32 ? 1 : 0;
   ca.pg = L.pg;
   ca.fold_merge = fused_decode_grid > 0 ? 1 : 0;
