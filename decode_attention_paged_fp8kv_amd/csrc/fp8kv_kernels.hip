@@ -882,24 +882,35 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg_id, int 
     J.advance(s_pre, B, a.Hkv, X1, wave);
     return pid;
   };
-  auto issue = [&](int slot, int pid) {
+  // A page's K and V loads: together (one-tile form), or K as soon as the
+  // slot's K has been used and V after PV (two-tile pair step: its K refill
+  // then overlaps the softmax and PV of the pair); the V offset waits per slot
+  int64_t voff[DEPTH];
+  auto issue_k = [&](int slot, int pid) {
     const bool ok = I.real() && static_cast<unsigned>(pid) < static_cast<unsigned>(a.num_pages);
     const int64_t off =
         ok ? static_cast<int64_t>(pid) * a.page_stride + static_cast<int64_t>(I.p.g) * TB : 0;
     const auto krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_cache + off),
                                                        (short)0, ok ? TB : 0, kRsrcWord3);
-    const auto vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_cache + off),
-                                                       (short)0, ok ? TB : 0, kRsrcWord3);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       kr[slot][c] = __builtin_bit_cast(
           u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, c * 1024 + lane * 16, 0, kKvLoadPolicy));
+    okp[slot] = ok;
+    voff[slot] = off;
+    I.advance(s_pre, B, a.Hkv, X1, wave);
+  };
+  auto issue_v = [&](int slot) {
+    const auto vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.v_cache + voff[slot]), (short)0, okp[slot] ? TB : 0, kRsrcWord3);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       vr[slot][c] = __builtin_bit_cast(
           u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, c * 1024 + lane * 16, 0, kKvLoadPolicy));
-    okp[slot] = ok;
-    I.advance(s_pre, B, a.Hkv, X1, wave);
+  };
+  auto issue = [&](int slot, int pid) {
+    issue_k(slot, pid);
+    issue_v(slot);
   };
 
   // prime: loads for the first DEPTH pages, page ids for the next DEPTH
@@ -1031,6 +1042,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg_id, int 
               for (int c = 0; c < NC; ++c) vr[s][c] &= vmask;
             }
           }
+          // both pages' K is used: refill K a pair ahead (V follows after PV)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            issue_k(s, __builtin_amdgcn_readfirstlane(pid_ring[s]));
+            pid_ring[s] = fetch_pid();
+          }
           float p[NT][8];
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct) {
@@ -1096,10 +1113,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg_id, int 
             }
           }
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            issue(s, __builtin_amdgcn_readfirstlane(pid_ring[s]));
-            pid_ring[s] = fetch_pid();
-          }
+          for (int s = 0; s < 2; ++s) issue_v(s);
           continue;
         }
 #pragma unroll
