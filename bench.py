@@ -384,7 +384,8 @@ def shared_study(args):
             st.step(check_tags=True)
         warm_up([lambda: st.step(check_tags=True)])
         t = time_steps(lambda: st.step(check_tags=True), args.steps)
-        td = statistics.median(event_times([lambda: st.decode(True)], max(20, args.steps // 2))[0]) * 1e-3
+        td = statistics.median(event_times([lambda: st.prepared(True)[1]()],
+                                           max(20, args.steps // 2))[0]) * 1e-3
         res["shared" if shared else "private"] = {
             "workload": w.name, "pool_pages": w.num_pages, "ms_per_step": round(t * 1e3, 4),
             "tokens_s": round(int(live.sum()) / t, 1), "decode_us": round(td * 1e6, 2),
