@@ -323,8 +323,11 @@ def spec_study(args):
     warm_up([lambda: sp.step(True), lambda: base.step(True)])
     t_spec, t_one = interleaved_steps([lambda: sp.step(True), lambda: base.step(True)], args.steps)
     nev = max(20, args.steps // 2)
-    td_spec, td_one = event_times([lambda: sp.decode(True), lambda: base.decode(True)], nev)
-    ta = event_times([lambda: sp.verify_append() if sp.k_new_q is not None else sp.append(True)],
+    # the calls on their own, through the steps' prepared launches where there are
+    # (a context shorter than q_len takes the two-launch form, unprepared)
+    spec_dec = (lambda: sp.prepared()[1]()) if sp.k_new_q is not None else (lambda: sp.decode(True))
+    td_spec, td_one = event_times([spec_dec, lambda: base.prepared(True)[1]()], nev)
+    ta = event_times([lambda: sp.prepared()[0]() if sp.k_new_q is not None else sp.append(True)],
                      nev)[0]
     td_spec = statistics.median(td_spec) * 1e-3
     td_one = statistics.median(td_one) * 1e-3

@@ -181,34 +181,41 @@ class SpecStep:
                               self.first_pos, s.page_table, s.expected_tags, s.ctx_lens,
                               s.pool_tags, abort=s.abort, stream=stream)
 
-    def prepared(self, check_tags: bool = True):
-        """The default step's two prepared launches for the current stream:
-        (fused check + append, or the plain append without the tracker;
-        attention into the bf16 rows)."""
-        _, first, dec = self._prepare(check_tags)
+    def _prepare(self):
+        """The fused check + append of the q_len tokens and the multi-query
+        attention into the bf16 rows, prepared for the current stream (again
+        when the stream or any tensor they hold changes)."""
+        s = self.base
+        h = (torch.cuda.current_stream().cuda_stream, s.num_workers,
+             *map(id, (s.K, s.V, s.k_scale, s.v_scale, self.k_new_q, self.v_new_q,
+                       self.first_pos, s.page_table, s.expected_tags, s.ctx_lens, s.pool_tags,
+                       s.abort, self.q, self.out, self.workspace)))
+        if self._prepared is None or self._prepared[0] != h:
+            va = fp8kv.verify_append_q(s.desc, s.K, s.V, s.k_scale, s.v_scale, self.k_new_q,
+                                       self.v_new_q, self.first_pos, s.page_table,
+                                       s.expected_tags, s.ctx_lens, s.pool_tags,
+                                       abort=s.abort, prepare=True)
+            dec = fp8kv.decode_attention_q(
+                s.desc, s.K, s.V, s.k_scale, s.v_scale, self.q, s.page_table, s.ctx_lens,
+                abort=s.abort, out=self.out, out_dtype=fp8kv.OUT_BF16,
+                num_workers=s.num_workers, workspace=self.workspace, prepare=True)
+            self._prepared = (h, va, dec)
+        return self._prepared
+
+    def prepared(self):
+        """The step's two prepared launches for the current stream: the fused
+        check + append of the q_len tokens, and the multi-query attention."""
+        if self.k_new_q is None:
+            raise ValueError("a context shorter than q_len: the check and append are two launches")
+        _, first, dec = self._prepare()
         return first, dec
 
     def step(self, check_tags=True, out_dtype=fp8kv.OUT_BF16, stream=None, fused=True):
-        s = self.base
         if (check_tags and fused and self.k_new_q is not None and out_dtype == fp8kv.OUT_BF16
                 and stream is None):
-            # prepared launches, again when the stream or any tensor they hold changes
-            h = (torch.cuda.current_stream().cuda_stream, s.num_workers,
-                 *map(id, (s.K, s.V, s.k_scale, s.v_scale, self.k_new_q, self.v_new_q,
-                           self.first_pos, s.page_table, s.expected_tags, s.ctx_lens, s.pool_tags,
-                           s.abort, self.q, self.out, self.workspace)))
-            if self._prepared is None or self._prepared[0] != h:
-                va = fp8kv.verify_append_q(s.desc, s.K, s.V, s.k_scale, s.v_scale, self.k_new_q,
-                                           self.v_new_q, self.first_pos, s.page_table,
-                                           s.expected_tags, s.ctx_lens, s.pool_tags,
-                                           abort=s.abort, prepare=True)
-                dec = fp8kv.decode_attention_q(
-                    s.desc, s.K, s.V, s.k_scale, s.v_scale, self.q, s.page_table, s.ctx_lens,
-                    abort=s.abort, out=self.out, out_dtype=fp8kv.OUT_BF16,
-                    num_workers=s.num_workers, workspace=self.workspace, prepare=True)
-                self._prepared = (h, va, dec)
-            self._prepared[1]()
-            return self._prepared[2]()
+            _, first, dec = self._prepare()
+            first()
+            return dec()
         if check_tags and fused and self.k_new_q is not None:
             self.verify_append(stream)
         else:
