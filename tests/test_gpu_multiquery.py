@@ -69,7 +69,7 @@ def _setup(fp8kv, hist, T, Hq, Hkv, seed=SEED, cache_dtype=0):
     return st
 
 
-def _oracle(st, abort=None):
+def _oracle(st, abort=None, sm_scale=SM_SCALE):
     Ko, Vo = oracle.new_cache(st["N"], st["Hkv"], st["cd"])
     for b in range(st["B"]):
         c = int(st["ctx"][b])
@@ -80,18 +80,36 @@ def _oracle(st, abort=None):
                           st["toks"]["v"][b][:c], np.full(c, b, np.int32),
                           np.arange(c, dtype=np.int32), st["pt"], cache_dtype=st["cd"])
     ref, _ = oracle.attention_multi(Ko, Vo, st["scale"]["k"], st["scale"]["v"], st["q"], st["pt"],
-                                    st["ctx"], SM_SCALE, abort=abort, cache_dtype=st["cd"])
+                                    st["ctx"], sm_scale, abort=abort, cache_dtype=st["cd"])
     return Ko, Vo, ref
 
 
-def _run(st, out_dtype, num_workers=0, abort=None):
+def _run(st, out_dtype, num_workers=0, abort=None, sm_scale=None):
     f = st["fp8kv"]
     ab = None if abort is None else torch.from_numpy(abort).cuda()
     out = f.decode_attention_q(st["d"], st["K"], st["V"], st["ks"], st["vs"], st["q_d"],
                                st["pt_d"], st["ctx_d"], abort=ab, out_dtype=out_dtype,
-                               num_workers=num_workers)
+                               num_workers=num_workers, sm_scale=sm_scale)
     torch.cuda.synchronize()
     return (out.view(torch.int16) if out.dtype == torch.bfloat16 else out).cpu().numpy()
+
+
+@pytest.mark.parametrize("sm_scale", [0.0, -0.3, 4.0])
+@pytest.mark.parametrize("Hq,Hkv,T", [(64, 8, 1), (64, 8, 4)])
+@pytest.mark.parametrize("cd", [0, 1])
+def test_score_scale_zero_negative_and_large(Hq, Hkv, T, cd, sm_scale):
+    """The kernels fold the score scale's sign into Q and keep a zero scale
+    just above 0: sm_scale 0 weighs every visible token alike, a negative
+    one favours the lowest scores, a large one is nearly one-hot.  One tile
+    (8 columns) and two tiles (32 columns), both cache types."""
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    st = _setup(fp8kv, [1, 14, 47, 100, 300], T, Hq, Hkv, cache_dtype=cd)
+    _, _, ref = _oracle(st, sm_scale=sm_scale)
+    for nw in (0, 64):
+        o32 = _run(st, fp8kv.OUT_F32, nw, sm_scale=sm_scale)
+        o16 = _run(st, fp8kv.OUT_BF16, nw, sm_scale=sm_scale).view(np.uint16)
+        err = check_outputs(o32, o16, ref)
+        print(f"sm_scale={sm_scale} T={T} cache={cd} workers={nw}: max abs err {err:.3e}")
 
 
 @pytest.mark.parametrize("Hq,Hkv,T", [(64, 8, 2), (8, 2, 3), (4, 4, 5),

@@ -166,7 +166,7 @@ def _shared_state(Hq, Hkv, cache_dtype=0, B=5, prefix=48, suffix=40, seed=6):
 
 
 def _shared_call(fp8kv, w, st, out_dtype, workers=0, ctx=None, abort=None, prefix=None,
-                 groups=None):
+                 groups=None, sm_scale=None):
     """The shared-prompt call: by default one group (the whole batch) on the
     workload's prompt; `groups` = (group_start, prefix_len) overrides it."""
     prefix = w.prefix_len if prefix is None else prefix
@@ -174,7 +174,7 @@ def _shared_call(fp8kv, w, st, out_dtype, workers=0, ctx=None, abort=None, prefi
     out = fp8kv.decode_attention_shared(
         st.desc, st.K, st.V, st.k_scale, st.v_scale, st.q, st.page_table,
         st.ctx_lens if ctx is None else ctx, gs, pl, abort=abort, out_dtype=out_dtype,
-        num_workers=workers)
+        num_workers=workers, sm_scale=sm_scale)
     torch.cuda.synchronize()
     return (out.view(torch.int16) if out.dtype == torch.bfloat16 else out).cpu().numpy()
 
@@ -195,6 +195,26 @@ def test_shared_call_matches_oracle(Hq, Hkv, cd):
         err = check_outputs(o32, o16, ref)
         assert np.abs(o32 - plain).max() <= 1e-5
         print(f"shared call Hq={Hq} Hkv={Hkv} cache={cd} workers={nw}: max abs err {err:.3e}")
+
+
+@pytest.mark.parametrize("sm_scale", [0.0, -0.3, 4.0])
+@pytest.mark.parametrize("Hq,Hkv,cd", [(64, 8, 0), (64, 8, 1), (8, 1, 0)])
+def test_shared_call_score_scales(Hq, Hkv, cd, sm_scale):
+    """A zero, a negative and a large score scale through the prompt pass and
+    the own-token decode (fused grid, bf16 cache's separate launches, 8
+    columns) against the oracle."""
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    from _helpers import oracle_state
+    w, st = _shared_state(Hq, Hkv, cd)
+    Ko, Vo = oracle_state(w, st.k_scale_host, st.v_scale_host, cd)
+    ref, _ = oracle.attention(Ko, Vo, st.k_scale_host, st.v_scale_host, w.q_bits(), w.page_table,
+                              w.ctx_lens, sm_scale, cache_dtype=cd)
+    for nw in (0, 64):
+        o32 = _shared_call(fp8kv, w, st, fp8kv.OUT_F32, nw, sm_scale=sm_scale)
+        o16 = _shared_call(fp8kv, w, st, fp8kv.OUT_BF16, nw, sm_scale=sm_scale).view(np.uint16)
+        err = check_outputs(o32, o16, ref)
+        print(f"shared call sm_scale={sm_scale} Hq={Hq} cache={cd} workers={nw}: "
+              f"max abs err {err:.3e}")
 
 
 @pytest.mark.parametrize("cd", [0, 1])
