@@ -280,6 +280,34 @@ def test_empty_context_and_abort_rows_are_zero(lib, dev):
     st.ctx_lens.copy_(cl)
 
 
+def test_bad_page_ids_without_the_check(lib, dev):
+    """The no-op tracker (no abort array) on a table with ids outside the pool
+    in one request: nothing outside the pool is read (the loads of such a page
+    are empty), the other requests' rows keep their bits, and the plain,
+    multi-query and shared-prompt calls all return."""
+    w = workloads.custom("bad_ids", [40, 100, 300, 77], Hq=16, Hkv=2, seed=9, pool_slack=3)
+    st = dev.build(w, num_workers=16)
+    st.step(check_tags=True)
+    good = _host(st.decode(use_abort=False, out_dtype=lib.OUT_F32)).copy()
+    pt = st.page_table.clone()
+    N = w.num_pages
+    bad = torch.tensor([-1, -7, N, N + 5, 2 ** 31 - 1, -(2 ** 31)], dtype=torch.int32, device="cuda")
+    st.page_table[2, 1:1 + bad.numel()] = bad
+    out = _host(st.decode(use_abort=False, out_dtype=lib.OUT_F32))
+    keep = [0, 1, 3]
+    assert (out[keep] == good[keep]).all()
+    assert np.isfinite(out[2]).all()
+    q4 = st.q.unsqueeze(1).expand(-1, 2, -1, -1).contiguous()        # two queries per request
+    o4 = lib.decode_attention_q(st.desc, st.K, st.V, st.k_scale, st.v_scale, q4, st.page_table,
+                                st.ctx_lens, out_dtype=lib.OUT_F32, num_workers=16)
+    assert np.isfinite(_host(o4)).all()
+    osh = lib.decode_attention_shared(st.desc, st.K, st.V, st.k_scale, st.v_scale, st.q,
+                                      st.page_table, st.ctx_lens, [0, 4], [32],
+                                      out_dtype=lib.OUT_F32, num_workers=16)
+    assert np.isfinite(_host(osh)).all()
+    st.page_table.copy_(pt)
+
+
 # ---------------------------------------------------------------------------
 # invariants
 # ---------------------------------------------------------------------------
