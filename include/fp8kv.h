@@ -189,6 +189,8 @@ fp8kv_status fp8kv_verify_tags(const int32_t *d_page_table, const uint32_t *d_ex
 /* skips tokens of aborted requests -- a stale mapping must not write into a */
 /* page now owned by someone else.  Tokens whose request, position or page   */
 /* id is out of range are skipped; nothing outside the pools is written.     */
+/* Tokens are written in parallel: if several tokens of one call name the    */
+/* same slot, the slot holds one of them (which one is not specified).       */
 /* ------------------------------------------------------------------------ */
 fp8kv_status fp8kv_append(const fp8kv_cache_desc *desc, void *d_k_cache, void *d_v_cache,
                           const float *d_k_scale, const float *d_v_scale,

@@ -45,7 +45,7 @@ def lib():
         L.oracle_verify.argtypes = [_p, _p, _i32, _p, _i32, _p, _i32, _i32, _p]
         L.oracle_append.restype = ctypes.c_int
         L.oracle_append.argtypes = [_i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p,
-                                    _i32, _p, _p, _p, _i32, _p]
+                                    _i32, _p, _p, _p, _i32, _i32, _p]
         L.oracle_attention.restype = ctypes.c_int
         L.oracle_attention.argtypes = [_i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _i32,
                                        _p, _i32, _p, _i32, ctypes.c_float, _p, _p, _p, _p, _i32]
@@ -123,7 +123,7 @@ def append(k_cache, v_cache, k_scale, v_scale, k_new, v_new, token_seq, token_po
     ab = None if abort is None else _c(abort, np.uint8)
     return lib().oracle_append(cache_dtype, N, S, Hkv, D, _ptr(k_cache), _ptr(v_cache),
                                _ptr(ks), _ptr(vs), _ptr(kn), _ptr(vn), ts.shape[0],
-                               _ptr(ts), _ptr(tp), _ptr(pt), pt.shape[1], _ptr(ab))
+                               _ptr(ts), _ptr(tp), _ptr(pt), pt.shape[0], pt.shape[1], _ptr(ab))
 
 
 def attention(k_cache, v_cache, k_scale, v_scale, q, page_table, ctx_lens, sm_scale,

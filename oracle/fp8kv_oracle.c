@@ -187,15 +187,17 @@ void oracle_verify(const int32_t *page_table, const uint32_t *expected_tags,
 /* x/s in binary64 and rounding to binary32 gives exactly that quotient     */
 /* (binary64 carries more than 2*24+2 significand bits).                     */
 /* A BF16 cache stores the BF16 bits unchanged.                              */
-/* Tokens of aborted requests are skipped; so are tokens whose page entry   */
-/* is out of range (nothing is written).  Returns the number skipped for an */
-/* invalid entry.                                                            */
+/* Tokens of aborted requests are skipped; so are tokens whose request is   */
+/* not a row of the table (num_seqs rows), whose position falls outside the  */
+/* table, or whose page entry is out of range (nothing is written: a token  */
+/* with no valid destination must not land in a page someone else holds).  */
+/* Returns the number skipped for an invalid request, position or entry.    */
 /* ------------------------------------------------------------------------ */
 int oracle_append(int32_t cache_dtype, int32_t num_pages, int32_t page_size,
                   int32_t num_kv_heads, int32_t head_dim, void *k_cache, void *v_cache,
                   const float *k_scale, const float *v_scale, const uint16_t *k_new,
                   const uint16_t *v_new, int32_t num_tokens, const int32_t *token_seq,
-                  const int32_t *token_pos, const int32_t *page_table,
+                  const int32_t *token_pos, const int32_t *page_table, int32_t num_seqs,
                   int32_t max_pages, const uint8_t *abort_flags) {
     /* 1. where each token goes: page and slot (page -1: nowhere) */
     size_t nt = (size_t)(num_tokens > 0 ? num_tokens : 1);
@@ -207,6 +209,10 @@ int oracle_append(int32_t cache_dtype, int32_t num_pages, int32_t page_size,
         int pos = token_pos[t];
         dst_page[t] = -1;
         dst_slot[t] = 0;
+        if (b < 0 || b >= num_seqs) {
+            ++skipped;
+            continue;
+        }
         if (abort_flags && abort_flags[b]) continue;
         if (pos < 0 || pos / page_size >= max_pages) {
             ++skipped;

@@ -30,8 +30,8 @@ int oracle_append(int32_t cache_dtype, int32_t num_pages, int32_t page_size,
                   int32_t num_kv_heads, int32_t head_dim, void *k_cache, void *v_cache,
                   const float *k_scale, const float *v_scale, const uint16_t *k_new,
                   const uint16_t *v_new, int32_t num_tokens, const int32_t *token_seq,
-                  const int32_t *token_pos, const int32_t *page_table, int32_t max_pages,
-                  const uint8_t *abort_flags);
+                  const int32_t *token_pos, const int32_t *page_table, int32_t num_seqs,
+                  int32_t max_pages, const uint8_t *abort_flags);
 int oracle_attention(int32_t cache_dtype, int32_t num_pages, int32_t page_size,
                      int32_t num_kv_heads, int32_t head_dim, const void *k_cache,
                      const void *v_cache, const float *k_scale, const float *v_scale,
@@ -197,9 +197,9 @@ int main(void) {
   uint8_t *ko = calloc(elems, 1), *vo = calloc(elems, 1);
   int32_t nseq[B];
   for (int b = 0; b < B; ++b) nseq[b] = b;
-  oracle_append(0, NPAGES, PAGE, HKV, D, ko, vo, ks, vs, kp, vp, nprompt, seq, pos, &pt[0][0],
+  oracle_append(0, NPAGES, PAGE, HKV, D, ko, vo, ks, vs, kp, vp, nprompt, seq, pos, &pt[0][0], B,
                 MAXP, NULL);
-  oracle_append(0, NPAGES, PAGE, HKV, D, ko, vo, ks, vs, kn, vn, B, nseq, new_pos, &pt[0][0],
+  oracle_append(0, NPAGES, PAGE, HKV, D, ko, vo, ks, vs, kn, vn, B, nseq, new_pos, &pt[0][0], B,
                 MAXP, ab_o);
   double *ref = malloc(sizeof(double) * B * HQ * D);
   if (oracle_attention(0, NPAGES, PAGE, HKV, D, ko, vo, ks, vs, qb, HQ, &pt[0][0], MAXP, ctx, B,

@@ -75,6 +75,37 @@ def test_append_every_bf16_pattern(lib, cache_dtype):
         assert bad_k.size == 0 and bad_v.size == 0, (s, bad_k[:8], bad_v[:8])
 
 
+@pytest.mark.parametrize("cache_dtype", [0, 1])
+def test_append_skips_what_is_out_of_range(lib, cache_dtype):
+    """Tokens naming a request outside the table, a negative position, a
+    position past the table, or a page id outside the pool are skipped: the
+    pools hold exactly what the oracle writes for the valid tokens."""
+    N, Hkv, P = 12, 2, 4
+    rng = np.random.default_rng(17)
+    pt = rng.permutation(N)[:3 * P].astype(np.int32).reshape(3, P)
+    pt[1, 2] = -1
+    pt[2, 3] = N + 3
+    seq = np.array([0, 0, -1, 3, 1, 1, 1, 2, 2, 2, 0, 1], np.int32)
+    pos = np.array([0, 17, 5, 5, -1, 33, 40, 63, 1, P * 16, 63, 2], np.int32)
+    T = seq.size
+    kn = rng.integers(0, 2 ** 16, (T, Hkv, 128)).astype(np.uint16)
+    vn = rng.integers(0, 2 ** 16, (T, Hkv, 128)).astype(np.uint16)
+    # no NaN inputs (their codes are checked elsewhere): clear the top exponent bit
+    kn &= np.uint16(0xBFFF)
+    vn &= np.uint16(0xBFFF)
+    sc = np.array([0.05, 0.2], np.float32)
+    d = lib.desc(N, Hkv, cache_dtype)
+    K, V = lib.new_cache(d)
+    lib.append(d, K, V, torch.from_numpy(sc).cuda(), torch.from_numpy(sc).cuda(),
+               torch.from_numpy(kn.view(np.int16)).cuda(), torch.from_numpy(vn.view(np.int16)).cuda(),
+               torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), torch.from_numpy(pt).cuda())
+    Ko, Vo = oracle.new_cache(N, Hkv, cache_dtype)
+    skipped = oracle.append(Ko, Vo, sc, sc, kn, vn, seq, pos, pt, cache_dtype=cache_dtype)
+    assert (unswizzle(_host(K), Hkv, cache_dtype, range(N), False) == Ko).all()
+    assert (unswizzle(_host(V), Hkv, cache_dtype, range(N), True) == Vo).all()
+    print(f"append: {T} tokens, oracle skipped {skipped}")
+
+
 # ---------------------------------------------------------------------------
 # tag check
 # ---------------------------------------------------------------------------

@@ -4,7 +4,8 @@
     bit-level encoder of test_oracle_e4m3 and numpy's binary32 division
     (IEEE correctly rounded) -- the definition, computed another way;
   * closed form: x = DEC(c) * 2^k with scale 2^k re-encodes to c;
-  * aborted requests and invalid page entries write nothing;
+  * aborted requests, invalid page entries and tokens outside the table
+    write nothing;
   * a BF16 cache stores the input bits unchanged.
 """
 import numpy as np
@@ -87,6 +88,24 @@ def test_abort_and_invalid_entries_skip():
     assert (K[pt[1, L[1] // 16], :, L[1] % 16] == 0).all()   # aborted: untouched
     assert (K[pt[0, L[0] // 16], :, L[0] % 16] != 0).any()   # written
     assert K.sum() == K[pt[0, L[0] // 16]].sum()
+
+
+def test_tokens_outside_the_table_skip():
+    """A token whose request is not a row of the table (negative or past the
+    last row) or whose position lies before 0 or past the table's width is
+    skipped and counted; the valid tokens are written exactly as alone."""
+    L, pt, kn, vn = _one_step_inputs()
+    B, Hkv, D = kn.shape
+    sc = np.ones(Hkv, np.float32)
+    seq = np.array([0, -1, B, 2], np.int32)
+    pos = np.array([L[0], 3, 3, 4 * 16], np.int32)       # the last one: past the table
+    k4 = np.concatenate([kn, kn[:1]])
+    v4 = np.concatenate([vn, vn[:1]])
+    K, V = oracle.new_cache(12, Hkv)
+    assert oracle.append(K, V, sc, sc, k4, v4, seq, pos, pt) == 3
+    K1, V1 = oracle.new_cache(12, Hkv)
+    oracle.append(K1, V1, sc, sc, kn[:1], vn[:1], seq[:1], pos[:1], pt)
+    assert (K == K1).all() and (V == V1).all()
 
 
 def test_bf16_cache_copies_bits():
