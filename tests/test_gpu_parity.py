@@ -339,6 +339,35 @@ def test_bad_page_ids_without_the_check(lib, dev):
     st.page_table.copy_(pt)
 
 
+def test_calls_on_another_stream(lib, dev):
+    """The entry points enqueue on the stream they are given, or torch's
+    current one: the step on a side stream (prepared launches made for it),
+    then the check + append and the attention with an explicit stream
+    argument, give the default stream's bits; the stale requests abort alike."""
+    w = workloads.make(5, batch=24)
+    a = dev.build(w, num_workers=64)
+    b = dev.build(w, num_workers=64)
+    c = dev.build(w, num_workers=64)
+    ref = a.step(check_tags=True).clone()
+    torch.cuda.synchronize()
+    s1 = torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        out1 = b.step(check_tags=True)
+    s1.synchronize()
+    s2 = torch.cuda.Stream()
+    lib.verify_append(c.desc, c.K, c.V, c.k_scale, c.v_scale, c.k_new, c.v_new, c.token_pos,
+                      c.page_table, c.expected_tags, c.ctx_lens, c.pool_tags, abort=c.abort,
+                      stream=s2)
+    out2 = lib.decode_attention(c.desc, c.K, c.V, c.k_scale, c.v_scale, c.q, c.page_table,
+                                c.ctx_lens, abort=c.abort, num_workers=64, stream=s2)
+    s2.synchronize()
+    assert (_host(a.abort) == w.expected_abort).all()
+    for st, out in ((b, out1), (c, out2)):
+        assert torch.equal(out, ref)
+        assert torch.equal(st.abort, a.abort)
+        assert torch.equal(st.K, a.K) and torch.equal(st.V, a.V)
+
+
 # ---------------------------------------------------------------------------
 # invariants
 # ---------------------------------------------------------------------------
