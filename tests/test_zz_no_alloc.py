@@ -2,7 +2,8 @@
 against the workspace form it shares its kernels with: the same outputs bit
 for bit (same inputs, same worker count), on two calls in a row, the second
 smaller than the first, whatever the shared scratch holds from earlier calls;
-sizes above the scratch are refused before anything runs."""
+sizes above the scratch are refused before anything runs; the call recorded in
+a HIP graph replays to the eager bits."""
 import numpy as np
 import pytest
 import torch
@@ -87,3 +88,38 @@ def test_noalloc_refuses_sizes_beyond_its_scratch():
                                    torch.empty(0, Hq, 128, dtype=torch.bfloat16, device="cuda"),
                                    z.view(0, 0), z, out)
     torch.cuda.synchronize()
+
+
+def test_noalloc_call_recorded_in_a_graph():
+    """The callers the entry point is for: a HIP graph records the call
+    (nothing to allocate at capture or at replay); three replays, with eager
+    calls of the workspace form and a cleared output in between, each equal
+    to the eager result bit for bit."""
+    import decode_attention_paged_fp8kv_amd as fp8kv
+    from workloads import device
+    w = workloads.make(5, batch=40)
+    st = device.build(w, num_workers=64)
+    st.step(check_tags=True)
+    torch.cuda.synchronize()
+    ref = st.decode(num_workers=64).clone()
+    out = torch.empty_like(ref)
+
+    def call():
+        fp8kv.decode_attention_noalloc(st.desc, st.K, st.V, st.k_scale, st.v_scale, st.q,
+                                       st.page_table, st.ctx_lens, out, abort=st.abort,
+                                       num_workers=64)
+    call()                      # the first call on the device looks up the scratch address
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()                  # marshalled inside the capture: it names the capturing stream
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), r
+        st.decode(num_workers=64)   # eager work between replays
+        torch.cuda.synchronize()
