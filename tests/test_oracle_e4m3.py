@@ -158,6 +158,7 @@ def test_bitlevel_encoder_agrees_on_every_binary32():
     spec = importlib.util.spec_from_file_location("c_tests_build", os.path.join(here, "c", "build.py"))
     b = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(b)
+    oracle.lib()                       # the oracle's library, built if missing
     binary = b.E4M3_BIN if os.path.exists(b.E4M3_BIN) else b.build_e4m3()
     r = subprocess.run([binary], capture_output=True, text=True, timeout=600)
     print(r.stdout.strip())
