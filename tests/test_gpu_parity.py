@@ -246,7 +246,8 @@ def test_short_segments_among_long_ones(lib, dev, workers):
 def test_largest_batch(lib, dev):
     """4096 requests (the largest batch) with short contexts, 1% of them holding
     one stale entry: every abort flag, every cache byte and every output row
-    against the oracle; one request more is rejected."""
+    against the oracle, also through the two-tile kernel with 8 queries per
+    request; one request more is rejected."""
     rng = np.random.default_rng(4096)
     L = rng.integers(0, 41, 4096)
     w = workloads.custom("max_batch", L, Hq=8, Hkv=2, seed=4096, pool_slack=3)
@@ -274,6 +275,15 @@ def test_largest_batch(lib, dev):
     assert (o32[exp_ab == 1] == 0).all()
     err = check_outputs(o32, _host(out16.view(torch.int16)), ref)
     print(f"4096 requests, {int(exp_ab.sum())} aborted: max abs err {err:.3e}")
+    # the same batch through the two-tile kernel: 8 queries per request (32 columns)
+    q8 = workloads.draw_bits(77, 0, 4096 * 8 * 8 * 128).reshape(4096, 8, 8, 128)
+    o8 = lib.decode_attention_q(st.desc, st.K, st.V, st.k_scale, st.v_scale,
+                                torch.from_numpy(q8.view(np.int16)).cuda(), st.page_table,
+                                st.ctx_lens, abort=st.abort, out_dtype=lib.OUT_F32)
+    ref8, _ = oracle.attention_multi(Ko, Vo, st.k_scale_host, st.v_scale_host, q8, w.page_table,
+                                     w.ctx_lens, SM_SCALE, abort=exp_ab)
+    err8 = check_outputs(_host(o8), None, ref8)
+    print(f"4096 requests x 8 queries (two tiles): max abs err {err8:.3e}")
     big = torch.zeros(4097, dtype=torch.int32, device="cuda")
     with pytest.raises(lib.Fp8kvError) as e:
         lib.decode_attention(st.desc, st.K, st.V, st.k_scale, st.v_scale,
